@@ -1,0 +1,109 @@
+/*
+ * Q4-weight x Q8-activation oracle: plain, slow, single-threaded CPU code.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library may include,
+ * link or call this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header, table or
+ * helper with the HIP path.
+ *
+ * What it computes.  The page "GGML：Backend 抽象与硬件加速" (sections
+ * "Metal 与 Vulkan：默认路径和生成路径" and "硬件选择怎样映射到本栈") states
+ * that every backend honours one convention -- 4-bit quantised weights dotted
+ * with 8-bit quantised activations -- and that hardware changes only the
+ * kernel, never that arithmetic.  The block format itself is defined in an
+ * earlier chapter that is not among the pages; this oracle uses the fixed
+ * format of this project:
+ *   - blocks of 32 consecutive elements along K;
+ *   - a Q4 block is an fp16 scale d plus 32 4-bit codes q in [0,15] that
+ *     stand for the values (q - 8) * d;
+ *   - a Q8 block is an fp32 scale plus 32 int8 codes;
+ *   - each block's integer dot product is exact in int32, is multiplied by
+ *     d_w * d_x and the products are summed in fp32.
+ * The fused RMSNorm -> multiply-by-norm-weight prologue follows the page
+ * "llama.cpp b10909：Metal后端融合表重构..." (the RMS_NORM+MUL fusion it
+ * restores).  Readings of every point the pages leave open are listed in the
+ * function comments below.
+ *
+ * Parity status: every function here is pinned by tests against closed
+ * forms, hand-derived examples, library routines or brute force; none is
+ * "parity unpinned".
+ *
+ * Plane layouts (all row-major, no padding):
+ *   qs  u8  [M][K/2]  block b of row m occupies bytes m*K/2 + 16b .. +15;
+ *                     byte j holds code j in its low nibble and code j+16
+ *                     in its high nibble.
+ *   d   u16 [M][K/32] fp16 bit patterns of the block scales.
+ *   xq  i8  [B][K]    activation codes.
+ *   xd  f32 [B][K/32] activation block scales.
+ *   xs  i32 [B][K/32] sum of the 32 codes of each activation block.
+ */
+#ifndef Q4Q8_ORACLE_H
+#define Q4Q8_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE 754 binary32 -> binary16, round to nearest even, with subnormals,
+ * overflow to +-inf, NaN kept quiet. */
+uint16_t orc_f32_to_f16(float f);
+/* binary16 -> binary32 (exact). */
+float orc_f16_to_f32(uint16_t h);
+
+/* Bulk forms of the two conversions (for exhaustive tests). */
+void orc_f32_to_f16_array(const float* in, int64_t n, uint16_t* out);
+void orc_f16_to_f32_array(const uint16_t* in, int64_t n, float* out);
+
+/* Q4 quantisation of W [M][K] (K % 32 == 0) into the qs / d planes. */
+void orc_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs, uint16_t* d);
+
+/* Unpack codes: q [M][K] u8 in [0,15] from the qs plane (layout inverse). */
+void orc_q4_unpack_codes(const uint8_t* qs, int64_t M, int64_t K, uint8_t* q);
+
+/* RMS normalisation of each row: out = x * s, s = 1/sqrt(mean(x^2) + eps),
+ * with the fixed reduction order described in the source. */
+void orc_rmsnorm(const float* x, int64_t B, int64_t K, float eps, float* out, float* scale_out);
+
+/* Elementwise out[b][k] = v[b][k] * g[k] (the MUL of RMS_NORM+MUL). */
+void orc_mul_rows(const float* v, int64_t B, int64_t K, const float* g, float* out);
+
+/* Q8 quantisation of rows v [B][K] into xq / xd (/ xs if non-null). */
+void orc_q8_quantize(const float* v, int64_t B, int64_t K, int8_t* xq, float* xd, int32_t* xs);
+
+/* Fused prologue: RMSNorm, multiply by g, Q8 quantise.  Equal bit for bit
+ * to orc_rmsnorm -> orc_mul_rows -> orc_q8_quantize.  no_norm != 0 skips
+ * the norm and the multiply and quantises x as it is (g may be NULL). */
+void orc_q8_quantize_rmsnorm(const float* x, int64_t B, int64_t K, const float* g, float eps,
+                             int no_norm, int8_t* xq, float* xd, int32_t* xs);
+
+/* Exact per-block integer dot products I [B][M][K/32] (int32). */
+void orc_block_dots(const uint8_t* qs, int64_t M, int64_t K, const int8_t* xq, int64_t B, int32_t* I);
+
+/* y [B][M] fp32: per row, blocks in ascending order,
+ *   acc = acc + float(I) * (f32(d_w) * d_x).
+ * y64 (nullable) [B][M]: the same terms summed in fp64 (exact products). */
+void orc_mul_mat(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                 const int8_t* xq, const float* xd, int64_t B, float* y, double* y64);
+
+/* Same result, output rows split over nthreads POSIX threads.  Each output
+ * element is computed by the identical sequential code, so the result is bit
+ * for bit that of orc_mul_mat. */
+void orc_mul_mat_mt(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                    const int8_t* xq, const float* xd, int64_t B, float* y, double* y64,
+                    int nthreads);
+
+/* Expert-routed product.  Weights qs [E][M][K/2], d [E][M][K/32];
+ * activations xq [T][n_x_slots][K], xd [T][n_x_slots][K/32] with
+ * n_x_slots == 1 (one row per token, shared by its slots) or == top_k (one
+ * row per token and slot); ids [T][top_k] int32.
+ *   y[t][s][:] = orc_mul_mat(expert ids[t][s], row (t, n_x_slots==1 ? 0 : s))
+ * An id outside [0, E) gives a row of quiet NaNs.  y [T][top_k][M]. */
+void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
+                    const int8_t* xq, const float* xd, int64_t n_x_slots,
+                    const int32_t* ids, int64_t T, int64_t top_k, float* y, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
