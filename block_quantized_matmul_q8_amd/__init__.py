@@ -1,0 +1,242 @@
+"""Python binding of the MI355X Q4 x Q8 library (``libq4q8.so``, C ABI in
+``include/q4q8.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and streams.  There
+is no CPU fallback: if the library is not built this module raises on import
+of the library (``lib()``), and a failed call raises ``Q4Q8Error``.
+
+The functions take torch CUDA (HIP) tensors in the plane layouts of the header:
+    qs u8 [M][K/2], d int16/uint16 [M][K/32] (fp16 bits), xq i8 [B][K],
+    xd f32 [B][K/32], y f32 [B][M].
+Outputs are allocated with torch when not passed in.  Calls are enqueued on
+``stream`` (default: the current torch stream of the tensors' device) and
+return without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+Q4Q8_OK = 0
+Q4Q8_E_ARG = -1
+Q4Q8_E_ALIGN = -2
+Q4Q8_E_ARCH = -3
+Q4Q8_E_LAUNCH = -4
+Q4Q8_E_UNSUPPORTED = -5
+
+Q8_NO_NORM = 1
+
+PATH_AUTO = 0
+PATH_GEMV = 1
+PATH_GEMM = 2
+
+QK = 32
+
+
+class Q4Q8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libq4q8.so`` (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                                  ctypes.c_float, ctypes.c_size_t)
+    L.q4q8_last_error.restype = ctypes.c_char_p
+    L.q4q8_last_error.argtypes = []
+    L.q4q8_version.restype = i32
+    L.q4q8_version.argtypes = []
+    L.q4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.q8_quantize_rmsnorm.argtypes = [vp, i64, i64, vp, f32, u32, vp, vp, vp, vp]
+    L.mul_mat_q4q8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
+    L.mul_mat_q4q8_blocksums.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.mul_mat_id_q4q8_workspace.argtypes = [i64, i64, i64]
+    L.mul_mat_id_q4q8_workspace.restype = sz
+    L.mul_mat_id_q4q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+    L.q4q8_set_path.argtypes = [i32]
+    L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
+    for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
+                 "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != Q4Q8_OK:
+        raise Q4Q8Error(fn, status, lib().q4q8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t, name, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_F16_BITS = (torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16,)
+
+
+def q4_quantize(w, qs=None, d=None, stream=None):
+    """fp32 W [M][K] -> (qs u8 [M][K/2], d int16 [M][K/32] fp16 bits)."""
+    _need(w, "w", (torch.float32,), 2)
+    M, K = w.shape
+    if qs is None:
+        qs = torch.empty((M, K // 2), dtype=torch.uint8, device=w.device)
+    if d is None:
+        d = torch.empty((M, max(K // QK, 0)), dtype=torch.int16, device=w.device)
+    _need(qs, "qs", (torch.uint8,))
+    _need(d, "d", _F16_BITS)
+    if qs.numel() != M * (K // 2) or d.numel() != M * (K // QK):
+        raise ValueError("qs / d shape does not match w")
+    _check("q4_quantize", lib().q4_quantize(_ptr(w), M, K, _ptr(qs), _ptr(d), _stream(stream, w.device)))
+    return qs, d
+
+
+def q8_quantize_rmsnorm(x, g, eps, flags=0, xq=None, xd=None, xs=None, want_xs=False, stream=None):
+    """fp32 x [B][K] (and g [K]) -> (xq i8 [B][K], xd f32 [B][K/32], xs i32 [B][K/32] or None)."""
+    _need(x, "x", (torch.float32,), 2)
+    B, K = x.shape
+    if g is not None:
+        _need(g, "g", (torch.float32,), 1)
+    if xq is None:
+        xq = torch.empty((B, K), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((B, K // QK), dtype=torch.float32, device=x.device)
+    if xs is None and want_xs:
+        xs = torch.empty((B, K // QK), dtype=torch.int32, device=x.device)
+    _need(xq, "xq", (torch.int8,))
+    _need(xd, "xd", (torch.float32,))
+    if xs is not None:
+        _need(xs, "xs", (torch.int32,))
+    if xq.numel() != B * K or xd.numel() != B * (K // QK):
+        raise ValueError("xq / xd shape does not match x")
+    _check("q8_quantize_rmsnorm",
+           lib().q8_quantize_rmsnorm(_ptr(x), B, K, _ptr(g), ctypes.c_float(eps), flags, _ptr(xq), _ptr(xd),
+                                     _ptr(xs), _stream(stream, x.device)))
+    return xq, xd, xs
+
+
+def _matmul_shapes(qs, d, xq, xd):
+    _need(qs, "qs", (torch.uint8,), 2)
+    _need(d, "d", _F16_BITS, 2)
+    _need(xq, "xq", (torch.int8,), 2)
+    _need(xd, "xd", (torch.float32,), 2)
+    M, half = qs.shape
+    K = 2 * half
+    B = xq.shape[0]
+    if xq.shape[1] != K or d.shape != (M, K // QK) or xd.shape != (B, K // QK):
+        raise ValueError(f"shape mismatch: qs {tuple(qs.shape)} d {tuple(d.shape)} xq {tuple(xq.shape)} "
+                         f"xd {tuple(xd.shape)}")
+    return M, K, B
+
+
+def mul_mat_q4q8(qs, d, xq, xd, y=None, stream=None):
+    """y f32 [B][M] = Q4 W [M][K] times Q8 x [B][K] (per column)."""
+    M, K, B = _matmul_shapes(qs, d, xq, xd)
+    if y is None:
+        y = torch.empty((B, M), dtype=torch.float32, device=qs.device)
+    _need(y, "y", (torch.float32,))
+    if y.numel() != B * M:
+        raise ValueError("y shape does not match")
+    _check("mul_mat_q4q8", lib().mul_mat_q4q8(_ptr(qs), _ptr(d), M, K, _ptr(xq), _ptr(xd), B, _ptr(y),
+                                              _stream(stream, qs.device)))
+    return y
+
+
+def mul_mat_q4q8_blocksums(qs, d, xq, xd, y=None, I=None, stream=None):
+    """As mul_mat_q4q8, also returning the exact block sums I i32 [B][M][K/32]."""
+    M, K, B = _matmul_shapes(qs, d, xq, xd)
+    if y is None:
+        y = torch.empty((B, M), dtype=torch.float32, device=qs.device)
+    if I is None:
+        I = torch.empty((B, M, K // QK), dtype=torch.int32, device=qs.device)
+    _need(y, "y", (torch.float32,))
+    _need(I, "I", (torch.int32,))
+    _check("mul_mat_q4q8_blocksums",
+           lib().mul_mat_q4q8_blocksums(_ptr(qs), _ptr(d), M, K, _ptr(xq), _ptr(xd), B, _ptr(y), _ptr(I),
+                                        _stream(stream, qs.device)))
+    return y, I
+
+
+def mul_mat_id_q4q8_workspace(E, T, top_k) -> int:
+    return int(lib().mul_mat_id_q4q8_workspace(E, T, top_k))
+
+
+def mul_mat_id_q4q8(qs, d, xq, xd, ids, y=None, ws=None, stream=None):
+    """Expert-routed product: qs u8 [E][M][K/2], d [E][M][K/32], xq i8 [T][S][K],
+    xd f32 [T][S][K/32] (S = 1 or top_k), ids i32 [T][top_k] -> y f32 [T][top_k][M]."""
+    _need(qs, "qs", (torch.uint8,), 3)
+    _need(d, "d", _F16_BITS, 3)
+    _need(xq, "xq", (torch.int8,), 3)
+    _need(xd, "xd", (torch.float32,), 3)
+    _need(ids, "ids", (torch.int32,), 2)
+    E, M, half = qs.shape
+    K = 2 * half
+    T, S, K2 = xq.shape
+    top_k = ids.shape[1]
+    if K2 != K or ids.shape[0] != T or d.shape != (E, M, K // QK) or xd.shape != (T, S, K // QK):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((T, top_k, M), dtype=torch.float32, device=qs.device)
+    _need(y, "y", (torch.float32,))
+    need = mul_mat_id_q4q8_workspace(E, T, top_k)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=qs.device)
+    _need(ws, "ws", (torch.uint8,))
+    _check("mul_mat_id_q4q8",
+           lib().mul_mat_id_q4q8(_ptr(qs), _ptr(d), E, M, K, _ptr(xq), _ptr(xd), S, _ptr(ids), T, top_k, _ptr(y),
+                                 _ptr(ws), ws.numel(), _stream(stream, qs.device)))
+    return y
+
+
+def q4q8_set_path(path: int) -> None:
+    _check("q4q8_set_path", lib().q4q8_set_path(path))
+
+
+def q4q8_dispatch_counts(reset: bool = False):
+    out = (ctypes.c_uint64 * 4)()
+    _check("q4q8_dispatch_counts", lib().q4q8_dispatch_counts(out, int(reset)))
+    return {"gemv": out[0], "gemm": out[1], "routed": out[2], "prologue": out[3]}
+
+
+def q4q8_last_error() -> str:
+    return lib().q4q8_last_error().decode()
+
+
+def q4q8_version() -> int:
+    return int(lib().q4q8_version())

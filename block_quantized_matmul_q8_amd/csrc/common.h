@@ -1,0 +1,109 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+// Not installed; the public interface is include/q4q8.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define Q4Q8_HIDDEN __attribute__((visibility("hidden")))
+
+namespace q4q8 {
+
+constexpr int kQK = 32;              // elements per quantisation block
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kMaxPrologueK = 131072;
+
+// MFMA accumulator seed: the int32 result of an i8 MFMA started from these
+// bits, read as fp32, is 1.5 * 2^23 + I exactly for |I| < 2^22, so
+// fma(F, d, -1.5 * 2^23 * d) gives fl(I * d) without a separate conversion.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits_rne(float f) {
+  // v_cvt_f16_f32 rounds to nearest even in the default mode and keeps
+  // fp16 subnormals.
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Correctly rounded fp32 square root.  On gfx950 both sqrtf and __fsqrt_rn
+// lower to the hardware estimate, which is not always the nearest float.  The
+// estimate is moved to the float whose rounding interval contains x: the
+// interval ends are the midpoints between neighbouring floats, each with at
+// most 25 significant bits, so their squares are exact in fp64.  (No fp32 x
+// has a square root exactly on a midpoint, so there are no ties.)
+// Zero, negative, infinite and NaN inputs return the hardware result.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  float y = __builtin_sqrtf(x);
+  if (!(x > 0.0f) || x == __builtin_inff()) return y;
+  const double xd = (double)x;
+#pragma unroll 1
+  for (int it = 0; it < 8; ++it) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, y);
+    const float lo = __builtin_bit_cast(float, b - 1u);
+    const double mlo = ((double)lo + (double)y) * 0.5;
+    if (xd < mlo * mlo) {
+      y = lo;
+      continue;
+    }
+    const float hi = __builtin_bit_cast(float, b + 1u);
+    const double mhi = ((double)y + (double)hi) * 0.5;
+    if (xd >= mhi * mhi) {
+      y = hi;
+      continue;
+    }
+    break;
+  }
+  return y;
+}
+
+// Exact int32 block product sum_j q_j * x_j of one Q4 block (16 bytes of
+// packed unsigned codes) with one Q8 block (two int4 of codes).
+__device__ __forceinline__ int dot_block(const uint4 w, const int4 xa, const int4 xb) {
+  // lo nibbles of byte j = code j (pairs with x codes 0..15 = xa);
+  // hi nibbles of byte j = code j+16 (pairs with x codes 16..31 = xb).
+  const uint32_t m = 0x0F0F0F0Fu;
+  int s = 0;
+  s = __builtin_amdgcn_sdot4((int)(w.x & m), xa.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)(w.y & m), xa.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)(w.z & m), xa.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)(w.w & m), xa.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)((w.x >> 4) & m), xb.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)((w.y >> 4) & m), xb.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)((w.z >> 4) & m), xb.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)((w.w >> 4) & m), xb.w, s, false);
+  return s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Route selection helpers (host).
+Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
+
+// Launchers: enqueue on `s`, return the launch status.
+Q4Q8_HIDDEN hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
+                                          uint16_t* d, hipStream_t s);
+Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g,
+                                         float eps, bool no_norm, int8_t* xq, float* xd,
+                                         int32_t* xs, hipStream_t s);
+Q4Q8_HIDDEN hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                                   const int8_t* xq, const float* xd, int64_t B, float* y,
+                                   int32_t* I, hipStream_t s);
+Q4Q8_HIDDEN hipError_t launch_gemm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                                   const int8_t* xq, const float* xd, int64_t B, float* y,
+                                   int32_t* I, hipStream_t s);
+Q4Q8_HIDDEN size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+Q4Q8_HIDDEN hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M,
+                                  int64_t K, const int8_t* xq, const float* xd, int64_t n_x_slots,
+                                  const int32_t* ids, int64_t T, int64_t top_k, float* y,
+                                  void* ws, hipStream_t s);
+
+}  // namespace q4q8

@@ -1,0 +1,171 @@
+/*
+ * q4q8.h -- C ABI of the MI355X (gfx950) Q4-weight x Q8-activation library.
+ *
+ * The operation.  "GGML：Backend 抽象与硬件加速", sections "Metal 与 Vulkan：
+ * 默认路径和生成路径" and "硬件选择怎样映射到本栈": every backend multiplies
+ * 4-bit block-quantised weights by 8-bit block-quantised activations with the
+ * same arithmetic; only the kernel changes with the hardware.  Section "CUDA：
+ * mmvq、mmq、cublas 三条矩阵路" of the same page routes a quantised
+ * matrix x vector product (decode) to a dedicated vector kernel and larger
+ * quantised products (prefill) to a matrix kernel.  The page "llama.cpp
+ * b10909：Metal后端融合表重构，修复约5% token生成性能回退" restores the fused
+ * RMS_NORM+MUL pattern whose loss cost about 5% of token generation; here it is
+ * the prologue that normalises, scales and quantises each activation row.
+ *
+ * Block format (fixed by this project; the pages defer it to a chapter that is
+ * not among them):
+ *   - 32 consecutive elements along K form a block; K must be a multiple of 32;
+ *   - Q4 weights: per block an fp16 scale d_w and 32 codes q in [0,15]
+ *     meaning (q - 8) * d_w;
+ *   - Q8 activations: per block an fp32 scale d_x and 32 int8 codes;
+ *   - I = sum_j (q_j - 8) * x_j is exact in int32; the output is the fp32 sum
+ *     over blocks of I * d_w * d_x.
+ *
+ * Plane layouts (row-major, caller-owned device memory):
+ *   qs u8  [M][K/2]   block b of row m at byte m*K/2 + 16b; byte j holds code j
+ *                     in its low nibble and code j+16 in its high nibble
+ *   d  u16 [M][K/32]  fp16 bit patterns of the weight block scales
+ *   xq i8  [B][K]     activation codes, one row per activation column / token
+ *   xd f32 [B][K/32]  activation block scales
+ *   xs i32 [B][K/32]  (optional) sum of the 32 codes of each activation block
+ *   y  f32 [B][M]     output, y[n][m] = sum over blocks of row m and column n
+ *
+ * Conventions common to every entry point:
+ *   - All array pointers are device pointers owned by the caller; the library
+ *     never frees, retains or allocates them.  Calls allocate no device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; the call returns after launch.
+ *     Inputs must stay unmodified and outputs unread until the stream reaches
+ *     the call (synchronise before reusing buffers).
+ *   - Arguments are validated on the host before anything is launched.  A bad
+ *     call returns a negative status, launches nothing and writes nothing;
+ *     q4q8_last_error() then returns a message for the calling thread.
+ *   - Empty problems (M == 0 or B == 0 or T == 0) are valid and launch nothing.
+ *   - NaN or infinite inputs give unspecified (but memory-safe) results.
+ *   - The current HIP device must be a gfx950 GPU.
+ */
+#ifndef Q4Q8_H
+#define Q4Q8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define Q4Q8_OK 0
+#define Q4Q8_E_ARG (-1)         /* null pointer, bad dimension, K % 32 != 0, ... */
+#define Q4Q8_E_ALIGN (-2)       /* a pointer violates its alignment requirement */
+#define Q4Q8_E_ARCH (-3)        /* current device is not gfx950 */
+#define Q4Q8_E_LAUNCH (-4)      /* the HIP runtime reported a launch error */
+#define Q4Q8_E_UNSUPPORTED (-5) /* valid request outside what is built */
+
+/* Flags of q8_quantize_rmsnorm. */
+#define Q8_NO_NORM 1u /* quantise x as it is: no normalisation, g ignored */
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* q4q8_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int q4q8_version(void);
+
+/*
+ * q4_quantize -- load-time quantisation of fp32 weights to the Q4 planes.
+ * Rule per 32-block: amax = max |w|; m = the element of lowest index with
+ * |w| = amax; d = m / -8 (fp32); codes = clamp(trunc(w * (1/d) + 8.5), 0, 15)
+ * from that fp32 d; stored scale = fp16(d) rounded to nearest even; an
+ * all-zero block stores d = +0 and codes 8.  (The page on the GGML backends,
+ * section "构建开关如何变成运行时能力", places weight re-layout at load time;
+ * this call is where the kernel-friendly SoA planes are produced.)
+ *   w  [M][K] f32, 16-byte aligned      qs [M][K/2] u8, 16-byte aligned
+ *   d  [M][K/32] u16, 2-byte aligned
+ */
+int q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs, uint16_t* d, void* stream);
+
+/*
+ * q8_quantize_rmsnorm -- fused activation prologue (RMS_NORM + MUL + Q8).
+ * Per row x[0..K-1]: p_b = fp32 sum of x^2 over block b in index order; the
+ * p_b are padded with zeros to a power-of-two count and summed pairwise,
+ * adjacent pairs, level by level; s = 1 / sqrt(sum / K + eps); v = (x * s) * g
+ * (two roundings, so the result equals the unfused RMS_NORM then MUL).  Then
+ * per 32-block: d = amax(|v|) / 127 (fp32), codes = roundf(v * (1/d)) with
+ * halves away from zero, clamped to [-127, 127]; an all-zero block gives d = 0
+ * and codes 0.  Codes and scales are bit-exact results of those fp32 steps.
+ * flags & Q8_NO_NORM: v = x (g may be NULL, eps ignored).
+ *   x  [B][K] f32, 16-byte aligned      g  [K] f32, 16-byte aligned
+ *   xq [B][K] i8, 16-byte aligned       xd [B][K/32] f32, 4-byte aligned
+ *   xs [B][K/32] i32 or NULL
+ *   K <= 131072.
+ */
+int q8_quantize_rmsnorm(const float* x, int64_t B, int64_t K, const float* g, float eps,
+                        uint32_t flags, int8_t* xq, float* xd, int32_t* xs, void* stream);
+
+/*
+ * mul_mat_q4q8 -- y = W x for M x K Q4 weights and B Q8 activation columns of
+ * length K.  Route (section "CUDA：mmvq、mmq、cublas 三条矩阵路" of the GGML
+ * backend page): small B takes the streaming matrix x vector kernel (the mmvq
+ * role), larger B the int8-MFMA tiled kernel (the mmq role).  Both compute the
+ * same block sums exactly; the fp32 accumulation order differs from the
+ * sequential reference, so outputs agree to rounding only.
+ *   qs [M][K/2] u8, 16-byte aligned     d  [M][K/32] u16, 2-byte aligned
+ *   xq [B][K] i8, 16-byte aligned       xd [B][K/32] f32, 4-byte aligned
+ *   y  [B][M] f32, 4-byte aligned, must not overlap the inputs
+ */
+int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                 const float* xd, int64_t B, float* y, void* stream);
+
+/*
+ * mul_mat_id_q4q8 -- expert-routed product (MUL_MAT_ID).  The scheduler
+ * section of the GGML backend page ("调度器三遍切图，pipeline 四个副本") notes
+ * that an expert matmul only touches the expert slices actually used; here the
+ * weights of experts that no token selects are never read.
+ *   qs  [E][M][K/2] u8 (16-byte aligned), d [E][M][K/32] u16
+ *   xq  [T][n_x_slots][K] i8 (16-byte aligned), xd [T][n_x_slots][K/32] f32;
+ *       n_x_slots is 1 (each token's row is shared by its top_k slots, as for
+ *       gate/up) or top_k (one row per token and slot, as for down)
+ *   ids [T][top_k] i32, expert index per token and slot
+ *   y   [T][top_k][M] f32: y[t][s] = W[ids[t][s]] * x[t][n_x_slots==1 ? 0 : s];
+ *       a row whose id lies outside [0, E) is filled with quiet NaNs
+ *   ws  device workspace of at least mul_mat_id_q4q8_workspace(E, T, top_k)
+ *       bytes, 16-byte aligned, owned by the caller; its contents on entry do
+ *       not matter and on exit are unspecified.  Calls that share a workspace
+ *       must be ordered on one stream.
+ *   T * top_k <= 65536, top_k <= 64.
+ */
+size_t mul_mat_id_q4q8_workspace(int64_t E, int64_t T, int64_t top_k);
+int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
+                    const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
+                    int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Test hooks (not for production use).  The GGML backend page's CUDA section
+ * keeps switches that force one matrix route only for cross-checking; these
+ * are the equivalent.
+ * ------------------------------------------------------------------------- */
+
+#define Q4Q8_PATH_AUTO 0
+#define Q4Q8_PATH_GEMV 1
+#define Q4Q8_PATH_GEMM 2
+
+/* Force the route taken by mul_mat_q4q8 (process-wide).  Forcing GEMV for a
+ * shape it cannot hold returns Q4Q8_E_UNSUPPORTED from mul_mat_q4q8. */
+int q4q8_set_path(int path);
+
+/* Like mul_mat_q4q8, and also writes the exact per-block integer sums
+ * I [B][M][K/32] (int32, 4-byte aligned) computed by the same kernel that
+ * produced y (a debug instance of the same kernel template). */
+int mul_mat_q4q8_blocksums(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                           const int8_t* xq, const float* xd, int64_t B, float* y, int32_t* I,
+                           void* stream);
+
+/* Per-route dispatch counters since load or the last reset:
+ * out[0] GEMV launches, out[1] GEMM launches, out[2] routed (MUL_MAT_ID)
+ * calls, out[3] prologue launches.  reset != 0 clears them after reading. */
+int q4q8_dispatch_counts(uint64_t out[4], int reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4Q8_H */

@@ -1,0 +1,93 @@
+"""GPU parity of mul_mat_id_q4q8 (expert-routed product) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("block_quantized_matmul_q8_amd")
+
+
+def _experts(seed, E, M, K):
+    w = np.stack([workloads.weight(seed, 0, e, M, K) for e in range(E)])
+    qs, d = oracle.q4_quantize(w.reshape(E * M, K))
+    return w, qs.reshape(E, M, K // 2), d.reshape(E, M, K // 32)
+
+
+def _acts(seed, T, S, K):
+    x = workloads.activation(seed, 1, S, T * S, K)
+    g = workloads.norm_weight(seed, 1, S, K)
+    xq, xd, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+    return xq.reshape(T, S, K), xd.reshape(T, S, K // 32)
+
+
+def _gpu(qs, d, xq, xd, ids):
+    y = q.mul_mat_id_q4q8(to_dev(qs), to_dev(d.view(np.int16)), to_dev(xq), to_dev(xd), to_dev(ids))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _check_rows(y, y_o, ids, E):
+    for t in range(ids.shape[0]):
+        for s in range(ids.shape[1]):
+            if 0 <= ids[t, s] < E:
+                assert_close(y[t, s], y_o[t, s], f"t={t} s={s}")
+            else:
+                assert np.all(np.isnan(y[t, s]))
+
+
+@pytest.mark.parametrize("mode", ["broadcast", "per_slot"])
+@pytest.mark.parametrize("E,M,K,T,top_k", [(6, 40, 1408, 5, 3), (9, 130, 512, 11, 4), (3, 7, 32, 2, 2)])
+def test_small(mode, E, M, K, T, top_k):
+    S = 1 if mode == "broadcast" else top_k
+    _, qs, d = _experts(31, E, M, K)
+    xq, xd = _acts(31, T, S, K)
+    ids = workloads.expert_ids(31, T, E, top_k)
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(y, y_o, ids, E)
+
+
+def test_bad_ids_give_nan_rows():
+    E, M, K, T, top_k = 4, 24, 256, 6, 2
+    _, qs, d = _experts(32, E, M, K)
+    xq, xd = _acts(32, T, 1, K)
+    ids = workloads.expert_ids(32, T, E, top_k)
+    ids[0, 1] = E
+    ids[3, 0] = -7
+    ids[5, 1] = 1 << 30
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids)
+    _check_rows(y, y_o, ids, E)
+
+
+def test_single_expert_reduces_to_mul_mat():
+    E, M, K, T = 1, 96, 1408, 7
+    _, qs, d = _experts(33, E, M, K)
+    xq, xd = _acts(33, T, 1, K)
+    ids = np.zeros((T, 1), np.int32)
+    y = _gpu(qs, d, xq, xd, ids)
+    y_mm = q.mul_mat_q4q8(to_dev(qs[0]), to_dev(d[0].view(np.int16)), to_dev(xq[:, 0]), to_dev(xd[:, 0]))
+    torch.cuda.synchronize()
+    y_o, _ = oracle.mul_mat(qs[0], d[0], xq[:, 0], xd[:, 0])
+    assert_close(y[:, 0], y_o)
+    assert_close(y_mm.cpu().numpy(), y_o)
+
+
+def test_full_moe_decode():
+    """The MoE decode workload at full shape: 64 experts, gate/up 1408 x 2048
+    fed by each token's row (shared by its 8 slots), down 2048 x 1408 fed by one
+    row per (token, slot); 16 tokens, top-8 ids uniform without replacement."""
+    cfg = workloads.MOE
+    ids = workloads.expert_ids(0, cfg.T, cfg.E, cfg.top_k)
+    for name, M, K, S in (("gate", cfg.ffn, cfg.hidden, 1), ("up", cfg.ffn, cfg.hidden, 1),
+                          ("down", cfg.hidden, cfg.ffn, cfg.top_k)):
+        _, qs, d = _experts(0 if name != "up" else 1, cfg.E, M, K)
+        xq, xd = _acts(0, cfg.T, S, K)
+        y = _gpu(qs, d, xq, xd, ids)
+        y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=16)
+        assert_close(y, y_o, name)

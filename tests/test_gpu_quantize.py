@@ -1,0 +1,99 @@
+"""GPU parity of the quantisation kernels against the oracle: bit-exact codes,
+scales and code sums (Q4 weight planes; fused RMSNorm * g -> Q8 prologue)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import f16_bits, f32_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("block_quantized_matmul_q8_amd")
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 64), (256, 512), (129, 1408), (2048, 2048), (64, 14336)])
+def test_q4_quantize_bit_exact(M, K):
+    w = workloads.weight(11, M, K % 97, M, K)
+    if M >= 3:
+        w[1, :32] = 0.0                                   # all-zero block
+        w[2, :32] = [-8 + (j % 16) for j in range(32)]    # hand example E1
+        w[0, :32] = np.float32(1e-3) * w[0, :32]
+    qs, d = q.q4_quantize(to_dev(w))
+    qs_o, d_o = oracle.q4_quantize(w)
+    assert np.array_equal(qs.cpu().numpy(), qs_o)
+    assert np.array_equal(f16_bits(d), d_o)
+
+
+def test_q4_quantize_hand_examples(hand_examples):
+    rows = [np.array([-8 + (j % 16) for j in range(32)], np.float32),
+            np.array(hand_examples["E2a"]["w"], np.float32),
+            np.array(hand_examples["E2b"]["w"], np.float32),
+            np.zeros(32, np.float32)]
+    qs, d = q.q4_quantize(to_dev(np.stack(rows)))
+    qs = qs.cpu().numpy()
+    d = f16_bits(d)
+    assert qs[0].tolist() == hand_examples["E1"]["qs"] and d[0, 0] == 0x3C00
+    assert qs[1].tolist() == hand_examples["E2a"]["qs"] and d[1, 0] == 0x3C00
+    assert qs[2].tolist() == hand_examples["E2b"]["qs"] and d[2, 0] == 0xBC00
+    assert np.all(qs[3] == hand_examples["E3"]["q4_qs_byte"]) and d[3, 0] == 0
+
+
+def test_q4_quantize_wide_range_and_subnormal_scales():
+    """Scales that round to fp16 subnormals and to large fp16 values."""
+    g = np.random.default_rng(5)
+    w = g.standard_normal((8, 256), dtype=np.float32)
+    w[0] *= np.float32(1e-6)
+    w[1] *= np.float32(3e-5)
+    w[2] *= np.float32(1e4)
+    qs, d = q.q4_quantize(to_dev(w))
+    qs_o, d_o = oracle.q4_quantize(w)
+    assert np.array_equal(qs.cpu().numpy(), qs_o)
+    assert np.array_equal(f16_bits(d), d_o)
+
+
+@pytest.mark.parametrize("B,K", [(1, 32), (5, 512), (3, 1408), (4, 2048), (2, 8192), (1, 14336),
+                                 (2048, 4096), (16, 131072)])
+def test_q8_rmsnorm_bit_exact(B, K):
+    x = workloads.activation(12, B % 89, K % 83, B, K)
+    gw = workloads.norm_weight(12, 0, K % 83, K)
+    if B >= 3:
+        x[1] = 0.0                    # all-zero row
+        x[2, : K // 2] *= np.float32(1e-3)
+    xq, xd, xs = q.q8_quantize_rmsnorm(to_dev(x), to_dev(gw), workloads.RMS_EPS, want_xs=True)
+    xq_o, xd_o, xs_o = oracle.q8_quantize_rmsnorm(x, gw, workloads.RMS_EPS)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert np.array_equal(f32_bits(xd), xd_o.view(np.uint32))
+    assert np.array_equal(xs.cpu().numpy(), xs_o)
+
+
+def test_q8_rmsnorm_hand_examples(hand_examples):
+    for key in ("E5", "E6"):
+        ex = hand_examples[key]
+        x = np.full((1, ex["K"]), ex["x"], np.float32)
+        gw = np.full(ex["K"], ex["g"], np.float32)
+        xq, xd, _ = q.q8_quantize_rmsnorm(to_dev(x), to_dev(gw), ex["eps"])
+        assert int(f32_bits(xd)[0, 0]) == int(ex["xd_bits"], 16), key
+        assert np.all(xq.cpu().numpy() == ex["code"]), key
+
+
+def test_q8_no_norm_flag(hand_examples):
+    e4 = hand_examples["E4"]
+    v = np.array([e4["v"]], np.float32)
+    xq, xd, xs = q.q8_quantize_rmsnorm(to_dev(v), None, 0.0, flags=q.Q8_NO_NORM, want_xs=True)
+    assert xq.cpu().numpy()[0].tolist() == e4["codes"]
+    assert float(xd.cpu().numpy()[0, 0]) == e4["d"] and int(xs.cpu().numpy()[0, 0]) == e4["sum"]
+    x = workloads.activation(13, 0, 0, 7, 1408) * np.float32(3.0)
+    xq, xd, xs = q.q8_quantize_rmsnorm(to_dev(x), None, 0.0, flags=q.Q8_NO_NORM, want_xs=True)
+    o = oracle.q8_quantize_rmsnorm(x, None, 0.0, no_norm=True)
+    assert np.array_equal(xq.cpu().numpy(), o[0])
+    assert np.array_equal(f32_bits(xd), o[1].view(np.uint32))
+    assert np.array_equal(xs.cpu().numpy(), o[2])
+
+
+def test_prologue_empty_batch():
+    import torch
+    x = torch.empty((0, 64), dtype=torch.float32, device="cuda:0")
+    g = torch.ones(64, dtype=torch.float32, device="cuda:0")
+    xq, xd, _ = q.q8_quantize_rmsnorm(x, g, 1e-5)
+    assert xq.shape == (0, 64) and xd.shape == (0, 2)
