@@ -1,0 +1,626 @@
+"""Throughput of the Q4 x Q8 block-quantised matmul path on one MI355X.
+
+Headline: Llama-3.2-1B-shaped decode at batch 1.  One step reads every Q4
+weight of 16 layers once (Q, K, V, O 2048 x 2048 / 512 x 2048, gate/up
+8192 x 2048, down 2048 x 8192).  Each layer has four synthetic fp32
+activation rows x ~ N(0,1) (attention input, O input, FFN input, down input)
+with their own norm weights g ~ N(1, 0.1); every row goes through the fused
+RMSNorm * g -> Q8 prologue once and the products that share it read the same
+codes.  The step is one grouped call: a prologue pass over the 64 rows, then
+one streaming launch over the 112 products, captured in a HIP graph.
+value = algorithmic bytes per step / time per step, where the bytes are the
+Q4 weights (18 B per 32), each matrix's Q8 activation (36 B per 32) and its
+fp32 output.
+
+Also reported in the same JSON line (not part of value):
+  roofline      the streaming kernel alone (the dominant kernel), timed per
+                launch with HIP events on its stream, against 8 TB/s; traffic
+                is the calibrated FETCH_SIZE + WRITE_SIZE of the committed
+                counter summary, or null when the kernel sources changed since;
+  cpu_baseline  the multithreaded oracle on this host over the same step;
+  chained       the same step as a real decoder would order it (per layer:
+                Q/K/V group, O, gate/up group, down);
+  unfused       one prologue launch per activation row and one launch per
+                matrix (176 launches per step);
+  decode_8b     Llama-3-8B-shaped decode (8 layers) at B = 1, 2, 4, 8;
+  prefill       Llama-3-8B-shaped prefill GEMM (one layer) at T = 512, 2048,
+                int8 TOPS against 5.0 POPS;
+  moe           MUL_MAT_ID decode (64 experts, 16 tokens, top-8).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-extras]
+       python bench.py --kernel-only 10      (launches for rocprofv3 runs)
+       python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (traffic summary)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+I8_PEAK_TOPS = 5000.0
+
+
+def q4_bytes(M, K):
+    return M * K * 9 // 16
+
+
+def gemv_bytes(M, K, B):
+    return q4_bytes(M, K) + B * K * 9 // 8 + B * M * 4
+
+
+def blocks_per_lane(K):
+    """Register blocking class of the streaming kernel for rows of K (32-blocks
+    per lane, rounded up to a power of two)."""
+    j = -(-(K // 32) // 64)
+    return 1 if j <= 1 else 2 if j <= 2 else 4 if j <= 4 else 8 if j <= 8 else 16
+
+
+def capture(fn):
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, steps, warmup):
+    """Median-free plain average over `steps` replays after `warmup`, bracketed
+    by synchronisation on both sides (one process, so no barrier is needed)."""
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_direct(fn, steps, warmup):
+    """Average time of `steps` back-to-back calls of fn on the current stream
+    after `warmup` calls, bracketed by synchronisation on both sides (one
+    process, so no barrier is needed)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def per_launch_ms(fn, reps):
+    """Average duration of one launch of fn, HIP events recorded around each
+    launch on the stream it runs on."""
+    import torch
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+class DecodeModel:
+    """Quantised weights, activations and outputs of a decode workload."""
+
+    def __init__(self, layer_shapes, n_layers, B, seed, dev):
+        import torch
+
+        import block_quantized_matmul_q8_amd as q
+        import workloads as wl
+
+        self.layer_shapes, self.n_layers, self.B = layer_shapes, n_layers, B
+        self.mats = []      # per layer: list of dicts
+        self.acts = []      # per layer: {slot: (x, g)}
+        for l in range(n_layers):
+            acts = {}
+            for slot, K in wl.slot_k(layer_shapes).items():
+                acts[slot] = (wl.activation_device(seed, l, slot, B, K, dev),
+                              wl.norm_weight_device(seed, l, slot, K, dev))
+            mats = []
+            for mi, m in enumerate(layer_shapes):
+                w = wl.weight_device(seed, l, mi, m.M, m.K, dev)
+                qs, d = q.q4_quantize(w)
+                del w
+                mats.append({"name": m.name, "M": m.M, "K": m.K, "slot": m.slot, "qs": qs, "d": d,
+                             "y": torch.zeros((B, m.M), dtype=torch.float32, device=dev)})
+            self.mats.append(mats)
+            self.acts.append(acts)
+        torch.cuda.synchronize()
+        self.step_bytes = n_layers * sum(gemv_bytes(m.M, m.K, B) for m in layer_shapes)
+
+    def problems(self, layer, names=None):
+        out = []
+        for m in self.mats[layer]:
+            if names is not None and m["name"] not in names:
+                continue
+            x, g = self.acts[layer][m["slot"]]
+            out.append({"qs": m["qs"], "d": m["d"], "y": m["y"], "x": x, "g": g, "eps": 1e-5})
+        return out
+
+
+def decode_1b_groups(model):
+    """The headline step (fp32 rows, prologue pass + streaming pass) and the
+    same products over precomputed Q8 planes (the streaming pass alone)."""
+    import block_quantized_matmul_q8_amd as q
+
+    probs = []
+    for l in range(model.n_layers):
+        probs += model.problems(l)
+    step = q.Group(probs, B=model.B)
+    q8 = []
+    for l in range(model.n_layers):
+        planes = {s: q.q8_quantize_rmsnorm(x, g, 1e-5)[:2] for s, (x, g) in model.acts[l].items()}
+        for m in model.mats[l]:
+            xq, xd = planes[m["slot"]]
+            q8.append({"qs": m["qs"], "d": m["d"], "y": m["y"], "xq": xq, "xd": xd})
+    stream_only = q.Group(q8, B=model.B)
+    return step, stream_only
+
+
+KERNEL_SOURCES = ("block_quantized_matmul_q8_amd/csrc/gemv.hip", "block_quantized_matmul_q8_amd/csrc/common.h",
+                  "block_quantized_matmul_q8_amd/csrc/prologue_dev.h")
+TRAFFIC_SUMMARY = "profiles/gemv_stream_llama1b_decode_traffic.txt"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """Calibrated HBM bytes per launch of the streaming kernel from the
+    committed counter summary, if it was taken on the current sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("RESULT "):
+                rec = json.loads(line[len("RESULT "):])
+    if rec is None:
+        return None, "counter summary without a RESULT line"
+    if rec.get("source_hash") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return rec["traffic_bytes_per_launch"], TRAFFIC_SUMMARY
+
+
+def bench_decode_1b(args, dev, report):
+    import workloads as wl
+
+    model = DecodeModel(wl.LLAMA_3_2_1B, 16, 1, 0, dev)
+    step, stream_only = decode_1b_groups(model)
+    ms, wall = time_direct(lambda: step(), args.steps, args.warmup)
+    value = model.step_bytes / (ms * 1e-3) / 1e9
+    g_step = capture(lambda: step())
+    ms_graph, _ = time_graph(g_step, args.steps, args.warmup)
+    del g_step
+
+    # dominant kernel: the streaming pass, the same launch as the step's second
+    # kernel (same products, Q8 planes of the same values)
+    dom_ms = per_launch_ms(lambda: stream_only(), max(args.steps, 10))
+    dom_gbs = model.step_bytes / (dom_ms * 1e-3) / 1e9
+    traffic, traffic_src = committed_traffic()
+
+    extras = {}
+    if not args.skip_extras:
+        extras.update(decode_1b_extras(args, dev, model))
+
+    report.update({
+        "metric": "Q4xQ8 GEMV HBM GB/s at B=1 (Llama-3.2-1B-shaped decode step)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(ms, 5),
+        "wall_s_timed": round(wall, 4),
+        "step_bytes": model.step_bytes,
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "launches_per_step": 2,
+        "timing": "steps launched back to back on one stream, HIP events around the timed steps",
+        "graph_replay": {"GB/s": round(model.step_bytes / (ms_graph * 1e-3) / 1e9, 1),
+                         "ms_per_step": round(ms_graph, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "kernel": f"q4q8::gemv_kernel<1, {blocks_per_lane(stream_only.plan.max_k)}, true, false> "
+                               "(streaming pass over the 112 products)",
+                     "bytes_per_launch": model.step_bytes, "avg_launch_ms": round(dom_ms, 5)},
+    })
+    report.update(extras)
+    return model
+
+
+def decode_1b_extras(args, dev, model):
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+
+    extras = {}
+    # chained: per layer Q/K/V group, O, gate/up group, down (each a prologue
+    # pass and a streaming pass)
+    chain = []
+    for l in range(model.n_layers):
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            chain.append(q.Group(model.problems(l, names), B=1))
+    g_chain = capture(lambda: [c() for c in chain])
+    ms_c, _ = time_graph(g_chain, args.steps, args.warmup)
+    extras["chained"] = {"GB/s": round(model.step_bytes / (ms_c * 1e-3) / 1e9, 1),
+                         "ms_per_step": round(ms_c, 4), "launches_per_step": 8 * model.n_layers}
+    # unfused: one prologue launch per activation row, one launch per matrix
+    bufs = []
+    for l in range(model.n_layers):
+        per = {}
+        for slot, (x, gw) in model.acts[l].items():
+            K = x.shape[1]
+            per[slot] = (x, gw, torch.empty((1, K), dtype=torch.int8, device=dev),
+                         torch.empty((1, K // 32), dtype=torch.float32, device=dev))
+        bufs.append(per)
+
+    def unfused():
+        for l in range(model.n_layers):
+            for slot, (x, gw, xq, xd) in bufs[l].items():
+                q.q8_quantize_rmsnorm(x, gw, 1e-5, xq=xq, xd=xd)
+            for m in model.mats[l]:
+                _, _, xq, xd = bufs[l][m["slot"]]
+                q.mul_mat_q4q8(m["qs"], m["d"], xq, xd, y=m["y"])
+
+    g_unf = capture(unfused)
+    ms_u, _ = time_graph(g_unf, args.steps, args.warmup)
+    extras["unfused"] = {"GB/s": round(model.step_bytes / (ms_u * 1e-3) / 1e9, 1),
+                         "ms_per_step": round(ms_u, 4), "launches_per_step": 11 * model.n_layers}
+    # folded: the prologue folded into every workgroup of the streaming kernel
+    # (single-product entry point, one launch per matrix)
+    def folded():
+        for l in range(model.n_layers):
+            for m in model.mats[l]:
+                x, gw = model.acts[l][m["slot"]]
+                q.mul_mat_q4q8_rmsnorm(m["qs"], m["d"], x, gw, 1e-5, y=m["y"])
+    g_fold = capture(folded)
+    ms_f, _ = time_graph(g_fold, args.steps, args.warmup)
+    extras["folded_per_matrix"] = {"GB/s": round(model.step_bytes / (ms_f * 1e-3) / 1e9, 1),
+                                   "ms_per_step": round(ms_f, 4), "launches_per_step": 7 * model.n_layers}
+    del g_chain, g_unf, g_fold
+    return extras
+
+
+def kernel_only(n, dev):
+    """Launch sequence for profiler runs: a calibration copy of 256 MiB, then
+    n headline steps and n streaming passes."""
+    import torch
+
+    import workloads as wl
+
+    model = DecodeModel(wl.LLAMA_3_2_1B, 16, 1, 0, dev)
+    step, stream_only = decode_1b_groups(model)
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for i in range(n):
+        step()
+        stream_only()
+    torch.cuda.synchronize()
+    print(f"[kernel-only] {n} copies of 256 MiB, {n} steps, {n} streaming passes; step_bytes {model.step_bytes}",
+          flush=True)
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the streaming kernel,
+    scaled by what the same counters read for the 256 MiB copy."""
+    import csv
+    import glob
+    import statistics
+
+    def read(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = {}
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+                    rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
+        per = {}
+        for (k, _), v in rows.items():
+            per.setdefault(k, []).append(v)
+        return per
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+
+    def pick(per, needle):
+        ks = [k for k in per if needle in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {needle}: {sorted(per)[:8]}")
+        return statistics.median(v for k in ks for v in per[k])
+
+    copy_f, copy_w = pick(fetch, "copyBuffer") * 1024, pick(write, "copyBuffer") * 1024
+    f_factor, w_factor = copy_bytes / copy_f, copy_bytes / copy_w
+    gem_f, gem_w = pick(fetch, "gemv_kernel") * 1024, pick(write, "gemv_kernel") * 1024
+    traffic = gem_f * f_factor + gem_w * w_factor
+    import workloads as wl
+    step_bytes = 16 * sum(gemv_bytes(m.M, m.K, 1) for m in wl.LLAMA_3_2_1B)
+    lines = [
+        "calibration: 256 MiB device copy (torch copy_ kernel)",
+        f"  FETCH_SIZE {copy_f / 1024:.0f} KiB per dispatch -> factor {f_factor:.4f}",
+        f"  WRITE_SIZE {copy_w / 1024:.0f} KiB per dispatch -> factor {w_factor:.4f}",
+        "streaming kernel (gemv_kernel, Llama-3.2-1B-shaped decode step, 112 products, median over dispatches)",
+        f"  FETCH_SIZE raw {gem_f / 1024:.0f} KiB -> {gem_f * f_factor / 1e6:.2f} MB",
+        f"  WRITE_SIZE raw {gem_w / 1024:.0f} KiB -> {gem_w * w_factor / 1e6:.3f} MB",
+        f"  calibrated traffic {traffic / 1e6:.2f} MB per launch vs {step_bytes / 1e6:.2f} MB algorithmic "
+        f"({traffic / step_bytes:.3f}x)",
+    ]
+    rec = {"traffic_bytes_per_launch": int(round(traffic)), "algorithmic_bytes": step_bytes,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "source_hash": kernel_source_hash()}
+    print("\n".join(lines))
+    print("RESULT " + json.dumps(rec))
+
+
+def bench_decode_8b(args, dev):
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    out = {}
+    n_layers = 8
+    for B in (1, 2, 4, 8):
+        model = DecodeModel(wl.LLAMA_3_8B, n_layers, B, 1, dev)
+        if B <= 4:
+            probs = []
+            for l in range(n_layers):
+                probs += model.problems(l)
+            try:
+                grp = q.Group(probs, B=B)
+                fn = lambda: grp()
+                route = "grouped: prologue pass + streaming pass"
+            except q.Q4Q8Error:
+                grp = None
+        else:
+            grp = None
+        if grp is None:
+            bufs = {}
+            for l in range(n_layers):
+                for slot, (x, gw) in model.acts[l].items():
+                    K = x.shape[1]
+                    bufs[(l, slot)] = (x, gw, torch.empty((B, K), dtype=torch.int8, device=dev),
+                                       torch.empty((B, K // 32), dtype=torch.float32, device=dev))
+
+            def fn():
+                for l in range(n_layers):
+                    for slot in model.acts[l]:
+                        x, gw, xq, xd = bufs[(l, slot)]
+                        q.q8_quantize_rmsnorm(x, gw, 1e-5, xq=xq, xd=xd)
+                    for m in model.mats[l]:
+                        _, _, xq, xd = bufs[(l, m["slot"])]
+                        q.mul_mat_q4q8(m["qs"], m["d"], xq, xd, y=m["y"])
+            route = "prologue + mul_mat per matrix (auto route)"
+        g = capture(fn)
+        ms, _ = time_graph(g, max(5, args.steps // 2), 2)
+        out[f"B={B}"] = {"GB/s": round(model.step_bytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 4),
+                         "route": route}
+        del g, model
+        torch.cuda.empty_cache()
+    return {"layers": n_layers, **out}
+
+
+def bench_prefill(args, dev):
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    out = {}
+    layer = wl.LLAMA_3_8B
+    mats = []
+    for mi, m in enumerate(layer):
+        w = wl.weight_device(2, 0, mi, m.M, m.K, dev)
+        qs, d = q.q4_quantize(w)
+        del w
+        mats.append((m, qs, d))
+    for T in (512, 2048):
+        acts = {}
+        for slot, K in wl.slot_k(layer).items():
+            x = wl.activation_device(2, 0, slot, T, K, dev)
+            gw = wl.norm_weight_device(2, 0, slot, K, dev)
+            acts[slot] = q.q8_quantize_rmsnorm(x, gw, 1e-5)[:2]
+        ys = [torch.empty((T, m.M), dtype=torch.float32, device=dev) for m, _, _ in mats]
+
+        def fn():
+            for (m, qs, d), y in zip(mats, ys):
+                xq, xd = acts[m.slot]
+                q.mul_mat_q4q8(qs, d, xq, xd, y=y)
+        g = capture(fn)
+        ms, _ = time_graph(g, max(5, args.steps // 2), 2)
+        ops = 2 * T * sum(m.M * m.K for m in layer)
+        tops = ops / (ms * 1e-3) / 1e12
+        out[f"T={T}"] = {"TOPS": round(tops, 1), "frac_i8_peak": round(tops / I8_PEAK_TOPS, 4),
+                         "ms_per_layer": round(ms, 4)}
+        del g
+    return out
+
+
+def bench_moe(args, dev):
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    cfg = wl.MOE
+    ids = torch.from_numpy(wl.expert_ids(0, cfg.T, cfg.E, cfg.top_k)).to(dev)
+    mats = []
+    for name, M, K, S in (("gate", cfg.ffn, cfg.hidden, 1), ("up", cfg.ffn, cfg.hidden, 1),
+                          ("down", cfg.hidden, cfg.ffn, cfg.top_k)):
+        w = wl.weight_device(3, 0, len(mats), cfg.E * M, K, dev)
+        qs, d = q.q4_quantize(w)
+        del w
+        x = wl.activation_device(3, 0, len(mats), cfg.T * S, K, dev)
+        gw = wl.norm_weight_device(3, 0, len(mats), K, dev)
+        xq, xd, _ = q.q8_quantize_rmsnorm(x, gw, 1e-5)
+        y = torch.empty((cfg.T, cfg.top_k, M), dtype=torch.float32, device=dev)
+        ws = torch.empty(q.mul_mat_id_q4q8_workspace(cfg.E, cfg.T, cfg.top_k), dtype=torch.uint8, device=dev)
+        mats.append((qs.view(cfg.E, M, K // 2), d.view(cfg.E, M, K // 32), xq.view(cfg.T, S, K),
+                     xd.view(cfg.T, S, K // 32), y, ws, M, K, S))
+
+    def fn():
+        for qs, d, xq, xd, y, ws, M, K, S in mats:
+            q.mul_mat_id_q4q8(qs, d, xq, xd, ids, y=y, ws=ws)
+    g = capture(fn)
+    ms, _ = time_graph(g, max(5, args.steps // 2), 2)
+    distinct = len(set(ids.cpu().numpy().ravel().tolist()))
+    nbytes = 0
+    for qs, d, xq, xd, y, ws, M, K, S in mats:
+        nbytes += distinct * q4_bytes(M, K) + cfg.T * S * K * 9 // 8 + cfg.T * cfg.top_k * M * 4
+    return {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 4),
+            "distinct_experts": distinct, "bytes": nbytes}
+
+
+def cpu_baseline(model, seconds=10.0):
+    """The oracle (plain C, output rows split over threads) on this host over
+    the same decode step: oracle prologue per activation row, then every
+    matrix; repeated until `seconds` have passed (at least once)."""
+    import numpy as np
+
+    import oracle
+
+    nthreads = min(os.cpu_count() or 1, 16)
+    host = []
+    for l in range(model.n_layers):
+        acts = {s: (x.cpu().numpy(), g.cpu().numpy()) for s, (x, g) in model.acts[l].items()}
+        mats = [(m["slot"], m["qs"].cpu().numpy(), m["d"].cpu().numpy().view(np.uint16)) for m in model.mats[l]]
+        host.append((acts, mats))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for acts, mats in host:
+            q8 = {s: oracle.q8_quantize_rmsnorm(x, g, 1e-5)[:2] for s, (x, g) in acts.items()}
+            for slot, qs, d in mats:
+                xq, xd = q8[slot]
+                oracle.mul_mat(qs, d, xq, xd, nthreads=nthreads, want_y64=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = model.step_bytes * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{reps} full decode step(s) of the Llama-3.2-1B-shaped workload (16 layers, B=1), "
+                      f"{el:.1f} s, {nthreads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-extras", action="store_true", help="only the headline step and its roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
+                    help="launch N steps and N streaming passes (after a calibration copy) and exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --kernel-only (no GPU needed)")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path does not shard across GPUs in this build "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    from block_quantized_matmul_q8_amd.build import LIB_PATH, build
+
+    if not os.path.exists(LIB_PATH):
+        build()
+    q.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.kernel_only:
+        kernel_only(args.kernel_only, dev)
+        return
+    report = {}
+    model = bench_decode_1b(args, dev, report)
+    print(f"[bench] decode step done: {report['value']} GB/s", file=sys.stderr, flush=True)
+    if not args.skip_extras:
+        report["decode_8b"] = bench_decode_8b(args, dev)
+        print("[bench] 8B decode done", file=sys.stderr, flush=True)
+        report["prefill"] = bench_prefill(args, dev)
+        print("[bench] prefill done", file=sys.stderr, flush=True)
+        report["moe"] = bench_moe(args, dev)
+        print("[bench] moe done", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        report["cpu_baseline"] = cpu_baseline(model, args.cpu_seconds)
+    else:
+        report["cpu_baseline"] = None
+
+    line = {
+        "metric": report.pop("metric"),
+        "value": report.pop("value"),
+        "unit": report.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": report.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded, device-drawn N(0,0.02) weights, N(0,1) activations, N(1,0.1) norm weights)",
+        "config": {"workload": "llama-3.2-1b-shaped decode, B=1, 16 layers x 7 Q4 matrices; RMSNorm*g->Q8 "
+                               "prologue pass over the 64 activation rows + one streaming launch, in a HIP graph",
+                   "hidden": 2048, "ffn": 8192, "kv_rows": 512, "layers": 16, "B": 1},
+        "roofline": report.pop("roofline"),
+        "cpu_baseline": report.pop("cpu_baseline"),
+    }
+    line.update(report)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,6 +44,21 @@ class Q4Q8Error(RuntimeError):
         self.status = status
 
 
+class GemvDesc(ctypes.Structure):
+    """q4q8_gemv_desc of include/q4q8.h."""
+    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("xq", ctypes.c_void_p), ("xd", ctypes.c_void_p), ("x", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("flags", ctypes.c_uint32), ("y", ctypes.c_void_p)]
+
+
+class GroupPlan(ctypes.Structure):
+    """q4q8_group_plan of include/q4q8.h."""
+    _fields_ = [("magic", ctypes.c_uint32), ("B", ctypes.c_int32), ("n_records", ctypes.c_int32),
+                ("n_prologue", ctypes.c_int32), ("n_windows", ctypes.c_int64), ("max_k", ctypes.c_int64),
+                ("map_offset", ctypes.c_int64), ("prologue_offset", ctypes.c_int64),
+                ("table_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -68,10 +83,15 @@ def lib() -> ctypes.CDLL:
     L.mul_mat_id_q4q8_workspace.argtypes = [i64, i64, i64]
     L.mul_mat_id_q4q8_workspace.restype = sz
     L.mul_mat_id_q4q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+    L.mul_mat_q4q8_rmsnorm.argtypes = [vp, vp, i64, i64, vp, vp, f32, u32, i64, vp, vp]
+    L.q4q8_group_build.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int32, i64, vp, sz, vp, sz,
+                                   ctypes.POINTER(GroupPlan)]
+    L.mul_mat_q4q8_group.argtypes = [vp, ctypes.POINTER(GroupPlan), vp]
     L.q4q8_set_path.argtypes = [i32]
     L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
-                 "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts"):
+                 "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
+                 "q4q8_group_build", "mul_mat_q4q8_group"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -191,6 +211,123 @@ def mul_mat_q4q8_blocksums(qs, d, xq, xd, y=None, I=None, stream=None):
            lib().mul_mat_q4q8_blocksums(_ptr(qs), _ptr(d), M, K, _ptr(xq), _ptr(xd), B, _ptr(y), _ptr(I),
                                         _stream(stream, qs.device)))
     return y, I
+
+
+def mul_mat_q4q8_rmsnorm(qs, d, x, g, eps, flags=0, y=None, stream=None):
+    """y f32 [B][M] = Q4 W [M][K] times Q8(RMSNorm(x) * g) for fp32 x [B][K], the
+    prologue folded into the product kernel (same codes as q8_quantize_rmsnorm)."""
+    _need(qs, "qs", (torch.uint8,), 2)
+    _need(d, "d", _F16_BITS, 2)
+    _need(x, "x", (torch.float32,), 2)
+    if g is not None:
+        _need(g, "g", (torch.float32,), 1)
+    M, half = qs.shape
+    K = 2 * half
+    B = x.shape[0]
+    if x.shape[1] != K or d.shape != (M, K // QK):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((B, M), dtype=torch.float32, device=qs.device)
+    _need(y, "y", (torch.float32,))
+    _check("mul_mat_q4q8_rmsnorm",
+           lib().mul_mat_q4q8_rmsnorm(_ptr(qs), _ptr(d), M, K, _ptr(x), _ptr(g), ctypes.c_float(eps), flags, B,
+                                      _ptr(y), _stream(stream, qs.device)))
+    return y
+
+
+def q4q8_group_plan(descs, B):
+    """Validate descriptors (a sequence of GemvDesc) and return the GroupPlan
+    alone (sizes of the table image and of the workspace)."""
+    n = len(descs)
+    arr = (GemvDesc * n)(*descs)
+    plan = GroupPlan()
+    _check("q4q8_group_build", lib().q4q8_group_build(arr, n, B, None, 0, None, 0, ctypes.byref(plan)))
+    return plan
+
+
+def q4q8_group_build(descs, B, workspace=None):
+    """Validate descriptors and return (table image as a numpy uint8 array,
+    GroupPlan); `workspace` is a device uint8 tensor of at least
+    plan.workspace_bytes (see q4q8_group_plan), or None when no product takes
+    fp32 rows."""
+    import numpy as np
+
+    n = len(descs)
+    arr = (GemvDesc * n)(*descs)
+    plan = q4q8_group_plan(descs, B)
+    nbytes = int(plan.table_bytes)
+    image = np.zeros(max(nbytes, 16) + 16, dtype=np.uint8)
+    off = (-image.ctypes.data) % 16
+    image = image[off:off + nbytes]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,))
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    _check("q4q8_group_build", lib().q4q8_group_build(arr, n, B, ws_ptr, ws_bytes,
+                                                      image.ctypes.data_as(ctypes.c_void_p), nbytes,
+                                                      ctypes.byref(plan)))
+    return image, plan
+
+
+def mul_mat_q4q8_group(table_dev, plan, stream=None):
+    _need(table_dev, "table", (torch.uint8,))
+    _check("mul_mat_q4q8_group", lib().mul_mat_q4q8_group(_ptr(table_dev), ctypes.byref(plan),
+                                                          _stream(stream, table_dev.device)))
+
+
+class Group:
+    """A list of independent streaming products launched together.
+
+    Each product is given as keyword arguments: qs, d (weights), y (output),
+    and either xq, xd (Q8 activations) or x with g / eps (fp32 activations
+    that the group's prologue pass normalises and quantises; flags=Q8_NO_NORM
+    skips the norm).  The tensors must stay alive and in place while the group
+    is used; the group owns its device table and workspace.
+    """
+
+    def __init__(self, problems, B=1, device=None):
+        descs = []
+        self._keep = []
+        for i, p in enumerate(problems):
+            qs, d, y = p["qs"], p["d"], p["y"]
+            _need(qs, f"problems[{i}].qs", (torch.uint8,), 2)
+            M, half = qs.shape
+            K = 2 * half
+            _need(d, f"problems[{i}].d", _F16_BITS, 2)
+            _need(y, f"problems[{i}].y", (torch.float32,), 2)
+            if tuple(d.shape) != (M, K // 32) or tuple(y.shape) != (B, M):
+                raise ValueError(f"problems[{i}]: d must be ({M}, {K // 32}) and y ({B}, {M})")
+            desc = GemvDesc(qs=qs.data_ptr(), d=d.data_ptr(), M=M, K=K, y=y.data_ptr(),
+                            eps=float(p.get("eps", 0.0)), flags=int(p.get("flags", 0)))
+            if p.get("xq") is not None:
+                _need(p["xq"], f"problems[{i}].xq", (torch.int8,), 2)
+                _need(p["xd"], f"problems[{i}].xd", (torch.float32,), 2)
+                if tuple(p["xq"].shape) != (B, K) or tuple(p["xd"].shape) != (B, K // 32):
+                    raise ValueError(f"problems[{i}]: xq must be ({B}, {K}) and xd ({B}, {K // 32})")
+                desc.xq = p["xq"].data_ptr()
+                desc.xd = p["xd"].data_ptr()
+            else:
+                _need(p["x"], f"problems[{i}].x", (torch.float32,), 2)
+                if tuple(p["x"].shape) != (B, K):
+                    raise ValueError(f"problems[{i}]: x must be ({B}, {K})")
+                desc.x = p["x"].data_ptr()
+                if p.get("g") is not None:
+                    _need(p["g"], f"problems[{i}].g", (torch.float32,), 1)
+                    if p["g"].numel() != K:
+                        raise ValueError(f"problems[{i}]: g must have {K} elements")
+                    desc.g = p["g"].data_ptr()
+            descs.append(desc)
+            self._keep.append(p)
+        dev = device if device is not None else problems[0]["qs"].device
+        plan = q4q8_group_plan(descs, B)
+        self.workspace = None
+        if plan.workspace_bytes > 0:
+            self.workspace = torch.empty(int(plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        image, self.plan = q4q8_group_build(descs, B, self.workspace)
+        self.table = torch.from_numpy(image.copy()).to(dev)
+
+    def __call__(self, stream=None):
+        mul_mat_q4q8_group(self.table, self.plan, stream)
 
 
 def mul_mat_id_q4q8_workspace(E, T, top_k) -> int:

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/q4q8.h"
 #include "common.h"
@@ -89,6 +90,18 @@ int check_matmul_args(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K
   return Q4Q8_OK;
 }
 
+q4q8::GemvProblem single_problem(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, float* y) {
+  q4q8::GemvProblem p;
+  memset(&p, 0, sizeof p);
+  p.qs = qs;
+  p.d = d;
+  p.y = y;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.win_begin = 0;
+  return p;
+}
+
 int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
                   const float* xd, int64_t B, float* y, int32_t* I, void* stream) {
   int st = check_matmul_args(qs, d, M, K, xq, xd, B, y);
@@ -109,8 +122,14 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
     use_gemv = gemv_ok;
   }
   if (use_gemv) {
+    q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
+    p.xq = xq;
+    p.xd = xd;
+    p.mode = q4q8::kModeQ8;
+    const int win = q4q8::gemv_window_rows(K, B);
+    p.n_win = (int32_t)((M + win - 1) / win);
     g_counts[0].fetch_add(1, std::memory_order_relaxed);
-    return launched(q4q8::launch_gemv(qs, d, M, K, xq, xd, B, y, I, s), "gemv");
+    return launched(q4q8::launch_gemv_table(p, nullptr, nullptr, p.n_win, K, B, false, I, s), "gemv");
   }
   if (B > (int64_t)65535 * 128) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld exceeds the GEMM grid", (long long)B);
   g_counts[1].fetch_add(1, std::memory_order_relaxed);
@@ -192,6 +211,226 @@ Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E,
   return launched(q4q8::launch_moe(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y, ws,
                                    static_cast<hipStream_t>(stream)),
                   "mul_mat_id_q4q8");
+}
+
+Q4Q8_EXPORT int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
+                                     const float* x, const float* g, float eps, uint32_t flags, int64_t B,
+                                     float* y, void* stream) {
+  int st;
+  if ((st = check_k(K)) || (st = check_dims(M, B))) return st;
+  if (flags & ~Q8_NO_NORM) return fail(Q4Q8_E_ARG, "unknown flags 0x%x", flags);
+  const bool no_norm = (flags & Q8_NO_NORM) != 0;
+  if (M == 0 || B == 0) return ok();
+  if (!qs || !d || !x || !y || (!no_norm && !g)) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(qs, 16) || !aligned(x, 16) || (!no_norm && !aligned(g, 16)) || !aligned(d, 2) || !aligned(y, 4))
+    return fail(Q4Q8_E_ALIGN, "qs, x, g must be 16-byte aligned; d 2-byte; y 4-byte");
+  if (!no_norm && !(eps >= 0.0f)) return fail(Q4Q8_E_ARG, "eps must be >= 0");
+  if (!q4q8::gemv_fused_supported(K, B))
+    return fail(Q4Q8_E_UNSUPPORTED, "B = %lld, K = %lld too large for the folded-in prologue", (long long)B,
+                (long long)K);
+  if ((st = check_device())) return st;
+  q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
+  p.x = x;
+  p.g = no_norm ? nullptr : g;
+  p.eps = eps;
+  p.mode = no_norm ? q4q8::kModeRaw : q4q8::kModeNorm;
+  const int win = q4q8::gemv_window_rows(K, B);
+  p.n_win = (int32_t)((M + win - 1) / win);
+  g_counts[0].fetch_add(1, std::memory_order_relaxed);
+  g_counts[3].fetch_add(1, std::memory_order_relaxed);
+  return launched(q4q8::launch_gemv_table(p, nullptr, nullptr, p.n_win, K, B, true, nullptr,
+                                          static_cast<hipStream_t>(stream)),
+                  "mul_mat_q4q8_rmsnorm");
+}
+
+namespace {
+constexpr uint32_t kGroupMagic = 0x51344738u;  // "Q4G8"
+
+}  // namespace
+
+Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t B, void* workspace,
+                                 size_t workspace_bytes, void* table_host, size_t table_bytes,
+                                 q4q8_group_plan* plan) {
+  if (!plan) return fail(Q4Q8_E_ARG, "null plan");
+  memset(plan, 0, sizeof *plan);
+  if (n <= 0 || n > (1 << 20)) return fail(Q4Q8_E_ARG, "n = %d must be in [1, 2^20]", n);
+  if (!descs) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (B < 1 || B > 4) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld: grouped products take 1 <= B <= 4", (long long)B);
+  for (int32_t i = 0; i < n; ++i) {
+    const q4q8_gemv_desc& e = descs[i];
+    int st;
+    if ((st = check_k(e.K)) || (st = check_dims(e.M, B))) {
+      char msg[sizeof g_err];
+      memcpy(msg, g_err, sizeof msg);
+      return fail(st, "descriptor %d: %s", i, msg);
+    }
+    if (e.M == 0) continue;
+    if (!e.qs || !e.d || !e.y) return fail(Q4Q8_E_ARG, "descriptor %d: null pointer", i);
+    if (!aligned(e.qs, 16) || !aligned(e.d, 2) || !aligned(e.y, 4)) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
+    if (e.flags & ~Q8_NO_NORM) return fail(Q4Q8_E_ARG, "descriptor %d: unknown flags", i);
+    if (!q4q8::gemv_supported(e.M, e.K, B))
+      return fail(Q4Q8_E_UNSUPPORTED, "descriptor %d: K = %lld with B = %lld exceeds the streaming kernel", i,
+                  (long long)e.K, (long long)B);
+    if (e.xq) {
+      if (!e.xd) return fail(Q4Q8_E_ARG, "descriptor %d: xq without xd", i);
+      if (!aligned(e.xq, 16) || !aligned(e.xd, 4)) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
+    } else {
+      const bool no_norm = (e.flags & Q8_NO_NORM) != 0;
+      if (!e.x || (!no_norm && !e.g)) return fail(Q4Q8_E_ARG, "descriptor %d: needs xq/xd or x (and g)", i);
+      if (!aligned(e.x, 16) || (!no_norm && !aligned(e.g, 16))) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
+      if (!no_norm && !(e.eps >= 0.0f)) return fail(Q4Q8_E_ARG, "descriptor %d: eps must be >= 0", i);
+    }
+  }
+  // Distinct fp32 inputs, in order of first use; each gets its Q8 planes in
+  // the workspace: codes [B][K] then scales [B][K/32], each 16-byte aligned.
+  struct Input {
+    const float* x;
+    const float* g;
+    int64_t K;
+    uint32_t eps_bits;
+    uint32_t raw;
+    int64_t ws_off;
+  };
+  std::vector<Input> inputs;
+  std::vector<int32_t> input_of(n, -1);
+  int64_t ws_total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const q4q8_gemv_desc& e = descs[i];
+    if (e.M == 0 || e.xq) continue;
+    const uint32_t raw = (e.flags & Q8_NO_NORM) ? 1u : 0u;
+    const float* g = raw ? nullptr : e.g;
+    uint32_t eps_bits = 0;
+    if (!raw) memcpy(&eps_bits, &e.eps, sizeof eps_bits);
+    int32_t found = -1;
+    for (size_t k = 0; k < inputs.size(); ++k) {
+      const Input& in = inputs[k];
+      if (in.x == e.x && in.g == g && in.K == e.K && in.eps_bits == eps_bits && in.raw == raw) {
+        found = (int32_t)k;
+        break;
+      }
+    }
+    if (found < 0) {
+      found = (int32_t)inputs.size();
+      inputs.push_back({e.x, g, e.K, eps_bits, raw, ws_total});
+      ws_total += (B * e.K + 15) / 16 * 16 + (B * (e.K / q4q8::kQK) * 4 + 15) / 16 * 16;
+    }
+    input_of[i] = found;
+  }
+  // Product records in the caller's order, all in one streaming launch (the
+  // kernel dispatches per product on its register-blocking class).
+  std::vector<q4q8::GemvProblem> recs;
+  std::vector<int64_t> rec_tiles;
+  int64_t tiles = 0, max_k = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const q4q8_gemv_desc& e = descs[i];
+    if (e.M == 0) continue;
+    q4q8::GemvProblem p = single_problem(e.qs, e.d, e.M, e.K, e.y);
+    p.mode = q4q8::kModeQ8;
+    if (e.xq) {
+      p.xq = e.xq;
+      p.xd = e.xd;
+    } else if (workspace) {
+      char* base = static_cast<char*>(workspace) + inputs[input_of[i]].ws_off;
+      p.xq = reinterpret_cast<const int8_t*>(base);
+      p.xd = reinterpret_cast<const float*>(base + (B * e.K + 15) / 16 * 16);
+    }
+    const int win = q4q8::gemv_window_rows(e.K, B);
+    const int64_t t = (e.M + win - 1) / win;
+    p.win_begin = (int32_t)tiles;
+    p.n_win = (int32_t)t;
+    tiles += t;
+    if (tiles > INT32_MAX) return fail(Q4Q8_E_ARG, "too many windows");
+    if (e.K > max_k) max_k = e.K;
+    recs.push_back(p);
+    rec_tiles.push_back(t);
+  }
+  plan->B = (int32_t)B;
+  plan->n_records = (int32_t)recs.size();
+  plan->n_prologue = (int32_t)inputs.size();
+  plan->n_windows = tiles;
+  plan->max_k = max_k;
+  plan->map_offset = (int64_t)(recs.size() * sizeof(q4q8::GemvProblem));
+  plan->prologue_offset = (plan->map_offset + tiles * (int64_t)sizeof(int32_t) + 15) / 16 * 16;
+  plan->table_bytes = plan->prologue_offset + (int64_t)(inputs.size() * sizeof(q4q8::PrologueJob));
+  plan->workspace_bytes = ws_total;
+  plan->magic = kGroupMagic;
+  if (!table_host) return ok();
+  const char* why = nullptr;
+  int st = Q4Q8_E_ARG;
+  if (table_bytes < (size_t)plan->table_bytes) {
+    why = "table buffer is smaller than plan->table_bytes";
+  } else if (!aligned(table_host, 16)) {
+    why = "table buffer must be 16-byte aligned";
+    st = Q4Q8_E_ALIGN;
+  } else if (ws_total > 0 && !workspace) {
+    why = "products take fp32 rows: a workspace of plan->workspace_bytes is required";
+  } else if (ws_total > 0 && workspace_bytes < (size_t)ws_total) {
+    why = "workspace is smaller than plan->workspace_bytes";
+  } else if (ws_total > 0 && !aligned(workspace, 16)) {
+    why = "workspace must be 16-byte aligned";
+    st = Q4Q8_E_ALIGN;
+  }
+  if (why) {
+    plan->magic = 0;
+    return fail(st, "%s", why);
+  }
+  char* out = static_cast<char*>(table_host);
+  memset(out, 0, (size_t)plan->table_bytes);
+  memcpy(out, recs.data(), recs.size() * sizeof(q4q8::GemvProblem));
+  int32_t* map = reinterpret_cast<int32_t*>(out + plan->map_offset);
+  int64_t m = 0;
+  for (size_t r = 0; r < recs.size(); ++r)
+    for (int64_t t = 0; t < rec_tiles[r]; ++t) map[m++] = (int32_t)r;
+  q4q8::PrologueJob* jobs = reinterpret_cast<q4q8::PrologueJob*>(out + plan->prologue_offset);
+  for (size_t k = 0; k < inputs.size(); ++k) {
+    const Input& in = inputs[k];
+    char* base = static_cast<char*>(workspace) + in.ws_off;
+    q4q8::PrologueJob j;
+    memset(&j, 0, sizeof j);
+    j.x = in.x;
+    j.g = in.g;
+    j.xq = reinterpret_cast<int8_t*>(base);
+    j.xd = reinterpret_cast<float*>(base + (B * in.K + 15) / 16 * 16);
+    j.K = (int32_t)in.K;
+    memcpy(&j.eps, &in.eps_bits, sizeof j.eps);
+    j.raw = (int32_t)in.raw;
+    jobs[k] = j;
+  }
+  return ok();
+}
+
+Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan* plan, void* stream) {
+  if (!plan || plan->magic != kGroupMagic) return fail(Q4Q8_E_ARG, "plan not built by q4q8_group_build");
+  if (plan->n_records == 0) return ok();
+  if (!table_dev) return fail(Q4Q8_E_ARG, "null table");
+  if (!aligned(table_dev, 16)) return fail(Q4Q8_E_ALIGN, "table must be 16-byte aligned");
+  if (plan->n_records < 0 || plan->B < 1 || plan->B > 4 || plan->n_windows < plan->n_records ||
+      plan->n_windows > INT32_MAX || plan->n_prologue < 0 || plan->n_prologue > plan->n_records ||
+      plan->max_k < q4q8::kQK || plan->max_k % q4q8::kQK != 0 ||
+      !q4q8::gemv_supported(1, plan->max_k, plan->B) ||
+      plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
+      plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
+      plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob))
+    return fail(Q4Q8_E_ARG, "corrupt plan");
+  int st;
+  if ((st = check_device())) return st;
+  const char* base = static_cast<const char*>(table_dev);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan->n_prologue > 0) {
+    g_counts[3].fetch_add(1, std::memory_order_relaxed);
+    st = launched(q4q8::launch_group_prologue(
+                      reinterpret_cast<const q4q8::PrologueJob*>(base + plan->prologue_offset),
+                      plan->n_prologue, plan->B, s),
+                  "mul_mat_q4q8_group (prologue pass)");
+    if (st) return st;
+  }
+  q4q8::GemvProblem unused;
+  memset(&unused, 0, sizeof unused);
+  g_counts[0].fetch_add(1, std::memory_order_relaxed);
+  return launched(q4q8::launch_gemv_table(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
+                                          reinterpret_cast<const int32_t*>(base + plan->map_offset),
+                                          plan->n_windows, plan->max_k, plan->B, false, nullptr, s),
+                  "mul_mat_q4q8_group");
 }
 
 Q4Q8_EXPORT int q4q8_set_path(int path) {

@@ -20,6 +20,25 @@ constexpr int kMaxPrologueK = 131072;
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
+// Pointers read from a record in memory are generic (flat) pointers; loads
+// through them are flat loads, which also count against the LDS counter and
+// force coarser waits.  All buffers here are global memory, so accesses go
+// through explicit global-address-space pointers.
+#define Q4Q8_GLOBAL __attribute__((address_space(1)))
+// Native vector types (HIP's float4 / uint4 classes cannot be copied out of
+// an explicitly global pointer).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ const Q4Q8_GLOBAL T* gptr(const T* p) {
+  return (const Q4Q8_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ Q4Q8_GLOBAL T* gptr_w(T* p) {
+  return (Q4Q8_GLOBAL T*)(p);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
@@ -63,7 +82,7 @@ __device__ __forceinline__ float sqrt_rn(float x) {
 
 // Exact int32 block product sum_j q_j * x_j of one Q4 block (16 bytes of
 // packed unsigned codes) with one Q8 block (two int4 of codes).
-__device__ __forceinline__ int dot_block(const uint4 w, const int4 xa, const int4 xb) {
+__device__ __forceinline__ int dot_block(const u32x4 w, const i32x4 xa, const i32x4 xb) {
   // lo nibbles of byte j = code j (pairs with x codes 0..15 = xa);
   // hi nibbles of byte j = code j+16 (pairs with x codes 16..31 = xb).
   const uint32_t m = 0x0F0F0F0Fu;
@@ -85,8 +104,57 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One product of a (grouped) GEMV launch, as the kernel reads it.
+enum GemvMode : int32_t {
+  kModeQ8 = 0,    // activations given as Q8 planes xq / xd
+  kModeNorm = 1,  // fp32 x and norm weight g: RMSNorm * g -> Q8 folded in
+  kModeRaw = 2,   // fp32 x quantised as it is
+};
+
+struct alignas(16) GemvProblem {
+  const uint8_t* qs;   // [M][K/2]
+  const uint16_t* d;   // [M][K/32]
+  const int8_t* xq;    // [B][K]       (kModeQ8)
+  const float* xd;     // [B][K/32]    (kModeQ8)
+  const float* x;      // [B][K]       (kModeNorm, kModeRaw)
+  const float* g;      // [K]          (kModeNorm)
+  float* y;            // [B][M]
+  int32_t M;
+  int32_t K;
+  float eps;
+  int32_t mode;
+  int32_t win_begin;   // index of this problem's first window in the launch
+  int32_t n_win;       // windows of this problem (ceil(M / window rows))
+  int32_t pad[2];
+};
+static_assert(sizeof(GemvProblem) == 96, "GemvProblem layout");
+
+// One fp32 input of a grouped launch, quantised by the prologue pass into
+// Q8 planes that the streaming pass then reads.
+struct alignas(16) PrologueJob {
+  const float* x;  // [B][K]
+  const float* g;  // [K] (null when raw)
+  int8_t* xq;      // [B][K]
+  float* xd;       // [B][K/32]
+  int32_t K;       // <= 16384
+  float eps;
+  int32_t raw;     // quantise x as it is
+  int32_t pad;
+};
+static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
+
 // Route selection helpers (host).
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
+Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
+// Rows per window (the unit a workgroup streams) for a product with K and B.
+Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B);
+// Persistent launch over the products of a device `table`, window w of the
+// launch belonging to record map[w]; or, when table == nullptr, over the
+// single record `p`.  `n_windows` = total windows; `max_k` = largest K among
+// the products (selects the kernel instance and the LDS size).
+Q4Q8_HIDDEN hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table,
+                                         const int32_t* map, int64_t n_windows, int64_t max_k,
+                                         int64_t B, bool any_fused, int32_t* I, hipStream_t s);
 
 // Launchers: enqueue on `s`, return the launch status.
 Q4Q8_HIDDEN hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
@@ -94,9 +162,8 @@ Q4Q8_HIDDEN hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, 
 Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g,
                                          float eps, bool no_norm, int8_t* xq, float* xd,
                                          int32_t* xs, hipStream_t s);
-Q4Q8_HIDDEN hipError_t launch_gemv(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
-                                   const int8_t* xq, const float* xd, int64_t B, float* y,
-                                   int32_t* I, hipStream_t s);
+Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B,
+                                             hipStream_t s);
 Q4Q8_HIDDEN hipError_t launch_gemm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
                                    const int8_t* xq, const float* xd, int64_t B, float* y,
                                    int32_t* I, hipStream_t s);

@@ -123,24 +123,24 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(
       for (int b0 = 0; b0 < nb; b0 += kWave) {
         const int b = b0 + lane;
         if (b < nb) {
-          uint4 w[kMoeRU];
+          u32x4 w[kMoeRU];
           float dw[kMoeRU];
 #pragma unroll
           for (int r = 0; r < kMoeRU; ++r) {
             const int row = row0 + r;
             if (row < m_end) {
-              w[r] = *reinterpret_cast<const uint4*>(qs_e + row * row_bytes + (int64_t)b * 16);
+              w[r] = *reinterpret_cast<const u32x4*>(qs_e + row * row_bytes + (int64_t)b * 16);
               dw[r] = f16_bits_to_f32(d_e[(int64_t)row * nb + b]);
             } else {
-              w[r] = make_uint4(0, 0, 0, 0);
+              w[r] = u32x4{0, 0, 0, 0};
               dw[r] = 0.0f;
             }
           }
 #pragma unroll
           for (int c = 0; c < kMoeCols; ++c) {
             if (c < nc) {
-              const int4* xp = reinterpret_cast<const int4*>(sx + (size_t)c * K + (size_t)b * kQK);
-              const int4 xa = xp[0], xb = xp[1];
+              const i32x4* xp = reinterpret_cast<const i32x4*>(sx + (size_t)c * K + (size_t)b * kQK);
+              const i32x4 xa = xp[0], xb = xp[1];
               const float xdc = sxd[c * nb + b];
               const int xsc = sxs[c * nb + b];
 #pragma unroll

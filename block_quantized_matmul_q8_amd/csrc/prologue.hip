@@ -6,7 +6,7 @@
 // (explicit __f*_rn intrinsics, and the file is built without FMA
 // contraction); the reduction order of the RMS statistic is fixed (see
 // rmsnorm_q8_kernel).
-#include "common.h"
+#include "prologue_dev.h"
 
 namespace q4q8 {
 
@@ -89,102 +89,35 @@ hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
 }
 
 // ---------------------------------------------------------------------------
-// Fused RMSNorm * g -> Q8.  One workgroup per activation row.
-//   Phase 1: thread b computes p_b = sum_{j<32} x_j^2 for block b, adding in
-//            index order (one rounding per multiply and per add).
-//   Phase 2: p is padded with +0 to P = next_pow2(nb) and reduced pairwise,
-//            level by level: p[i] = p[2i] + p[2i+1] (ping-pong LDS buffers).
-//   Phase 3: s = 1 / sqrt(ssq / K + eps) (correctly rounded div and sqrt;
-//            see sqrt_rn).
-//   Phase 4: v = (x * s) * g; per block d = amax / 127, id = 1 / d,
-//            q = roundf(v * id) (halves away from zero), clamp +-127.
-// The two roundings of phase 4 keep the fused kernel equal to the unfused
-// RMS_NORM then MUL pair ("llama.cpp b10909：Metal后端融合表重构..." restores
-// exactly that fusion).  With no_norm the row is quantised as it is.
+// Fused RMSNorm * g -> Q8 (standalone prologue).  One workgroup per activation
+// row; the steps and their order are those of prologue_dev.h.  Rows of up to
+// 16384 elements take the register form (one pass over x), longer rows the
+// LDS-tree form; both give the same bits.  With no_norm the row is quantised
+// as it is.
 // ---------------------------------------------------------------------------
 constexpr int kPrologueThreads = 256;
-
-__device__ __forceinline__ void load_block32(const float* p, float (&v)[kQK]) {
-  const float4* s = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < kQK / 4; ++i) {
-    const float4 t = s[i];
-    v[4 * i + 0] = t.x;
-    v[4 * i + 1] = t.y;
-    v[4 * i + 2] = t.z;
-    v[4 * i + 3] = t.w;
-  }
-}
 
 __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
     const float* __restrict__ x, int K, const float* __restrict__ g, float eps, int no_norm,
     int P, int8_t* __restrict__ xq, float* __restrict__ xd, int32_t* __restrict__ xs) {
-  extern __shared__ float red[];  // 2 * P floats
-  __shared__ float s_scale;
+  extern __shared__ float red[];  // 2 * P floats (long rows only)
+  __shared__ float s_slot;
+  __shared__ float groups[8];
   const int nb = K / kQK;
   const int64_t row = blockIdx.x;
   const float* xr = x + row * (int64_t)K;
   const int tid = threadIdx.x;
-
-  float s = 1.0f;
-  if (!no_norm) {
-    for (int b = tid; b < P; b += kPrologueThreads) {
-      float acc = 0.0f;
-      if (b < nb) {
-        float v[kQK];
-        load_block32(xr + b * kQK, v);
-#pragma unroll
-        for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(v[j], v[j]));
-      }
-      red[b] = acc;
-    }
-    __syncthreads();
-    float* src = red;
-    float* dst = red + P;
-    for (int h = P / 2; h >= 1; h /= 2) {
-      for (int i = tid; i < h; i += kPrologueThreads) dst[i] = __fadd_rn(src[2 * i], src[2 * i + 1]);
-      __syncthreads();
-      float* t = src;
-      src = dst;
-      dst = t;
-    }
-    if (tid == 0) {
-      const float mean = __fdiv_rn(src[0], (float)K);
-      const float r = sqrt_rn(__fadd_rn(mean, eps));
-      s_scale = __fdiv_rn(1.0f, r);
-    }
-    __syncthreads();
-    s = s_scale;
+  if (K <= kFastPrologueK) {
+    wg_q8_row_fast(xr, g, K, eps, no_norm != 0, xq + row * (int64_t)K, xd + row * nb,
+                   xs ? xs + row * nb : nullptr, groups, tid);
+    return;
   }
-
+  const float s = no_norm ? 1.0f : wg_rms_scale(xr, K, eps, P, red, &s_slot, tid, kPrologueThreads);
   for (int b = tid; b < nb; b += kPrologueThreads) {
-    float v[kQK];
-    load_block32(xr + b * kQK, v);
-    if (!no_norm) {
-      float gv[kQK];
-      load_block32(g + b * kQK, gv);
-#pragma unroll
-      for (int j = 0; j < kQK; ++j) v[j] = __fmul_rn(__fmul_rn(v[j], s), gv[j]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    const float dd = __fdiv_rn(amax, 127.0f);
-    const float id = dd != 0.0f ? __fdiv_rn(1.0f, dd) : 0.0f;
-    int sum = 0;
     uint32_t packed[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
-        qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-        sum += qi;
-        word |= ((uint32_t)qi & 0xFFu) << (8 * k);
-      }
-      packed[i] = word;
-    }
+    float dd;
+    int sum;
+    q8_block_codes(xr, g, b, s, no_norm != 0, packed, dd, sum);
     uint4* dst = reinterpret_cast<uint4*>(xq + row * (int64_t)K + b * kQK);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -195,12 +128,28 @@ __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
 
 hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g, float eps,
                              bool no_norm, int8_t* xq, float* xd, int32_t* xs, hipStream_t s) {
-  const int nb = (int)(K / kQK);
-  int P = 1;
-  while (P < nb) P *= 2;
-  const size_t lds = no_norm ? 0 : 2 * (size_t)P * sizeof(float);
+  const int P = next_pow2_int((int)(K / kQK));
+  const size_t lds = (no_norm || K <= kFastPrologueK) ? 0 : 2 * (size_t)P * sizeof(float);
   hipLaunchKernelGGL(rmsnorm_q8_kernel, dim3((unsigned)B), dim3(kPrologueThreads), lds, s, x,
                      (int)K, g, eps, no_norm ? 1 : 0, P, xq, xd, xs);
+  return hipGetLastError();
+}
+
+// Prologue pass of a grouped launch: workgroup (j, c) quantises row c of the
+// fp32 input of job j into the job's Q8 planes.  Every job has K <= 16384.
+__global__ __launch_bounds__(kPrologueThreads) void group_prologue_kernel(
+    const PrologueJob* __restrict__ jobs) {
+  __shared__ float groups[8];
+  const PrologueJob& J = jobs[blockIdx.x];
+  const int c = blockIdx.y;
+  const int K = J.K, nb = K / kQK;
+  wg_q8_row_fast(J.x + (int64_t)c * K, J.g, K, J.eps, J.raw != 0, J.xq + (int64_t)c * K,
+                 J.xd + (int64_t)c * nb, nullptr, groups, threadIdx.x);
+}
+
+hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B, hipStream_t s) {
+  hipLaunchKernelGGL(group_prologue_kernel, dim3((unsigned)n_jobs, (unsigned)B), dim3(kPrologueThreads), 0,
+                     s, jobs);
   return hipGetLastError();
 }
 

@@ -1,0 +1,211 @@
+// Device-side steps of the RMSNorm * g -> Q8 prologue, shared by the
+// standalone prologue kernel and the GEMV kernel that folds the prologue in.
+// Both therefore produce the same codes and scales bit for bit.
+//
+// Order of operations (each a single IEEE-rounded fp32 operation):
+//   p_b  = sum_{j<32} x_j * x_j over block b, in index order;
+//   the p_b are padded with +0 to P = next_pow2(nb) values and reduced
+//   pairwise, adjacent pairs, level by level (p[i] = p[2i] + p[2i+1]);
+//   s    = 1 / sqrt(ssq / K + eps);
+//   v_j  = (x_j * s) * g_j   (or v = x when the norm is skipped);
+//   per 32-block: d = amax(|v|) / 127, id = 1 / d (0 if d == 0),
+//   q_j = roundf(v_j * id) (halves away from zero), clamped to [-127, 127].
+// The two roundings in v keep the fused RMS_NORM+MUL equal to the unfused
+// pair ("llama.cpp b10909：Metal后端融合表重构..." restores that fusion).
+#pragma once
+
+#include "common.h"
+
+namespace q4q8 {
+
+__device__ __forceinline__ void load_block32(const float* p, float (&v)[kQK]) {
+  const Q4Q8_GLOBAL f32x4* s = gptr(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+  for (int i = 0; i < kQK / 4; ++i) {
+    const f32x4 t = s[i];
+    v[4 * i + 0] = t.x;
+    v[4 * i + 1] = t.y;
+    v[4 * i + 2] = t.z;
+    v[4 * i + 3] = t.w;
+  }
+}
+
+__host__ __device__ __forceinline__ int next_pow2_int(int n) {
+  int p = 1;
+  while (p < n) p *= 2;
+  return p;
+}
+
+// RMS scale s of one row, computed cooperatively by all `nthreads` threads of
+// the workgroup (every thread must call it).  `red` is LDS scratch of 2 * P
+// floats; `s_slot` one LDS float.  Returns s to every thread.
+__device__ __forceinline__ float wg_rms_scale(const float* __restrict__ xr, int K, float eps, int P,
+                                              float* red, float* s_slot, int tid, int nthreads) {
+  const int nb = K / kQK;
+  for (int b = tid; b < P; b += nthreads) {
+    float acc = 0.0f;
+    if (b < nb) {
+      float v[kQK];
+      load_block32(xr + b * kQK, v);
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(v[j], v[j]));
+    }
+    red[b] = acc;
+  }
+  __syncthreads();
+  float* src = red;
+  float* dst = red + P;
+  for (int h = P / 2; h >= 1; h /= 2) {
+    for (int i = tid; i < h; i += nthreads) dst[i] = __fadd_rn(src[2 * i], src[2 * i + 1]);
+    __syncthreads();
+    float* t = src;
+    src = dst;
+    dst = t;
+  }
+  if (tid == 0) {
+    const float mean = __fdiv_rn(src[0], (float)K);
+    const float r = sqrt_rn(__fadd_rn(mean, eps));
+    *s_slot = __fdiv_rn(1.0f, r);
+  }
+  __syncthreads();
+  return *s_slot;
+}
+
+// Q8 codes of block b of one row: packed[8] holds the 32 int8 codes in index
+// order (4 per dword, little-endian), d the fp32 scale, sum the code sum.
+__device__ __forceinline__ void q8_block_codes(const float* __restrict__ xr, const float* __restrict__ g,
+                                               int b, float s, bool no_norm, uint32_t (&packed)[8],
+                                               float& d, int& sum) {
+  float v[kQK];
+  load_block32(xr + b * kQK, v);
+  if (!no_norm) {
+    float gv[kQK];
+    load_block32(g + b * kQK, gv);
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) v[j] = __fmul_rn(__fmul_rn(v[j], s), gv[j]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  d = __fdiv_rn(amax, 127.0f);
+  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
+      qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+      sum += qi;
+      word |= ((uint32_t)qi & 0xFFu) << (8 * k);
+    }
+    packed[i] = word;
+  }
+}
+
+// The same prologue for one row, latency-optimised for a workgroup that
+// folds it into a product kernel (K <= 16384, i.e. at most 2 blocks per
+// thread of a 256-thread workgroup).  Produces bit for bit what
+// wg_rms_scale + q8_block_codes produce:
+//   - each thread loads x (and g) of its blocks once, into registers;
+//   - per-block sums in index order; the first six levels of the pairwise
+//     tree are a 64-lane xor butterfly within each wave (block = 64 * group +
+//     lane, so the butterfly pairs exactly the tree's pairs, and the zero
+//     padding of missing blocks adds exact zeros); one barrier publishes the
+//     per-wave group sums; every thread finishes the tree over the groups
+//     and computes s itself;
+//   - each thread quantises its blocks from the registers it holds.
+// Writes codes to sx [K] (int8), scales to sxd [nb] and, when sxs is not
+// null, code sums to sxs [nb] (LDS or global memory); `groups` is LDS scratch
+// of 8 floats.  Ends with a barrier.
+constexpr int kFastPrologueK = 16384;
+
+__device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
+                                               const float* __restrict__ g, int K, float eps,
+                                               bool raw, int8_t* sx, float* sxd, int* sxs,
+                                               float* groups, int tid) {
+  constexpr int kThreads = 256;
+  const int nb = K / kQK;
+  const int lane = tid & 63, wave = tid >> 6;
+  float xv[2][kQK], gv[2][kQK];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = tid + kThreads * h;
+    if (b < nb) {
+      load_block32(xr + b * kQK, xv[h]);
+      if (!raw) load_block32(g + b * kQK, gv[h]);
+    }
+  }
+  float s = 1.0f;
+  if (!raw) {
+    float gsum[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = tid + kThreads * h;
+      float acc = 0.0f;
+      if (b < nb) {
+#pragma unroll
+        for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(xv[h][j], xv[h][j]));
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) acc = __fadd_rn(acc, __shfl_xor(acc, off, 64));
+      gsum[h] = acc;
+    }
+    if (lane == 0) {
+      groups[wave] = gsum[0];
+      groups[4 + wave] = gsum[1];
+    }
+    __syncthreads();
+    // The tree's levels above the wave groups.  Groups past the padded count
+    // hold +0 and adding +0 to a non-negative sum is exact, so a fixed
+    // three-level tree over all 8 slots gives the bits of the tree over the
+    // next_pow2(nb) / 64 slots for every row length.
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = groups[i];
+#pragma unroll
+    for (int h = 4; h >= 1; h /= 2)
+#pragma unroll
+      for (int i = 0; i < h; ++i) t[i] = __fadd_rn(t[2 * i], t[2 * i + 1]);
+    const float mean = __fdiv_rn(t[0], (float)K);
+    const float r = sqrt_rn(__fadd_rn(mean, eps));
+    s = __fdiv_rn(1.0f, r);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = tid + kThreads * h;
+    if (b < nb) {
+      float v[kQK];
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) v[j] = raw ? xv[h][j] : __fmul_rn(__fmul_rn(xv[h][j], s), gv[h][j]);
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      const float d = __fdiv_rn(amax, 127.0f);
+      const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+      int sum = 0;
+      uint32_t packed[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
+          qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+          sum += qi;
+          word |= ((uint32_t)qi & 0xFFu) << (8 * k);
+        }
+        packed[i] = word;
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(sx + (size_t)b * kQK);
+      dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+      sxd[b] = d;
+      if (sxs) sxs[b] = sum;
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace q4q8

@@ -117,6 +117,87 @@ int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, con
                  const float* xd, int64_t B, float* y, void* stream);
 
 /*
+ * mul_mat_q4q8_rmsnorm -- mul_mat_q4q8 with the activation prologue folded in:
+ * the B fp32 activation rows x [B][K] go through exactly the steps of
+ * q8_quantize_rmsnorm (same codes and scales, bit for bit) inside the product
+ * kernel, so the Q8 planes never travel through HBM.  flags & Q8_NO_NORM
+ * quantises x as it is (g may then be NULL).  Served by the streaming route
+ * only: B <= 4, B * ceil(K / 2048) <= 8 (rounded up to a power of two), and
+ * B*K + 8*B*(K/32) + 32 <= 65536 bytes of staging; otherwise
+ * Q4Q8_E_UNSUPPORTED (call q8_quantize_rmsnorm, then mul_mat_q4q8).
+ *   x [B][K] f32, g [K] f32 (both 16-byte aligned), y [B][M] f32.
+ */
+int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const float* x,
+                         const float* g, float eps, uint32_t flags, int64_t B, float* y, void* stream);
+
+/*
+ * Grouped streaming products.  Decode issues many small independent products
+ * (the Q/K/V projections share one activation row, gate/up another); on this
+ * GPU a kernel launch costs more than streaming a small matrix, so one launch
+ * serves a whole list.  (The GGML backend page's CUDA section gives launch
+ * cost as the reason batch-1 products take the vector kernel.)
+ *
+ * Usage: fill q4q8_gemv_desc records on the host; q4q8_group_build validates
+ * them and writes a table image into caller host memory plus a plan; the
+ * caller copies the image unchanged to device memory (16-byte aligned) once;
+ * mul_mat_q4q8_group then launches from the device table, any number of times
+ * (it is safe to capture in a HIP graph).  Products with M == 0 are dropped.
+ * Every product uses B activation columns (1 <= B <= 4).  Products must not
+ * write overlapping outputs.
+ *
+ * A product's activations are either Q8 planes (xq, xd; x == NULL) or fp32
+ * rows x (xq == NULL) that go through the prologue of q8_quantize_rmsnorm
+ * (g and eps, or flags = Q8_NO_NORM).  Each distinct fp32 input (same x, g,
+ * K, eps and flags) is quantised once per call, by a prologue pass that runs
+ * before the streaming pass, into the caller's device workspace
+ * (plan->workspace_bytes, 16-byte aligned, passed to q4q8_group_build because
+ * the table records point into it).  The workspace belongs to the group:
+ * calls of one group that may overlap in time (different streams) race on it.
+ * Products sharing an input therefore see the same codes, bit for bit those
+ * of q8_quantize_rmsnorm.  One call is one launch, or two when any product
+ * takes fp32 rows.
+ */
+typedef struct q4q8_gemv_desc {
+  const uint8_t* qs;  /* [M][K/2], 16-byte aligned */
+  const uint16_t* d;  /* [M][K/32] */
+  int64_t M;
+  int64_t K;
+  const int8_t* xq;   /* [B][K] Q8 codes, or NULL */
+  const float* xd;    /* [B][K/32] Q8 scales (with xq) */
+  const float* x;     /* [B][K] fp32 activations (when xq == NULL), 16-byte aligned */
+  const float* g;     /* [K] norm weight, 16-byte aligned (with x, unless Q8_NO_NORM) */
+  float eps;
+  uint32_t flags;     /* Q8_NO_NORM or 0 */
+  float* y;           /* [B][M] */
+} q4q8_gemv_desc;
+
+typedef struct q4q8_group_plan {
+  uint32_t magic;          /* set by q4q8_group_build */
+  int32_t B;
+  int32_t n_records;       /* product records in the table image */
+  int32_t n_prologue;      /* distinct fp32 inputs the prologue pass quantises */
+  int64_t n_windows;       /* work windows of the streaming pass (rows of ~32 KiB of weights) */
+  int64_t max_k;           /* largest K of a product */
+  int64_t map_offset;      /* byte offset of the window -> record map in the image */
+  int64_t prologue_offset; /* byte offset of the prologue records in the image */
+  int64_t table_bytes;     /* size of the table image */
+  int64_t workspace_bytes; /* device workspace the prologue pass writes (0 if none) */
+} q4q8_group_plan;
+
+/* Validate n descriptors and fill the plan.  With table_host == NULL only the
+ * plan is computed (table_bytes and workspace_bytes tell the sizes; workspace
+ * may then be NULL); otherwise the table image (table_bytes >=
+ * plan->table_bytes, 16-byte aligned host memory) is written, with the
+ * records pointing into `workspace` (device memory of workspace_bytes >=
+ * plan->workspace_bytes, 16-byte aligned; may be NULL when no product takes
+ * fp32 rows).  Host only; no device work. */
+int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t B, void* workspace,
+                     size_t workspace_bytes, void* table_host, size_t table_bytes,
+                     q4q8_group_plan* plan);
+/* Launch every product of a built group from its device table image. */
+int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan* plan, void* stream);
+
+/*
  * mul_mat_id_q4q8 -- expert-routed product (MUL_MAT_ID).  The scheduler
  * section of the GGML backend page ("调度器三遍切图，pipeline 四个副本") notes
  * that an expert matmul only touches the expert slices actually used; here the

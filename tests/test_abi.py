@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import block_quantized_matmul_q8_amd as q
@@ -146,3 +147,139 @@ def test_product_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of q4q8_gemv_desc / q4q8_group_plan match the C layout."""
+    import subprocess
+    src = tmp_path / "sz.c"
+    src.write_text('#include "q4q8.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(q4q8_gemv_desc), sizeof(q4q8_group_plan),'
+                   ' offsetof(q4q8_gemv_desc, y), offsetof(q4q8_group_plan, workspace_bytes));return 0;}\n')
+    exe = tmp_path / "sz"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    assert int(out[0]) == ctypes.sizeof(q.GemvDesc)
+    assert int(out[1]) == ctypes.sizeof(q.GroupPlan)
+    assert int(out[2]) == q.GemvDesc.y.offset
+    assert int(out[3]) == q.GroupPlan.workspace_bytes.offset
+
+
+def _desc(M=64, K=2048, qs=256, d=256, xq=256, xd=256, x=None, g=None, y=256, flags=0, eps=1e-5):
+    return q.GemvDesc(qs=qs, d=d, M=M, K=K, xq=xq, xd=xd, x=x, g=g, y=y, eps=eps, flags=flags)
+
+
+def _build(descs, B, ws=0, ws_bytes=0):
+    """q4q8_group_build through the C ABI with a fake workspace address."""
+    n = len(descs)
+    arr = (q.GemvDesc * n)(*descs)
+    plan = q.GroupPlan()
+    st = q.lib().q4q8_group_build(arr, n, B, None, 0, None, 0, ctypes.byref(plan))
+    if st != q.Q4Q8_OK:
+        raise q.Q4Q8Error("q4q8_group_build", st, q.q4q8_last_error())
+    image = np.zeros(int(plan.table_bytes) + 16, np.uint8)
+    off = (-image.ctypes.data) % 16
+    image = image[off:off + int(plan.table_bytes)]
+    st = q.lib().q4q8_group_build(arr, n, B, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                                  image.ctypes.data_as(ctypes.c_void_p), int(plan.table_bytes), ctypes.byref(plan))
+    if st != q.Q4Q8_OK:
+        raise q.Q4Q8Error("q4q8_group_build", st, q.q4q8_last_error())
+    return image, plan
+
+
+def test_group_build_layout_is_host_only():
+    WS = 1 << 20
+    ok_q8 = _desc()
+    fused = _desc(xq=None, xd=None, x=512, g=768, K=8192)
+    same_input = _desc(xq=None, xd=None, x=512, g=768, K=8192, M=32, y=4096)   # shares the prologue job
+    other_eps = _desc(xq=None, xd=None, x=512, g=768, K=8192, eps=1e-6, M=8)    # a job of its own
+    raw = _desc(xq=None, xd=None, x=512, g=768, K=8192, flags=q.Q8_NO_NORM, M=8)  # g is ignored: own job
+    image, plan = _build([ok_q8, fused, _desc(M=0), same_input, other_eps, raw], 1, WS, 3 * 9216)
+    # the empty product dropped; a window is 16 rows' worth of 16-byte loads
+    # per lane for each of the 4 waves: 64 rows at K = 2048 (one 32-block per
+    # lane), 16 rows at K = 8192 (four per lane)
+    assert plan.n_records == 5 and plan.B == 1 and plan.n_prologue == 3 and plan.max_k == 8192
+    assert plan.n_windows == 1 + 4 + 2 + 1 + 1
+    # Q8 planes per job: 8192 codes then 256 fp32 scales, 16-byte aligned
+    assert plan.workspace_bytes == 3 * (8192 + 1024)
+    assert plan.map_offset == 5 * 96
+    assert plan.prologue_offset == (plan.map_offset + 4 * plan.n_windows + 15) // 16 * 16
+    assert plan.table_bytes == plan.prologue_offset + 3 * 48
+    recs = image[:plan.map_offset].view(np.int32).reshape(5, 24)
+    ptrs = image[:plan.map_offset].view(np.int64).reshape(5, 12)
+    # record fields: M, K at int32 offsets 14, 15; mode 17; win_begin / n_win at 18, 19
+    assert recs[0, 14] == 64 and recs[0, 15] == 2048 and recs[0, 18] == 0 and recs[0, 19] == 1
+    assert recs[1, 14] == 64 and recs[1, 15] == 8192 and recs[1, 18] == 1 and recs[1, 19] == 4
+    assert (recs[:, 17] == 0).all()           # the streaming pass always reads Q8 planes
+    # xq / xd pointers (int64 slots 2, 3) of the products with fp32 rows point at their job's planes
+    assert ptrs[0, 2] == 256 and ptrs[0, 3] == 256
+    for r, job in ((1, 0), (2, 0), (3, 1), (4, 2)):
+        assert ptrs[r, 2] == WS + job * 9216 and ptrs[r, 3] == WS + job * 9216 + 8192
+        assert ptrs[r, 4] == 0 and ptrs[r, 5] == 0
+    assert image[plan.map_offset:plan.map_offset + 4 * plan.n_windows].view(np.int32).tolist() == \
+        [0] + [1] * 4 + [2] * 2 + [3] + [4]
+    jobs = image[plan.prologue_offset:].view(np.int64).reshape(3, 6)
+    jobs32 = image[plan.prologue_offset:].view(np.int32).reshape(3, 12)
+    jobsf = image[plan.prologue_offset:].view(np.float32).reshape(3, 12)
+    assert jobs[:, 0].tolist() == [512, 512, 512]
+    assert jobs[:, 1].tolist() == [768, 768, 0]                       # raw jobs carry no g
+    assert jobs[:, 2].tolist() == [WS, WS + 9216, WS + 2 * 9216]
+    assert jobs[:, 3].tolist() == [WS + 8192, WS + 9216 + 8192, WS + 2 * 9216 + 8192]
+    assert jobs32[:, 8].tolist() == [8192] * 3 and jobs32[:, 10].tolist() == [0, 0, 1]
+    assert jobsf[0, 9] == np.float32(1e-5) and jobsf[1, 9] == np.float32(1e-6)
+    # B = 2: planes hold two rows
+    _, plan2 = _build([fused], 2, WS, 2 * 8192 + 2 * 1024)
+    assert plan2.workspace_bytes == 2 * 8192 + 2 * 1024
+    # a group of Q8 products needs no workspace
+    _, plan3 = _build([ok_q8], 1)
+    assert plan3.workspace_bytes == 0 and plan3.n_prologue == 0
+
+
+def test_group_build_validation_is_host_only():
+    bad = [
+        ([_desc(K=100)], 1, q.Q4Q8_E_ARG),
+        ([_desc(qs=264)], 1, q.Q4Q8_E_ALIGN),
+        ([_desc(xq=None, xd=None)], 1, q.Q4Q8_E_ARG),               # neither xq nor x
+        ([_desc(xd=None)], 1, q.Q4Q8_E_ARG),                        # xq without xd
+        ([_desc(xq=None, xd=None, x=512, g=None)], 1, q.Q4Q8_E_ARG),  # norm without g
+        ([_desc(xq=None, xd=None, x=520, g=768)], 1, q.Q4Q8_E_ALIGN),
+        ([_desc(flags=4)], 1, q.Q4Q8_E_ARG),
+        ([_desc()], 5, q.Q4Q8_E_UNSUPPORTED),                       # B beyond the streaming kernel
+        ([_desc(K=32768)], 1, q.Q4Q8_E_UNSUPPORTED),                # K beyond the register blocking
+        ([_desc(xq=None, xd=None, x=512, g=768, K=16384)], 4, q.Q4Q8_E_UNSUPPORTED),
+    ]
+    for descs, B, code in bad:
+        with pytest.raises(q.Q4Q8Error) as ei:
+            _build(descs, B, 1 << 20, 1 << 20)
+        assert ei.value.status == code, (descs[0].K, B)
+    fused = [_desc(xq=None, xd=None, x=512, g=768)]
+    for ws, nbytes, code in ((0, 0, q.Q4Q8_E_ARG),            # fp32 rows need a workspace
+                             (1 << 20, 2048 + 255, q.Q4Q8_E_ARG),  # too small
+                             ((1 << 20) + 8, 4096, q.Q4Q8_E_ALIGN)):
+        with pytest.raises(q.Q4Q8Error) as ei:
+            _build(fused, 1, ws, nbytes)
+        assert ei.value.status == code
+
+
+def test_group_launch_rejects_foreign_plans():
+    L = q.lib()
+    plan = q.GroupPlan()
+    assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(plan), None) == q.Q4Q8_E_ARG
+    _, good = _build([_desc()], 1)
+    assert L.mul_mat_q4q8_group(None, ctypes.byref(good), None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q4q8_group(ctypes.c_void_p(264), ctypes.byref(good), None) == q.Q4Q8_E_ALIGN
+    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 7)):
+        bad = q.GroupPlan.from_buffer_copy(good)
+        setattr(bad, field, value)
+        assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, field
+
+
+def test_fused_single_validation():
+    L = q.lib()
+    p = ctypes.c_void_p(256)
+    f = ctypes.c_float(1e-5)
+    # g missing without Q8_NO_NORM; misaligned x; too large for the folded-in prologue
+    assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, None, f, 0, 1, p, None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, ctypes.c_void_p(260), p, f, 0, 1, p, None) == q.Q4Q8_E_ALIGN
+    assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 16384, p, p, f, 0, 4, p, None) == q.Q4Q8_E_UNSUPPORTED
+    assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, p, f, 2, 1, p, None) == q.Q4Q8_E_ARG

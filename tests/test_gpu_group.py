@@ -1,0 +1,166 @@
+"""GPU parity of the folded-in prologue product (mul_mat_q4q8_rmsnorm) and of
+grouped streaming launches (mul_mat_q4q8_group) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("block_quantized_matmul_q8_amd")
+
+
+def _weights(seed, layer, matrix, M, K):
+    w = workloads.weight(seed, layer, matrix, M, K)
+    qs, d = oracle.q4_quantize(w)
+    return qs, d
+
+
+def _ref(qs, d, x, g, no_norm=False):
+    xq, xd, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS, no_norm=no_norm)
+    y, _ = oracle.mul_mat(qs, d, xq, xd, nthreads=16, want_y64=False)
+    return y
+
+
+@pytest.mark.parametrize("M,K,B", [(1, 32, 1), (7, 64, 1), (256, 512, 1), (130, 1408, 2), (1000, 2048, 1),
+                                   (300, 4096, 3), (64, 8192, 1), (200, 14336, 1), (96, 2048, 4),
+                                   (40, 8192, 2)])
+def test_fused_single(M, K, B):
+    qs, d = _weights(41, 0, M % 5, M, K)
+    x = workloads.activation(41, 0, 0, B, K)
+    g = workloads.norm_weight(41, 0, 0, K)
+    y = q.mul_mat_q4q8_rmsnorm(to_dev(qs), to_dev(d.view(np.int16)), to_dev(x), to_dev(g), workloads.RMS_EPS)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), _ref(qs, d, x, g), f"M={M} K={K} B={B}")
+
+
+@pytest.mark.parametrize("M,K,B,raw", [(256, 512, 1, False), (130, 1408, 2, False), (1000, 2048, 1, False),
+                                       (300, 4096, 3, False), (64, 8192, 1, False), (200, 14336, 1, False),
+                                       (96, 2048, 4, False), (77, 2048, 1, True), (40, 8192, 2, True)])
+def test_fused_codes_equal_standalone_prologue(M, K, B, raw):
+    """The folded-in prologue produces the codes of the standalone prologue
+    bit for bit: with identical codes the product kernel does identical
+    arithmetic in both modes, so the outputs must agree bit for bit."""
+    qs, d = _weights(44, 0, M % 5, M, K)
+    x = workloads.activation(44, 0, 1, B, K) * np.float32(2.5)
+    g = workloads.norm_weight(44, 0, 1, K)
+    qs_d, d_d, x_d = to_dev(qs), to_dev(d.view(np.int16)), to_dev(x)
+    g_d = None if raw else to_dev(g)
+    flags = q.Q8_NO_NORM if raw else 0
+    y_f = q.mul_mat_q4q8_rmsnorm(qs_d, d_d, x_d, g_d, workloads.RMS_EPS, flags=flags)
+    xq, xd, _ = q.q8_quantize_rmsnorm(x_d, g_d, workloads.RMS_EPS, flags=flags)
+    y_u = q.mul_mat_q4q8(qs_d, d_d, xq, xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_f.cpu().numpy().view(np.uint32), y_u.cpu().numpy().view(np.uint32))
+    xq_o, _, _ = oracle.q8_quantize_rmsnorm(x, None if raw else g, workloads.RMS_EPS, no_norm=raw)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+
+
+def test_fused_no_norm_and_special_rows(hand_examples):
+    M, K = 48, 1408
+    qs, d = _weights(42, 0, 0, M, K)
+    x = workloads.activation(42, 0, 0, 3, K) * np.float32(4.0)
+    x[1] = 0.0                      # all-zero row: codes 0, output 0
+    y = q.mul_mat_q4q8_rmsnorm(to_dev(qs), to_dev(d.view(np.int16)), to_dev(x), None, 0.0, flags=q.Q8_NO_NORM)
+    torch.cuda.synchronize()
+    ref = _ref(qs, d, x, None, no_norm=True)
+    assert_close(y.cpu().numpy(), ref)
+    assert np.all(y.cpu().numpy()[1] == 0.0)
+    # hand example E5 through the folded-in prologue: y = -15.999921 exactly
+    e5 = hand_examples["E5"]
+    w = np.array([[-8 + (j % 16) for j in range(32)]], np.float32)
+    qs1, d1 = oracle.q4_quantize(w)
+    y1 = q.mul_mat_q4q8_rmsnorm(to_dev(qs1), to_dev(d1.view(np.int16)), to_dev(np.ones((1, 32), np.float32)),
+                                to_dev(np.ones(32, np.float32)), 1e-5)
+    torch.cuda.synchronize()
+    assert int(y1.cpu().numpy().view(np.uint32)[0, 0]) == int(e5["y_bits"], 16)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_group_mixed(B):
+    """Products of different K classes and both activation modes in one group."""
+    dev = torch.device("cuda:0")
+    specs = [(512, 2048, "q8"), (130, 1408, "norm"), (64, 8192, "norm"), (300, 4096, "raw"),
+             (1, 32, "q8"), (2048, 2048, "norm"), (33, 14336, "q8")]
+    problems, refs = [], []
+    for i, (M, K, mode) in enumerate(specs):
+        if B * max(1, -(-K // 2048)) > 8:
+            continue
+        qs, d = _weights(43, 1, i, M, K)
+        x = workloads.activation(43, 1, i, B, K)
+        g = workloads.norm_weight(43, 1, i, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        p = {"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y}
+        if mode == "q8":
+            xq, xd, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+            p.update(xq=to_dev(xq), xd=to_dev(xd))
+            ref, _ = oracle.mul_mat(qs, d, xq, xd, nthreads=16, want_y64=False)
+        elif mode == "norm":
+            p.update(x=to_dev(x), g=to_dev(g), eps=workloads.RMS_EPS)
+            ref = _ref(qs, d, x, g)
+        else:
+            p.update(x=to_dev(x), flags=q.Q8_NO_NORM)
+            ref = _ref(qs, d, x, None, no_norm=True)
+        problems.append(p)
+        refs.append(ref)
+    grp = q.Group(problems, B=B)
+    assert grp.plan.n_prologue == sum(1 for p in problems if "x" in p)
+    for rep in range(2):          # the same device table launched twice
+        for p in problems:
+            p["y"].fill_(float("nan"))
+        grp()
+        torch.cuda.synchronize()
+        for p, ref in zip(problems, refs):
+            assert_close(p["y"].cpu().numpy(), ref, f"rep {rep} M={p['qs'].shape[0]}")
+    # the group's prologue pass gives the codes of the single-product calls,
+    # so the outputs agree bit for bit
+    for p in problems:
+        if "x" in p:
+            raw = p.get("flags", 0) == q.Q8_NO_NORM
+            single = q.mul_mat_q4q8_rmsnorm(p["qs"], p["d"], p["x"], None if raw else p["g"], workloads.RMS_EPS,
+                                            flags=p.get("flags", 0))
+        else:
+            single = q.mul_mat_q4q8(p["qs"], p["d"], p["xq"], p["xd"])
+        torch.cuda.synchronize()
+        assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
+
+
+def test_group_full_llama_1b_layer_in_a_graph():
+    """One Llama-3.2-1B layer (seven matrices, four activation rows with their
+    own norm weights) as one group with the prologue folded in, captured in a
+    HIP graph and replayed; every replay matches the oracle."""
+    dev = torch.device("cuda:0")
+    layer = workloads.LLAMA_3_2_1B
+    xs = {s: workloads.activation(0, 3, s, 1, K) for s, K in workloads.slot_k(layer).items()}
+    gs = {s: workloads.norm_weight(0, 3, s, K) for s, K in workloads.slot_k(layer).items()}
+    xs_d = {s: to_dev(v) for s, v in xs.items()}
+    gs_d = {s: to_dev(v) for s, v in gs.items()}
+    problems, refs = [], []
+    for mi, m in enumerate(layer):
+        qs, d = _weights(0, 3, mi, m.M, m.K)
+        y = torch.zeros((1, m.M), dtype=torch.float32, device=dev)
+        problems.append({"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": xs_d[m.slot],
+                         "g": gs_d[m.slot], "eps": workloads.RMS_EPS})
+        refs.append(_ref(qs, d, xs[m.slot], gs[m.slot]))
+    grp = q.Group(problems, B=1)
+    assert grp.plan.n_prologue == 4           # Q/K/V share a row, gate/up another
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        grp()                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp()
+    for rep in range(3):
+        for p in problems:
+            p["y"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, ref, m in zip(problems, refs, layer):
+            assert_close(p["y"].cpu().numpy(), ref, f"replay {rep} {m.name}")

@@ -52,8 +52,8 @@ def test_q4_quantize_wide_range_and_subnormal_scales():
     assert np.array_equal(f16_bits(d), d_o)
 
 
-@pytest.mark.parametrize("B,K", [(1, 32), (5, 512), (3, 1408), (4, 2048), (2, 8192), (1, 14336),
-                                 (2048, 4096), (16, 131072)])
+@pytest.mark.parametrize("B,K", [(1, 32), (5, 512), (3, 1408), (4, 2048), (2, 8192), (3, 8224), (1, 14336),
+                                 (2, 16384), (2, 16416), (2048, 4096), (16, 131072)])
 def test_q8_rmsnorm_bit_exact(B, K):
     x = workloads.activation(12, B % 89, K % 83, B, K)
     gw = workloads.norm_weight(12, 0, K % 83, K)
