@@ -5,6 +5,8 @@ Pinned against: the hand-derived examples in tests/golden/hand_examples.json
 closed forms for constant rows, and an fp64 RMS normalisation within the
 fp32 error bound of the fixed reduction order.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -199,3 +201,20 @@ def test_fused_equals_unfused(K):
     b = oracle.q8_quantize_rmsnorm(x, g, 1e-5)
     for u, w in zip(a, b):
         assert np.array_equal(u, w)
+
+
+def test_golden_rmsnorm_examples_rederived_exactly(hand_examples):
+    """The stored E5 / E6 values follow from the stated fp32 steps carried out
+    on exact rationals (tests/golden/derive_hand_examples.py), independently
+    of the oracle."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(__file__), "golden", "derive_hand_examples.py")
+    spec = importlib.util.spec_from_file_location("derive_hand_examples", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    for name, xv in (("E5", 1), ("E6", 2)):
+        r = mod.constant_row(xv)
+        assert mod.bits(r["s"]) == hand_examples[name]["s_bits"]
+        assert mod.bits(r["d"]) == hand_examples[name]["xd_bits"]
+        assert r["v_times_id"] == hand_examples[name]["code"]
+    assert mod.bits(mod.e5_y(mod.constant_row(1)["d"], hand_examples["E5"]["I"])) == hand_examples["E5"]["y_bits"]
