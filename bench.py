@@ -410,40 +410,16 @@ def bench_decode_8b(args, dev):
     n_layers = 8
     for B in (1, 2, 4, 8):
         model = DecodeModel(wl.LLAMA_3_8B, n_layers, B, 1, dev)
-        if B <= 4:
-            probs = []
-            for l in range(n_layers):
-                probs += model.problems(l)
-            try:
-                grp = q.Group(probs, B=B)
-                fn = lambda: grp()
-                route = "grouped: prologue pass + streaming pass"
-            except q.Q4Q8Error:
-                grp = None
-        else:
-            grp = None
-        if grp is None:
-            bufs = {}
-            for l in range(n_layers):
-                for slot, (x, gw) in model.acts[l].items():
-                    K = x.shape[1]
-                    bufs[(l, slot)] = (x, gw, torch.empty((B, K), dtype=torch.int8, device=dev),
-                                       torch.empty((B, K // 32), dtype=torch.float32, device=dev))
-
-            def fn():
-                for l in range(n_layers):
-                    for slot in model.acts[l]:
-                        x, gw, xq, xd = bufs[(l, slot)]
-                        q.q8_quantize_rmsnorm(x, gw, 1e-5, xq=xq, xd=xd)
-                    for m in model.mats[l]:
-                        _, _, xq, xd = bufs[(l, m["slot"])]
-                        q.mul_mat_q4q8(m["qs"], m["d"], xq, xd, y=m["y"])
-            route = "prologue + mul_mat per matrix (auto route)"
-        g = capture(fn)
-        ms, _ = time_graph(g, max(5, args.steps // 2), 2)
+        probs = []
+        for l in range(n_layers):
+            probs += model.problems(l)
+        grp = q.Group(probs, B=B)
+        fn = lambda: grp()
+        route = "grouped: prologue pass + streaming pass"
+        ms, _ = time_direct(fn, max(5, args.steps // 2), 2)
         out[f"B={B}"] = {"GB/s": round(model.step_bytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 4),
-                         "route": route}
-        del g, model
+                         "hbm_frac": round(model.step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "route": route}
+        del grp, model
         torch.cuda.empty_cache()
     return {"layers": n_layers, **out}
 

@@ -255,7 +255,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   memset(plan, 0, sizeof *plan);
   if (n <= 0 || n > (1 << 20)) return fail(Q4Q8_E_ARG, "n = %d must be in [1, 2^20]", n);
   if (!descs) return fail(Q4Q8_E_ARG, "null pointer argument");
-  if (B < 1 || B > 4) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld: grouped products take 1 <= B <= 4", (long long)B);
+  if (B < 1 || B > 8) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld: grouped products take 1 <= B <= 8", (long long)B);
   for (int32_t i = 0; i < n; ++i) {
     const q4q8_gemv_desc& e = descs[i];
     int st;
@@ -404,7 +404,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   if (plan->n_records == 0) return ok();
   if (!table_dev) return fail(Q4Q8_E_ARG, "null table");
   if (!aligned(table_dev, 16)) return fail(Q4Q8_E_ALIGN, "table must be 16-byte aligned");
-  if (plan->n_records < 0 || plan->B < 1 || plan->B > 4 || plan->n_windows < plan->n_records ||
+  if (plan->n_records < 0 || plan->B < 1 || plan->B > 8 || plan->n_windows < plan->n_records ||
       plan->n_windows > INT32_MAX || plan->n_prologue < 0 || plan->n_prologue > plan->n_records ||
       plan->max_k < q4q8::kQK || plan->max_k % q4q8::kQK != 0 ||
       !q4q8::gemv_supported(1, plan->max_k, plan->B) ||
@@ -420,7 +420,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
     g_counts[3].fetch_add(1, std::memory_order_relaxed);
     st = launched(q4q8::launch_group_prologue(
                       reinterpret_cast<const q4q8::PrologueJob*>(base + plan->prologue_offset),
-                      plan->n_prologue, plan->B, s),
+                      plan->n_prologue, plan->B, plan->max_k, s),
                   "mul_mat_q4q8_group (prologue pass)");
     if (st) return st;
   }

@@ -136,7 +136,7 @@ struct alignas(16) PrologueJob {
   const float* g;  // [K] (null when raw)
   int8_t* xq;      // [B][K]
   float* xd;       // [B][K/32]
-  int32_t K;       // <= 16384
+  int32_t K;
   float eps;
   int32_t raw;     // quantise x as it is
   int32_t pad;
@@ -163,7 +163,7 @@ Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, c
                                          float eps, bool no_norm, int8_t* xq, float* xd,
                                          int32_t* xs, hipStream_t s);
 Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B,
-                                             hipStream_t s);
+                                             int64_t max_k, hipStream_t s);
 Q4Q8_HIDDEN hipError_t launch_gemm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
                                    const int8_t* xq, const float* xd, int64_t B, float* y,
                                    int32_t* I, hipStream_t s);

@@ -1,25 +1,31 @@
 // Streaming Q4 x Q8 matrix x vector kernel for gfx950 (the decode route; the
 // mmvq role in "GGML：Backend 抽象与硬件加速", section "CUDA：mmvq、mmq、cublas
-// 三条矩阵路": batch-1 decode is a quantised matrix x vector product, and a
-// dedicated vector kernel is cheaper to launch than the matrix path).
+// 三条矩阵路": decode is a quantised matrix x vector product, and a dedicated
+// vector kernel is cheaper to launch than the matrix path).
 //
 // One persistent kernel serves a single product and a grouped launch over
 // many products (a device table of GemvProblem records plus a window ->
 // record map).  Per product segment of a workgroup:
-//   - the weight loads of each wave's first row group are issued first, so
-//     they are in flight while the activations are prepared;
-//   - activations come either as Q8 planes (loaded straight into registers)
-//     or as fp32 x + norm weight g, in which case the workgroup runs the
-//     RMSNorm * g -> Q8 prologue itself (prologue_dev.h, bit-identical to the
-//     standalone prologue) and stages the codes through LDS;
-//   - lane l holds the activation codes of blocks l, l + 64, ... in
-//     registers for the whole tile; each row is streamed with one 16-byte
-//     load per lane per 64 blocks (a whole 32-block, 1 KiB per wave load,
-//     fully coalesced), nibbles unpacked in registers, v_dot4_i32_i8 on the
-//     unsigned codes with the offset removed through the code sums
+//   - lane l holds the activation codes of blocks kb0 + l, kb0 + l + 64, ...
+//     in registers for the whole segment; each row is streamed with one
+//     16-byte load per lane per 64 blocks (a whole 32-block, 1 KiB per wave
+//     load, fully coalesced), nibbles unpacked in registers, v_dot4_i32_i8 on
+//     the unsigned codes with the offset removed through the code sums
 //     (I = sum q x - 8 sum x, exact), fp32 fma for the block scale;
-//   - RU rows are in flight per wave (the next group is loaded while the
-//     current one is computed) and finished with one multi-row butterfly.
+//   - when B columns times the blocks per lane would not fit in registers,
+//     K is split over S = 2 or 4 waves that stream the same rows (wave part
+//     kp covers blocks kb0 = kp * 64 * J onwards); their per-row partial sums
+//     meet in LDS and are added in part order;
+//   - activations come either as Q8 planes (loaded straight into registers)
+//     or, for a single product, as fp32 x + norm weight g, in which case the
+//     workgroup runs the RMSNorm * g -> Q8 prologue itself (prologue_dev.h,
+//     bit-identical to the standalone prologue) and stages the codes through
+//     LDS;
+//   - RU rows are in flight per wave in each of two register buffers (one is
+//     computed while the other loads) and finished with one multi-row
+//     butterfly.
+// Column counts are padded to BT in {1, 2, 4, 8}; the true count B is a
+// launch argument (columns past B read nothing and store nothing).
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -29,6 +35,7 @@
 namespace q4q8 {
 
 constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr size_t kGemvMaxLds = 64 * 1024;
 
 // Butterfly sum of N values per lane over the 64 lanes.  Lane L returns the
@@ -78,34 +85,69 @@ __device__ __forceinline__ int code_sum8(const i32x4 a, const i32x4 b) {
 #define Q4Q8_GEMV_ROWS_IN_FLIGHT 16  // 16-byte loads per lane in flight per row group
 #endif
 
-// Rows a wave keeps in flight per group for B columns and J blocks per lane.
-__host__ __device__ constexpr int gemv_rows_per_wave(int B, int J) {
-  return B <= 2 ? (Q4Q8_GEMV_ROWS_IN_FLIGHT / J > 0 ? Q4Q8_GEMV_ROWS_IN_FLIGHT / J : 1)
-                : (Q4Q8_GEMV_ROWS_IN_FLIGHT / J / 2 > 0 ? Q4Q8_GEMV_ROWS_IN_FLIGHT / J / 2 : 1);
+// Padded column count of the kernel instance serving B columns.
+__host__ __device__ constexpr int gemv_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+// Activation blocks (columns x blocks per lane) a lane may hold.
+__host__ __device__ constexpr int gemv_act_budget(int BT) { return BT <= 4 ? 8 : 16; }
+
+// Rows a wave keeps in flight per group for BT columns and J blocks per lane.
+__host__ __device__ constexpr int gemv_rows_per_wave(int BT, int J) {
+  return Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) > 0
+             ? Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4)
+             : 1;
 }
 
-template <int B, int J>
+// Register blocking class of a product: J blocks per lane, K split over S
+// waves (the smallest S whose blocks fit the register budget).  J == 0: the
+// streaming kernel does not serve the shape.
+struct GemvClass {
+  int J, S;
+};
+__host__ __device__ inline GemvClass gemv_class_of(int64_t K, int64_t B) {
+  if (B < 1 || B > 8 || K < kQK) return {0, 0};
+  const int64_t nb = K / kQK;
+  const int BT = gemv_bt((int)B);
+  for (int S = 1; S <= 4; S *= 2) {
+    const int64_t per = (nb + 64 * S - 1) / (64 * S);
+    const int J = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+    if (J <= 8 && BT * J <= gemv_act_budget(BT)) return {J, S};
+  }
+  return {0, 0};
+}
+
+template <int BT, int J, int S>
 struct GemvShape {
-  static constexpr int RU = gemv_rows_per_wave(B, J);
-  static constexpr int WIN = 4 * RU;  // rows per window (one row group per wave)
-  static constexpr int NV = RU * B;   // values reduced per row group
+  static constexpr int RU = gemv_rows_per_wave(BT, J);
+  static constexpr int SLOTS = kGemvWaves / S;  // row groups per window
+  static constexpr int WIN = SLOTS * RU;        // rows per window
+  static constexpr int NV = RU * BT;            // values reduced per row group
   static constexpr int NP = pow2_ceil_c(NV);
   static constexpr int SHIFT = 6 - ilog2_c(NP);
 };
+constexpr int kMaxNP = 32;  // largest NP over all classes (checked below)
 
-__host__ __device__ __forceinline__ int blocks_per_lane_of(int K) {
-  const int j = (K / kQK + kWave - 1) / kWave;
-  return j <= 1 ? 1 : j <= 2 ? 2 : j <= 4 ? 4 : j <= 8 ? 8 : 16;
-}
+// LDS exchange of the K-split partial sums: two parities x waves x values.
+struct SplitScratch {
+  float v[2][kGemvWaves][kMaxNP];
+};
 
 // Streams windows [wl0, wl1) of product P (window i = rows i*WIN .. +WIN;
-// wave w takes the RU rows at w*RU of each window) with J blocks per lane.
-template <int B, int J, bool FOLD, bool WRITE_I>
-__device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int wl1,
-                                             unsigned char* smem, int32_t* __restrict__ Iout) {
-  using S = GemvShape<B, J>;
-  constexpr int RU = S::RU, WIN = S::WIN, NV = S::NV, NP = S::NP, SHIFT = S::SHIFT;
+// the waves of row slot rs take the RU rows at rs*RU of each window, wave
+// part kp its share of K) with J blocks per lane.  `parity` alternates over
+// every compute of the workgroup (also across products) so that a K-split
+// exchange never overwrites values a slower wave has yet to read.
+template <int BT, int J, int S, bool FOLD, bool WRITE_I>
+__device__ __forceinline__ void gemv_segment(const GemvProblem& P, int B, int wl0, int wl1,
+                                             unsigned char* smem, SplitScratch* split, int& parity,
+                                             int32_t* __restrict__ Iout) {
+  using Sh = GemvShape<BT, J, S>;
+  constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT;
+  static_assert(NP <= kMaxNP, "split scratch too small");
+  static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rs = wave / S, kp = wave % S;
+  const int kb0 = kp * kWave * J;
   const int M = P.M, K = P.K, nb = K >> 5;
   const int64_t row_bytes = K >> 1;
 
@@ -125,7 +167,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
       const int rowc = min(row0 + r, row_last);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int bc = min(lane + kWave * j, nb - 1);
+        const int bc = min(kb0 + lane + kWave * j, nb - 1);
         w[r][j] = __builtin_nontemporal_load(
             &gptr(reinterpret_cast<const u32x4*>(P.qs))[rowc * (row_bytes / 16) + bc]);
         dw[r][j] = __builtin_nontemporal_load(&gptr(P.d)[(int64_t)rowc * nb + bc]);
@@ -135,33 +177,33 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
 
   u32x4 wA[RU][J], wB[RU][J];
   uint32_t dA[RU][J], dB[RU][J];
-  i32x4 xa[B][J], xb[B][J];
-  float xdr[B][J];
-  int xsr[B][J];
+  i32x4 xa[BT][J], xb[BT][J];
+  float xdr[BT][J];
+  int xsr[BT][J];
   if constexpr (!FOLD) {
     // Q8 planes: the activation loads go first (they are small and mostly
     // L2-resident), then the first two windows; loads complete in issue
     // order, so the first compute waits for the activations and window A
     // only while window B is already in flight.
 #pragma unroll
-    for (int c = 0; c < B; ++c)
+    for (int c = 0; c < BT; ++c)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int b = lane + kWave * j;
-        const int bc = min(b, nb - 1);
+        const int cc = min(c, B - 1);
+        const int bc = min(kb0 + lane + kWave * j, nb - 1);
         const Q4Q8_GLOBAL i32x4* src =
-            gptr(reinterpret_cast<const i32x4*>(P.xq + (int64_t)c * K + (int64_t)bc * kQK));
+            gptr(reinterpret_cast<const i32x4*>(P.xq + (int64_t)cc * K + (int64_t)bc * kQK));
         xa[c][j] = src[0];
         xb[c][j] = src[1];
-        xdr[c][j] = gptr(P.xd)[(int64_t)c * nb + bc];
+        xdr[c][j] = gptr(P.xd)[(int64_t)cc * nb + bc];
       }
-    load_group(wl0 * WIN + wave * RU, wA, dA);
-    load_group((wl0 + 1) * WIN + wave * RU, wB, dB);
+    load_group(wl0 * WIN + rs * RU, wA, dA);
+    load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
 #pragma unroll
-    for (int c = 0; c < B; ++c)
+    for (int c = 0; c < BT; ++c)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const bool valid = lane + kWave * j < nb;
+        const bool valid = c < B && kb0 + lane + kWave * j < nb;
         const i32x4 zero = {0, 0, 0, 0};
         xa[c][j] = valid ? xa[c][j] : zero;
         xb[c][j] = valid ? xb[c][j] : zero;
@@ -173,7 +215,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
     // workgroup quantises the activation rows (prologue_dev.h, the
     // register/butterfly form of the same steps) and stages the codes
     // through LDS; window B follows.
-    load_group(wl0 * WIN + wave * RU, wA, dA);
+    load_group(wl0 * WIN + rs * RU, wA, dA);
     int8_t* sx = reinterpret_cast<int8_t*>(smem);                  // [B][K]
     float* sxd = reinterpret_cast<float*>(smem + (size_t)B * K);   // [B][nb]
     int* sxs = reinterpret_cast<int*>(sxd + B * nb);               // [B][nb]
@@ -183,11 +225,11 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
       wg_q8_row_fast(P.x + (int64_t)c * K, P.g, K, P.eps, raw, sx + (size_t)c * K, sxd + c * nb,
                      sxs + c * nb, groups, tid);
 #pragma unroll
-    for (int c = 0; c < B; ++c)
+    for (int c = 0; c < BT; ++c)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int b = lane + kWave * j;
-        if (b < nb) {
+        if (c < B && b < nb) {
           const i32x4* src = reinterpret_cast<const i32x4*>(sx + (size_t)c * K + (size_t)b * kQK);
           xa[c][j] = src[0];
           xb[c][j] = src[1];
@@ -200,10 +242,11 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
           xsr[c][j] = 0;
         }
       }
-    load_group((wl0 + 1) * WIN + wave * RU, wB, dB);
+    load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
   }
 
-  // One row group: block sums, scale, multi-row reduction, store.
+  // One row group: block sums, scale, multi-row reduction, store (through
+  // the part exchange when K is split).
   auto compute_group = [&](int row0, const u32x4 (&w)[RU][J], const uint32_t (&dw)[RU][J]) {
     float acc[NP];
 #pragma unroll
@@ -214,28 +257,39 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
       for (int r = 0; r < RU; ++r) {
         const float dwf = f16_bits_to_f32((uint16_t)dw[r][j]);
 #pragma unroll
-        for (int c = 0; c < B; ++c) {
+        for (int c = 0; c < BT; ++c) {
           const int I = dot_block(w[r][j], xa[c][j], xb[c][j]) - xsr[c][j];
-          acc[r * B + c] = __builtin_fmaf((float)I, dwf * xdr[c][j], acc[r * B + c]);
+          acc[r * BT + c] = __builtin_fmaf((float)I, dwf * xdr[c][j], acc[r * BT + c]);
           if (WRITE_I) {
-            const int b = lane + kWave * j;
+            const int b = kb0 + lane + kWave * j;
             const int row = row0 + r;
-            if (b < nb && row <= row_last) Iout[((int64_t)c * M + row) * nb + b] = I;
+            if (c < B && b < nb && row <= row_last) Iout[((int64_t)c * M + row) * nb + b] = I;
           }
         }
       }
     const float v = multi_reduce<NP>(acc, lane);
     const int k = lane >> SHIFT;
-    if ((lane & ((1 << SHIFT) - 1)) == 0 && k < NV) {
-      const int row = row0 + k / B;
-      if (row <= row_last) gptr_w(P.y)[(int64_t)(k % B) * M + row] = v;
+    const bool holder = (lane & ((1 << SHIFT) - 1)) == 0 && k < NV;
+    const int row = row0 + k / BT, c = k % BT;
+    if constexpr (S == 1) {
+      if (holder && c < B && row <= row_last) gptr_w(P.y)[(int64_t)c * M + row] = v;
+    } else {
+      if (holder) split->v[parity][wave][k] = v;
+      __syncthreads();
+      if (kp == 0 && holder && c < B && row <= row_last) {
+        float t = v;
+#pragma unroll
+        for (int q = 1; q < S; ++q) t += split->v[parity][wave + q][k];
+        gptr_w(P.y)[(int64_t)c * M + row] = t;
+      }
+      parity ^= 1;
     }
   };
 
   // Ping-pong over two register buffers: while one window is computed the
   // other is in flight; a buffer is refilled right after it is consumed.
   for (int wi = wl0; wi < wl1; wi += 2) {
-    const int r0 = wi * WIN + wave * RU;
+    const int r0 = wi * WIN + rs * RU;
     compute_group(r0, wA, dA);
     load_group(r0 + 2 * WIN, wA, dA);
     if (wi + 1 >= wl1) break;
@@ -249,12 +303,12 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, int wl0, int 
 // workgroup carries the same load from start to end and the launch has no
 // rounds of short-lived workgroups.  A share spans few products; the next
 // product's record is requested when a segment starts, so it is at hand when
-// the segment ends.  The grouped instance serves products of every blocking
-// class up to JMAX (the workgroup dispatches uniformly on each product's own
-// J) and reads Q8 planes only; single-product instances compile their own
-// class only.  The grouped and single-product forms are separate instances
-// because selecting between the kernel argument and the table at run time
-// would make every access a generic flat access.
+// the segment ends.  The grouped instance serves every blocking class of its
+// column width (the workgroup dispatches uniformly on each product's class)
+// and reads Q8 planes only; single-product instances compile their own class
+// only.  The grouped and single-product forms are separate instances because
+// selecting between the kernel argument and the table at run time would make
+// every access a generic flat access.
 #ifndef Q4Q8_GEMV_MIN_WG_PER_CU
 #define Q4Q8_GEMV_MIN_WG_PER_CU 1
 #endif
@@ -266,19 +320,44 @@ enum GemvKind : int {
   kKindBlockSums = 3,  // one product, Q8 planes, per-block sums written out
 };
 
-template <int B, int JMAX, int KIND>
-__global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_kernel(GemvProblem p0,
-                                                            const GemvProblem* __restrict__ table,
-                                                            const int32_t* __restrict__ win_map,
-                                                            int n_windows,
-                                                            int32_t* __restrict__ Iout) {
+// Calls f.template operator()<J, S>() for the blocking class (J, S) of
+// column width BT; every class gemv_class_of can return for BT is listed.
+template <int BT, typename F>
+__host__ __device__ __forceinline__ void dispatch_class(int J, int S, F&& f) {
+  if constexpr (BT == 1) {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 1 && J == 4) f.template operator()<4, 1>();
+    if (S == 1 && J == 8) f.template operator()<8, 1>();
+    if (S == 2 && J == 8) f.template operator()<8, 2>();
+    if (S == 4 && J == 8) f.template operator()<8, 4>();
+  } else if constexpr (BT == 2) {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 1 && J == 4) f.template operator()<4, 1>();
+    if (S == 2 && J == 4) f.template operator()<4, 2>();
+    if (S == 4 && J == 4) f.template operator()<4, 4>();
+  } else {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 2 && J == 2) f.template operator()<2, 2>();
+    if (S == 4 && J == 2) f.template operator()<2, 4>();
+  }
+}
+
+template <int BT, int J, int S, int KIND>
+__global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_kernel(
+    GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ win_map,
+    int n_windows, int B, int32_t* __restrict__ Iout) {
   constexpr bool GROUPED = KIND == kKindGroup;
   constexpr bool FOLD = KIND == kKindFold;
   constexpr bool WRITE_I = KIND == kKindBlockSums;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SplitScratch split;
   const int64_t G = gridDim.x, g = blockIdx.x;
   const int w_begin = (int)(n_windows * g / G);
   const int w_end = (int)(n_windows * (g + 1) / G);
+  int parity = 0;
   if constexpr (GROUPED) {
     int rec = win_map[w_begin];
     const int rec_last = win_map[w_end - 1];
@@ -287,31 +366,23 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
       const int seg_end = min(w_end, P.win_begin + P.n_win);
       const GemvProblem Pn = table[min(rec + 1, rec_last)];
       const int wl0 = w - P.win_begin, wl1 = seg_end - P.win_begin;
-      const int J = blocks_per_lane_of(P.K);
-      if constexpr (JMAX >= 8 && B * 8 <= 8) {
-        if (J == 8) gemv_segment<B, 8, false, false>(P, wl0, wl1, smem, Iout);
-      }
-      if constexpr (JMAX >= 4 && B * 4 <= 8) {
-        if (J == 4) gemv_segment<B, 4, false, false>(P, wl0, wl1, smem, Iout);
-      }
-      if constexpr (JMAX >= 2 && B * 2 <= 8) {
-        if (J == 2) gemv_segment<B, 2, false, false>(P, wl0, wl1, smem, Iout);
-      }
-      if (J == 1) gemv_segment<B, 1, false, false>(P, wl0, wl1, smem, Iout);
+      const GemvClass cls = gemv_class_of(P.K, BT);
+      dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
+        gemv_segment<BT, JJ, SS, false, false>(P, B, wl0, wl1, smem, &split, parity, Iout);
+      });
       w = seg_end;
       P = Pn;
       ++rec;
     }
   } else {
-    if (w_begin < w_end) gemv_segment<B, JMAX, FOLD, WRITE_I>(p0, w_begin, w_end, smem, Iout);
+    if (w_begin < w_end)
+      gemv_segment<BT, J, S, FOLD, WRITE_I>(p0, B, w_begin, w_end, smem, &split, parity, Iout);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-
-static int blocks_per_lane(int64_t K) { return blocks_per_lane_of((int)K); }
 
 static size_t fused_lds_bytes(int64_t K, int64_t B) {
   const int64_t nb = K / kQK;
@@ -320,17 +391,18 @@ static size_t fused_lds_bytes(int64_t K, int64_t B) {
 
 bool gemv_supported(int64_t M, int64_t K, int64_t B) {
   (void)M;
-  if (B < 1 || B > 4) return false;
-  const int J = blocks_per_lane(K);
-  return J <= 8 && B * J <= 8;
+  return gemv_class_of(K, B).J != 0;
 }
 
 bool gemv_fused_supported(int64_t K, int64_t B) {
-  return gemv_supported(1, K, B) && fused_lds_bytes(K, B) <= kGemvMaxLds;
+  const GemvClass c = gemv_class_of(K, B);
+  return c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;
 }
 
 int gemv_window_rows(int64_t K, int64_t B) {
-  return 4 * gemv_rows_per_wave((int)B, blocks_per_lane(K));
+  const GemvClass c = gemv_class_of(K, B);
+  if (c.J == 0) return 0;
+  return (kGemvWaves / c.S) * gemv_rows_per_wave(gemv_bt((int)B), c.J);
 }
 
 // Workgroups that can be resident at once for one kernel instance and LDS
@@ -359,47 +431,51 @@ static int64_t resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <int B, int JMAX, int KIND>
+template <int BT, int J, int S, int KIND>
 static hipError_t launch_kind(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
-                              int64_t n_windows, size_t lds, int32_t* I, hipStream_t s) {
-  const void* k = (const void*)gemv_kernel<B, JMAX, KIND>;
+                              int64_t n_windows, int B, size_t lds, int32_t* I, hipStream_t s) {
+  const void* k = (const void*)gemv_kernel<BT, J, S, KIND>;
   int64_t grid = resident_workgroups(k, lds);
   if (grid > n_windows) grid = n_windows;
-  hipLaunchKernelGGL((gemv_kernel<B, JMAX, KIND>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, p, table,
-                     map, (int)n_windows, I);
+  hipLaunchKernelGGL((gemv_kernel<BT, J, S, KIND>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, p,
+                     table, map, (int)n_windows, B, I);
   return hipGetLastError();
 }
 
-template <int B, int JMAX>
-static hipError_t launch_bj(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
-                            int64_t n_windows, bool fold, size_t lds, int32_t* I, hipStream_t s) {
-  if (table) return launch_kind<B, JMAX, kKindGroup>(p, table, map, n_windows, 0, I, s);
-  if (fold) return launch_kind<B, JMAX, kKindFold>(p, table, map, n_windows, lds, I, s);
-  if (I) return launch_kind<B, JMAX, kKindBlockSums>(p, table, map, n_windows, 0, I, s);
-  return launch_kind<B, JMAX, kKindSingle>(p, table, map, n_windows, 0, I, s);
+template <int BT>
+static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
+                            int64_t n_windows, int64_t max_k, int B, bool fold, int32_t* I, hipStream_t s) {
+  if (table) return launch_kind<BT, 1, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+  const GemvClass c = gemv_class_of(max_k, B);
+  const size_t lds = fold ? fused_lds_bytes(max_k, B) : 0;
+  hipError_t err = hipErrorInvalidValue;
+  dispatch_class<BT>(c.J, c.S, [&]<int JJ, int SS>() {
+    if constexpr (SS == 1) {
+      if (fold) {
+        err = launch_kind<BT, JJ, SS, kKindFold>(p, nullptr, nullptr, n_windows, B, lds, I, s);
+        return;
+      }
+    }
+    if (fold) return;
+    if (I)
+      err = launch_kind<BT, JJ, SS, kKindBlockSums>(p, nullptr, nullptr, n_windows, B, 0, I, s);
+    else
+      err = launch_kind<BT, JJ, SS, kKindSingle>(p, nullptr, nullptr, n_windows, B, 0, I, s);
+  });
+  return err;
 }
 
 hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
                              int64_t n_windows, int64_t max_k, int64_t B, bool any_fused, int32_t* I,
                              hipStream_t s) {
-  const int J = blocks_per_lane(max_k);
   if (table && (any_fused || I)) return hipErrorInvalidValue;  // grouped launches read Q8 planes
-  const size_t lds = any_fused ? fused_lds_bytes(max_k, B) : 0;
-#define Q4Q8_GEMV_CASE(BB, JJ) \
-  if (B == BB && J == JJ) return launch_bj<BB, JJ>(p, table, map, n_windows, any_fused, lds, I, s);
-  Q4Q8_GEMV_CASE(1, 1)
-  Q4Q8_GEMV_CASE(1, 2)
-  Q4Q8_GEMV_CASE(1, 4)
-  Q4Q8_GEMV_CASE(1, 8)
-  Q4Q8_GEMV_CASE(2, 1)
-  Q4Q8_GEMV_CASE(2, 2)
-  Q4Q8_GEMV_CASE(2, 4)
-  Q4Q8_GEMV_CASE(3, 1)
-  Q4Q8_GEMV_CASE(3, 2)
-  Q4Q8_GEMV_CASE(4, 1)
-  Q4Q8_GEMV_CASE(4, 2)
-#undef Q4Q8_GEMV_CASE
-  return hipErrorInvalidValue;
+  if (gemv_class_of(max_k, B).J == 0) return hipErrorInvalidValue;
+  switch (gemv_bt((int)B)) {
+    case 1: return launch_bt<1>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
+    case 2: return launch_bt<2>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
+    case 4: return launch_bt<4>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
+    default: return launch_bt<8>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
+  }
 }
 
 }  // namespace q4q8

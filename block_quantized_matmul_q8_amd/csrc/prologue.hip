@@ -136,19 +136,42 @@ hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* 
 }
 
 // Prologue pass of a grouped launch: workgroup (j, c) quantises row c of the
-// fp32 input of job j into the job's Q8 planes.  Every job has K <= 16384.
+// fp32 input of job j into the job's Q8 planes, in the register form for
+// rows of up to 16384 elements and the LDS-tree form beyond (dynamic LDS of
+// 2 * next_pow2(K / 32) floats for the longest row of the launch).
 __global__ __launch_bounds__(kPrologueThreads) void group_prologue_kernel(
     const PrologueJob* __restrict__ jobs) {
+  extern __shared__ float red[];
+  __shared__ float s_slot;
   __shared__ float groups[8];
   const PrologueJob& J = jobs[blockIdx.x];
   const int c = blockIdx.y;
-  const int K = J.K, nb = K / kQK;
-  wg_q8_row_fast(J.x + (int64_t)c * K, J.g, K, J.eps, J.raw != 0, J.xq + (int64_t)c * K,
-                 J.xd + (int64_t)c * nb, nullptr, groups, threadIdx.x);
+  const int K = J.K, nb = K / kQK, tid = threadIdx.x;
+  const float* xr = J.x + (int64_t)c * K;
+  int8_t* xq = J.xq + (int64_t)c * K;
+  float* xd = J.xd + (int64_t)c * nb;
+  if (K <= kFastPrologueK) {
+    wg_q8_row_fast(xr, J.g, K, J.eps, J.raw != 0, xq, xd, nullptr, groups, tid);
+    return;
+  }
+  const int P = next_pow2_int(nb);
+  const float s = J.raw ? 1.0f : wg_rms_scale(xr, K, J.eps, P, red, &s_slot, tid, kPrologueThreads);
+  for (int b = tid; b < nb; b += kPrologueThreads) {
+    uint32_t packed[8];
+    float dd;
+    int sum;
+    q8_block_codes(xr, J.g, b, s, J.raw != 0, packed, dd, sum);
+    uint4* dst = reinterpret_cast<uint4*>(xq + b * kQK);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    xd[b] = dd;
+  }
 }
 
-hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B, hipStream_t s) {
-  hipLaunchKernelGGL(group_prologue_kernel, dim3((unsigned)n_jobs, (unsigned)B), dim3(kPrologueThreads), 0,
+hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B, int64_t max_k,
+                                 hipStream_t s) {
+  const size_t lds = max_k > kFastPrologueK ? 2 * (size_t)next_pow2_int((int)(max_k / kQK)) * sizeof(float) : 0;
+  hipLaunchKernelGGL(group_prologue_kernel, dim3((unsigned)n_jobs, (unsigned)B), dim3(kPrologueThreads), lds,
                      s, jobs);
   return hipGetLastError();
 }

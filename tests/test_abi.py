@@ -244,9 +244,9 @@ def test_group_build_validation_is_host_only():
         ([_desc(xq=None, xd=None, x=512, g=None)], 1, q.Q4Q8_E_ARG),  # norm without g
         ([_desc(xq=None, xd=None, x=520, g=768)], 1, q.Q4Q8_E_ALIGN),
         ([_desc(flags=4)], 1, q.Q4Q8_E_ARG),
-        ([_desc()], 5, q.Q4Q8_E_UNSUPPORTED),                       # B beyond the streaming kernel
-        ([_desc(K=32768)], 1, q.Q4Q8_E_UNSUPPORTED),                # K beyond the register blocking
-        ([_desc(xq=None, xd=None, x=512, g=768, K=16384)], 4, q.Q4Q8_E_UNSUPPORTED),
+        ([_desc()], 9, q.Q4Q8_E_UNSUPPORTED),                       # B beyond the streaming kernel
+        ([_desc(K=131072)], 1, q.Q4Q8_E_UNSUPPORTED),               # K beyond the register blocking
+        ([_desc(xq=None, xd=None, x=512, g=768, K=32768)], 8, q.Q4Q8_E_UNSUPPORTED),
     ]
     for descs, B, code in bad:
         with pytest.raises(q.Q4Q8Error) as ei:
@@ -268,7 +268,7 @@ def test_group_launch_rejects_foreign_plans():
     _, good = _build([_desc()], 1)
     assert L.mul_mat_q4q8_group(None, ctypes.byref(good), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q4q8_group(ctypes.c_void_p(264), ctypes.byref(good), None) == q.Q4Q8_E_ALIGN
-    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 7)):
+    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 9)):
         bad = q.GroupPlan.from_buffer_copy(good)
         setattr(bad, field, value)
         assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, field

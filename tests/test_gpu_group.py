@@ -79,16 +79,18 @@ def test_fused_no_norm_and_special_rows(hand_examples):
     assert int(y1.cpu().numpy().view(np.uint32)[0, 0]) == int(e5["y_bits"], 16)
 
 
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
 def test_group_mixed(B):
-    """Products of different K classes and both activation modes in one group."""
+    """Products of different blocking classes (K in one wave or split over
+    waves) and all activation modes in one group."""
     dev = torch.device("cuda:0")
     specs = [(512, 2048, "q8"), (130, 1408, "norm"), (64, 8192, "norm"), (300, 4096, "raw"),
-             (1, 32, "q8"), (2048, 2048, "norm"), (33, 14336, "q8")]
+             (1, 32, "q8"), (2048, 2048, "norm"), (33, 14336, "q8"), (70, 16384, "norm"),
+             (20, 16416, "raw")]
     problems, refs = [], []
     for i, (M, K, mode) in enumerate(specs):
-        if B * max(1, -(-K // 2048)) > 8:
-            continue
+        if K > 16384 and B > 2:
+            continue                # beyond the streaming kernel's register blocking for B > 2
         qs, d = _weights(43, 1, i, M, K)
         x = workloads.activation(43, 1, i, B, K)
         g = workloads.norm_weight(43, 1, i, K)
@@ -115,15 +117,17 @@ def test_group_mixed(B):
         torch.cuda.synchronize()
         for p, ref in zip(problems, refs):
             assert_close(p["y"].cpu().numpy(), ref, f"rep {rep} M={p['qs'].shape[0]}")
-    # the group's prologue pass gives the codes of the single-product calls,
-    # so the outputs agree bit for bit
+    # the group's prologue pass gives the codes of q8_quantize_rmsnorm and
+    # the streaming pass runs the single-product arithmetic, so the outputs
+    # agree bit for bit with the two standalone calls
     for p in problems:
         if "x" in p:
             raw = p.get("flags", 0) == q.Q8_NO_NORM
-            single = q.mul_mat_q4q8_rmsnorm(p["qs"], p["d"], p["x"], None if raw else p["g"], workloads.RMS_EPS,
-                                            flags=p.get("flags", 0))
+            xq, xd, _ = q.q8_quantize_rmsnorm(p["x"], None if raw else p["g"], workloads.RMS_EPS,
+                                              flags=p.get("flags", 0))
         else:
-            single = q.mul_mat_q4q8(p["qs"], p["d"], p["xq"], p["xd"])
+            xq, xd = p["xq"], p["xd"]
+        single = q.mul_mat_q4q8(p["qs"], p["d"], xq, xd)
         torch.cuda.synchronize()
         assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
 
@@ -164,3 +168,28 @@ def test_group_full_llama_1b_layer_in_a_graph():
         torch.cuda.synchronize()
         for p, ref, m in zip(problems, refs, layer):
             assert_close(p["y"].cpu().numpy(), ref, f"replay {rep} {m.name}")
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_group_full_llama_8b_layer(B):
+    """One Llama-3-8B layer at full shape as one grouped call with fp32 rows
+    (prologue pass, then the streaming pass; K = 14336 is split over waves
+    for B > 1), every output against the oracle."""
+    dev = torch.device("cuda:0")
+    layer = workloads.LLAMA_3_8B
+    xs = {s: workloads.activation(5, 0, s, B, K) for s, K in workloads.slot_k(layer).items()}
+    gs = {s: workloads.norm_weight(5, 0, s, K) for s, K in workloads.slot_k(layer).items()}
+    xs_d = {s: to_dev(v) for s, v in xs.items()}
+    gs_d = {s: to_dev(v) for s, v in gs.items()}
+    problems, refs = [], []
+    for mi, m in enumerate(layer):
+        qs, d = _weights(5, 0, mi, m.M, m.K)
+        y = torch.full((B, m.M), float("nan"), dtype=torch.float32, device=dev)
+        problems.append({"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": xs_d[m.slot],
+                         "g": gs_d[m.slot], "eps": workloads.RMS_EPS})
+        refs.append(_ref(qs, d, xs[m.slot], gs[m.slot]))
+    grp = q.Group(problems, B=B)
+    grp()
+    torch.cuda.synchronize()
+    for p, ref, m in zip(problems, refs, layer):
+        assert_close(p["y"].cpu().numpy(), ref, f"B={B} {m.name}")

@@ -51,8 +51,11 @@ def _auto_path():
 
 SHAPES = [
     (1, 32, 1), (7, 64, 1), (256, 512, 1), (129, 1408, 2), (1000, 2048, 3), (33, 4096, 4),
-    (64, 14336, 1), (300, 8192, 2),                                  # GEMV route
-    (130, 1408, 5), (256, 512, 8), (1000, 2048, 33), (257, 4096, 130), (64, 14336, 16),
+    (64, 14336, 1), (300, 8192, 2),                                  # GEMV route, K in one wave
+    (130, 1408, 5), (256, 512, 8), (33, 4096, 6), (77, 2048, 7),     # GEMV route, 5 to 8 columns
+    (64, 14336, 2), (40, 16384, 4), (70, 8224, 3), (50, 14336, 8),   # GEMV route, K split over waves
+    (3, 32768, 1), (5, 65536, 1), (40, 32768, 2),
+    (130, 1408, 9), (1000, 2048, 33), (257, 4096, 130), (64, 14336, 16),
     (128, 64, 128), (1, 32, 200),                                    # GEMM route
 ]
 
@@ -68,7 +71,7 @@ def test_blocksums_and_outputs(M, K, B):
     assert_close(y2, y_o, "production instance")
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9])
 def test_forced_routes_agree(B):
     """Cross-check of the two routes (the GGML page keeps force-route switches
     only for such cross-checks): identical block sums, outputs both in tolerance."""
@@ -80,7 +83,7 @@ def test_forced_routes_agree(B):
     yg, Ig = _run(qs, d, xq, xd)
     assert np.array_equal(Ig, I_o)
     assert_close(yg, y_o, "forced gemm")
-    if B <= 4:
+    if B <= 8:
         q.q4q8_set_path(q.PATH_GEMV)
         yv, Iv = _run(qs, d, xq, xd)
         assert np.array_equal(Iv, I_o)
