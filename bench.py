@@ -55,13 +55,6 @@ def gemv_bytes(M, K, B):
     return q4_bytes(M, K) + B * K * 9 // 8 + B * M * 4
 
 
-def blocks_per_lane(K):
-    """Register blocking class of the streaming kernel for rows of K (32-blocks
-    per lane, rounded up to a power of two)."""
-    j = -(-(K // 32) // 64)
-    return 1 if j <= 1 else 2 if j <= 2 else 4 if j <= 4 else 8 if j <= 8 else 16
-
-
 def capture(fn):
     import torch
     s = torch.cuda.Stream()
@@ -260,8 +253,8 @@ def bench_decode_1b(args, dev, report):
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": f"q4q8::gemv_kernel<1, {blocks_per_lane(stream_only.plan.max_k)}, 0> "
-                               "(grouped streaming pass over the 112 products)",
+                     "kernel": "q4q8::gemv_kernel<1, 1, 1, 0> (grouped streaming instance, B = 1; "
+                               "one launch over the 112 products)",
                      "bytes_per_launch": model.step_bytes, "avg_launch_ms": round(dom_ms, 5)},
     })
     report.update(extras)
