@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/q4q8.h"
@@ -131,9 +132,15 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
     g_counts[0].fetch_add(1, std::memory_order_relaxed);
     return launched(q4q8::launch_gemv_table(p, nullptr, nullptr, p.n_win, K, B, false, I, s), "gemv");
   }
-  if (B > (int64_t)65535 * 128) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld exceeds the GEMM grid", (long long)B);
+  const int64_t tiles = q4q8::gemm_tiles(M, B);
+  if (tiles > INT32_MAX || B > INT32_MAX)
+    return fail(Q4Q8_E_UNSUPPORTED, "M = %lld, B = %lld exceed the GEMM grid", (long long)M, (long long)B);
+  q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
+  p.xq = xq;
+  p.xd = xd;
+  p.n_win = (int32_t)tiles;
   g_counts[1].fetch_add(1, std::memory_order_relaxed);
-  return launched(q4q8::launch_gemm(qs, d, M, K, xq, xd, B, y, I, s), "gemm");
+  return launched(q4q8::launch_gemm(p, nullptr, nullptr, tiles, B, I, s), "gemm");
 }
 
 }  // namespace
@@ -255,7 +262,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   memset(plan, 0, sizeof *plan);
   if (n <= 0 || n > (1 << 20)) return fail(Q4Q8_E_ARG, "n = %d must be in [1, 2^20]", n);
   if (!descs) return fail(Q4Q8_E_ARG, "null pointer argument");
-  if (B < 1 || B > 8) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld: grouped products take 1 <= B <= 8", (long long)B);
+  if (B < 1 || B > 65535) return fail(Q4Q8_E_UNSUPPORTED, "B = %lld: grouped products take 1 <= B <= 65535", (long long)B);
+  const bool tiled = B > 8;  // the matrix route; B <= 8 streams
   for (int32_t i = 0; i < n; ++i) {
     const q4q8_gemv_desc& e = descs[i];
     int st;
@@ -268,7 +276,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (!e.qs || !e.d || !e.y) return fail(Q4Q8_E_ARG, "descriptor %d: null pointer", i);
     if (!aligned(e.qs, 16) || !aligned(e.d, 2) || !aligned(e.y, 4)) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
     if (e.flags & ~Q8_NO_NORM) return fail(Q4Q8_E_ARG, "descriptor %d: unknown flags", i);
-    if (!q4q8::gemv_supported(e.M, e.K, B))
+    if (!tiled && !q4q8::gemv_supported(e.M, e.K, B))
       return fail(Q4Q8_E_UNSUPPORTED, "descriptor %d: K = %lld with B = %lld exceeds the streaming kernel", i,
                   (long long)e.K, (long long)B);
     if (e.xq) {
@@ -279,6 +287,9 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
       if (!e.x || (!no_norm && !e.g)) return fail(Q4Q8_E_ARG, "descriptor %d: needs xq/xd or x (and g)", i);
       if (!aligned(e.x, 16) || (!no_norm && !aligned(e.g, 16))) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
       if (!no_norm && !(e.eps >= 0.0f)) return fail(Q4Q8_E_ARG, "descriptor %d: eps must be >= 0", i);
+      if (e.K > q4q8::kMaxPrologueK)
+        return fail(Q4Q8_E_ARG, "descriptor %d: K = %lld exceeds %d for fp32 rows", i, (long long)e.K,
+                    q4q8::kMaxPrologueK);
     }
   }
   // Distinct fp32 inputs, in order of first use; each gets its Q8 planes in
@@ -334,15 +345,33 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
       p.xq = reinterpret_cast<const int8_t*>(base);
       p.xd = reinterpret_cast<const float*>(base + (B * e.K + 15) / 16 * 16);
     }
-    const int win = q4q8::gemv_window_rows(e.K, B);
-    const int64_t t = (e.M + win - 1) / win;
-    p.win_begin = (int32_t)tiles;
-    p.n_win = (int32_t)t;
+    int64_t t;
+    if (tiled) {
+      t = q4q8::gemm_tiles(e.M, B);
+    } else {
+      const int win = q4q8::gemv_window_rows(e.K, B);
+      t = (e.M + win - 1) / win;
+    }
     tiles += t;
     if (tiles > INT32_MAX) return fail(Q4Q8_E_ARG, "too many windows");
+    p.n_win = (int32_t)t;
     if (e.K > max_k) max_k = e.K;
     recs.push_back(p);
     rec_tiles.push_back(t);
+  }
+  // Work order: streamed products in the caller's order; tiled products
+  // longest K first (their tiles take longest), ties in the caller's order.
+  std::vector<int32_t> order(recs.size());
+  for (size_t r = 0; r < recs.size(); ++r) order[r] = (int32_t)r;
+  if (tiled)
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return recs[a].K > recs[b].K; });
+  {
+    int64_t first = 0;
+    for (int32_t r : order) {
+      recs[r].win_begin = (int32_t)first;
+      first += rec_tiles[r];
+    }
   }
   plan->B = (int32_t)B;
   plan->n_records = (int32_t)recs.size();
@@ -379,8 +408,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   memcpy(out, recs.data(), recs.size() * sizeof(q4q8::GemvProblem));
   int32_t* map = reinterpret_cast<int32_t*>(out + plan->map_offset);
   int64_t m = 0;
-  for (size_t r = 0; r < recs.size(); ++r)
-    for (int64_t t = 0; t < rec_tiles[r]; ++t) map[m++] = (int32_t)r;
+  for (int32_t r : order)
+    for (int64_t t = 0; t < rec_tiles[r]; ++t) map[m++] = r;
   q4q8::PrologueJob* jobs = reinterpret_cast<q4q8::PrologueJob*>(out + plan->prologue_offset);
   for (size_t k = 0; k < inputs.size(); ++k) {
     const Input& in = inputs[k];
@@ -404,10 +433,11 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   if (plan->n_records == 0) return ok();
   if (!table_dev) return fail(Q4Q8_E_ARG, "null table");
   if (!aligned(table_dev, 16)) return fail(Q4Q8_E_ALIGN, "table must be 16-byte aligned");
-  if (plan->n_records < 0 || plan->B < 1 || plan->B > 8 || plan->n_windows < plan->n_records ||
+  const bool tiled = plan->B > 8;
+  if (plan->n_records < 0 || plan->B < 1 || plan->B > 65535 || plan->n_windows < plan->n_records ||
       plan->n_windows > INT32_MAX || plan->n_prologue < 0 || plan->n_prologue > plan->n_records ||
       plan->max_k < q4q8::kQK || plan->max_k % q4q8::kQK != 0 ||
-      !q4q8::gemv_supported(1, plan->max_k, plan->B) ||
+      (!tiled && !q4q8::gemv_supported(1, plan->max_k, plan->B)) ||
       plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
       plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
       plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob))
@@ -426,6 +456,13 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   }
   q4q8::GemvProblem unused;
   memset(&unused, 0, sizeof unused);
+  if (tiled) {
+    g_counts[1].fetch_add(1, std::memory_order_relaxed);
+    return launched(q4q8::launch_gemm(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
+                                      reinterpret_cast<const int32_t*>(base + plan->map_offset), plan->n_windows,
+                                      plan->B, nullptr, s),
+                    "mul_mat_q4q8_group (tiled)");
+  }
   g_counts[0].fetch_add(1, std::memory_order_relaxed);
   return launched(q4q8::launch_gemv_table(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                           reinterpret_cast<const int32_t*>(base + plan->map_offset),

@@ -164,9 +164,13 @@ Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, c
                                          int32_t* xs, hipStream_t s);
 Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B,
                                              int64_t max_k, hipStream_t s);
-Q4Q8_HIDDEN hipError_t launch_gemm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
-                                   const int8_t* xq, const float* xd, int64_t B, float* y,
-                                   int32_t* I, hipStream_t s);
+// Tiles (128 weight rows x 128 tokens) of one product on the tiled route.
+Q4Q8_HIDDEN int64_t gemm_tiles(int64_t M, int64_t B);
+// Tiled route over the single record `p` (table == nullptr, n_tiles =
+// gemm_tiles(p.M, B)) or over the products of a device `table`, tile t of the
+// launch belonging to record tile_map[t] (its first tile is win_begin).
+Q4Q8_HIDDEN hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
+                                   int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s);
 Q4Q8_HIDDEN size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
 Q4Q8_HIDDEN hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M,
                                   int64_t K, const int8_t* xq, const float* xd, int64_t n_x_slots,

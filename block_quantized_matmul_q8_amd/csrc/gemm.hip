@@ -5,19 +5,32 @@
 // One v_mfma_i32_32x32x32_i8 covers exactly one 32-element quantisation block,
 // so its int32 result is the exact block sum I for a 32 x 32 output tile.  The
 // accumulator input is seeded with the bits of 1.5 * 2^23: the result read as
-// fp32 is F = 1.5 * 2^23 + I exactly, and the per-block rescale is two fp32
-// fmas per output element: t = fma(F, d_w, -1.5 * 2^23 * d_w) = fl(I * d_w),
-// acc = fma(t, d_x, acc).
+// fp32 is F = 1.5 * 2^23 + I exactly (|I| < 2^22), and the per-block rescale
+// is two fp32 fmas per output element: t = fma(F, d_w, -1.5 * 2^23 * d_w) =
+// fl(I * d_w) (the product 1.5 * 2^23 * d_w is exact for an fp16 d_w), then
+// acc = fma(t, d_x, acc).  Those two fmas per output and block are the
+// kernel's bound: the vector ALU, not the matrix core.
 //
 // Operand roles: A = activations (MFMA rows = tokens), B = weights (MFMA
 // columns = weight rows).  Each lane then holds one weight row (one d_w per
 // lane) and 16 token rows, and the output y[token][row] is stored with
 // consecutive lanes on consecutive rows.
 //
-// Tiling: a workgroup of 4 waves computes 128 weight rows x 128 tokens; each
-// wave a 64 x 64 quadrant (2 x 2 MFMA tiles).  Per LDS stage, two 32-blocks of
-// K: weight nibbles are unpacked to signed int8 once per stage and shared by
-// all 128 tokens.
+// Tiling: a workgroup of 4 waves computes 128 tokens x 128 weight rows; each
+// wave a 64 x 64 quadrant (2 x 2 MFMA tiles).  A stage is 4 blocks of K (128
+// bytes of activation codes per token, 64 bytes of packed weight codes per
+// row), so every global load instruction covers whole cache lines.  Two LDS
+// stage buffers: while stage s is computed, stage s + 1 travels from global
+// memory into registers and then into the other buffer (weights unpacked to
+// signed int8 once, shared by all 128 tokens), so each stage costs one
+// barrier.  Loads are unconditional from clamped addresses; rows, tokens and
+// blocks past the end get zero scales, so they add exact zeros.
+//
+// One launch serves one product or a group of products (a device table of
+// records plus a tile -> record map; the map lists the long-K products
+// first).  Tiles of a product are ordered weight-tile major (consecutive
+// tiles share the weight tile); the token tiles of one weight tile run on one
+// XCD, so the weight tile is reused from that XCD's L2.
 #include "common.h"
 
 namespace q4q8 {
@@ -28,31 +41,118 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 128;  // weight rows per workgroup
 constexpr int kTN = 128;  // tokens per workgroup
-constexpr int kKB = 2;    // 32-blocks per LDS stage
+constexpr int kKB = 4;    // 32-blocks per stage
 constexpr int kGemmThreads = 256;
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ uint32_t nib_to_s8(uint32_t n) {
   // bytes in [0,15] -> signed bytes n - 8 (no carries cross byte lanes)
   return (n + 0x78787878u) ^ 0x80808080u;
 }
 
-template <bool WRITE_I>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
-    const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int M, int K,
-    const int8_t* __restrict__ xq, const float* __restrict__ xd, int B, float* __restrict__ y,
-    int32_t* __restrict__ Iout) {
-  __shared__ __align__(16) int8_t sA[kKB][kTN][kQK];
-  __shared__ __align__(16) int8_t sW[kKB][kTM][kQK];
-  __shared__ __align__(16) float sDX[kKB][kTN];
-  __shared__ float sDW[kKB][kTM];
-  __shared__ float sCW[kKB][kTM];
+struct GemmStage {
+  int8_t a[kKB][kTN][kQK];   // activation codes
+  int8_t w[kKB][kTM][kQK];   // weight codes as signed int8
+  float dx[kKB][kTN];        // activation scales (0 past the end)
+  float dw[kKB][kTM];        // weight scales (0 past the end)
+  float cw[kKB][kTM];        // -1.5 * 2^23 * dw
+};
+
+template <bool WRITE_I, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
+    GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
+    int n_tiles, int B, int32_t* __restrict__ Iout) {
+  __shared__ __align__(16) GemmStage st[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave >> 1, ww = wave & 1;
-  const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kTN;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // Tile of this workgroup.  The tile list is dealt to the XCDs (workgroup
+  // bid runs on XCD bid % 8) in chunks of n_nt consecutive tiles -- the token
+  // tiles of one weight tile -- round robin: a weight tile stays on one XCD
+  // (reused from its L2) while long and short products spread over all XCDs.
+  const int n_nt = (B + kTN - 1) / kTN;
+  const int bid = blockIdx.x;
+  const int span = kXcds * n_nt;
+  int L = bid;
+  if (bid < n_tiles / span * span) {
+    const int x = bid % kXcds, pos = bid / kXcds;
+    L = ((pos / n_nt) * kXcds + x) * n_nt + pos % n_nt;
+  }
+  const GemvProblem P = GROUPED ? table[tile_map[L]] : p0;
+  const int M = P.M, K = P.K;
+  const uint8_t* __restrict__ qs = P.qs;
+  const uint16_t* __restrict__ d = P.d;
+  const int8_t* __restrict__ xq = P.xq;
+  const float* __restrict__ xd = P.xd;
+  float* __restrict__ y = P.y;
   const int nb = K / kQK;
   const int64_t row_bytes = K / 2;
-  const int l32 = lane & 31, h = lane >> 5;
+  const int lt = L - P.win_begin;
+  const int m0 = (lt / n_nt) * kTM, n0 = (lt % n_nt) * kTN;
+
+  // Thread -> data of a stage: activation chunk c = 256 i + tid is token
+  // c / 8, 16-byte piece c % 8 (two pieces per block); weight chunk
+  // c = 256 i + tid is row c / 4, block c % 4; scales: row / token tid / 2,
+  // blocks 2 (tid % 2) and 2 (tid % 2) + 1 (read one value each: d rows are
+  // only 2-byte aligned).
+  auto fetch = [&](int kb0, i32x4 (&a)[4], u32x4 (&w)[2], uint32_t (&dw)[2], float (&dx)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 256 * i + tid;
+      const int n = min(n0 + c / 8, B - 1);
+      const int blk = min(kb0 + (c % 8) / 2, nb - 1);
+      a[i] = *gptr(reinterpret_cast<const i32x4*>(xq + (int64_t)n * K + (int64_t)blk * kQK + 16 * (c % 2)));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = 256 * i + tid;
+      const int m = min(m0 + c / 4, M - 1);
+      const int blk = min(kb0 + c % 4, nb - 1);
+      w[i] = __builtin_nontemporal_load(
+          gptr(reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * 16)));
+    }
+    const int m = min(m0 + tid / 2, M - 1);
+    const int n = min(n0 + tid / 2, B - 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int blk = min(kb0 + 2 * (tid % 2) + e, nb - 1);
+      dw[e] = gptr(d)[(int64_t)m * nb + blk];
+      dx[e] = gptr(xd)[(int64_t)n * nb + blk];
+    }
+  };
+
+  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[4], const u32x4 (&w)[2],
+                         const uint32_t (&dwb)[2], const float (&dxv)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 256 * i + tid;
+      *reinterpret_cast<i32x4*>(&sg.a[(c % 8) / 2][c / 8][16 * (c % 2)]) = a[i];
+    }
+    const uint32_t m4 = 0x0F0F0F0Fu;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = 256 * i + tid;
+      const u32x4 qv = w[i];
+      const u32x4 lo = {nib_to_s8(qv.x & m4), nib_to_s8(qv.y & m4), nib_to_s8(qv.z & m4), nib_to_s8(qv.w & m4)};
+      const u32x4 hi = {nib_to_s8((qv.x >> 4) & m4), nib_to_s8((qv.y >> 4) & m4), nib_to_s8((qv.z >> 4) & m4),
+                        nib_to_s8((qv.w >> 4) & m4)};
+      *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][0]) = lo;
+      *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][16]) = hi;
+    }
+    const int r = tid / 2;
+    const bool row_ok = m0 + r < M, tok_ok = n0 + r < B;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int blk = 2 * (tid % 2) + e;
+      const bool blk_ok = kb0 + blk < nb;
+      const float dwf = (row_ok && blk_ok) ? f16_bits_to_f32((uint16_t)dwb[e]) : 0.0f;
+      sg.dw[blk][r] = dwf;
+      sg.cw[blk][r] = -kMagic * dwf;
+      sg.dx[blk][r] = (tok_ok && blk_ok) ? dxv[e] : 0.0f;
+    }
+  };
 
   float acc[2][2][16];
 #pragma unroll
@@ -65,95 +165,81 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = kMagicBits;
 
+  i32x4 fa[4];
+  u32x4 fw[2];
+  uint32_t fdw[2];
+  float fdx[2];
+  fetch(0, fa, fw, fdw, fdx);
+  store_stage(st[0], 0, fa, fw, fdw, fdx);
+  __syncthreads();
+
+  int buf = 0;
   for (int kb0 = 0; kb0 < nb; kb0 += kKB) {
-    {
-      // activations: thread -> (token row, half) for each stage block
-      const int ar = tid >> 1, ah = tid & 1;
-#pragma unroll
-      for (int blk = 0; blk < kKB; ++blk) {
-        const int kb = kb0 + blk;
-        int4 v = make_int4(0, 0, 0, 0);
-        if (kb < nb && n0 + ar < B)
-          v = *reinterpret_cast<const int4*>(xq + (int64_t)(n0 + ar) * K + kb * kQK + ah * 16);
-        *reinterpret_cast<int4*>(&sA[blk][ar][ah * 16]) = v;
-      }
-      // weights: thread -> (weight row, stage block)
-      const int wr = tid & (kTM - 1), wb = tid / kTM;
-      const int kb = kb0 + wb;
-      uint4 q = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-      float dwv = 0.0f;
-      if (kb < nb && m0 + wr < M) {
-        q = *reinterpret_cast<const uint4*>(qs + (int64_t)(m0 + wr) * row_bytes + (int64_t)kb * 16);
-        dwv = f16_bits_to_f32(d[(int64_t)(m0 + wr) * nb + kb]);
-      }
-      const uint32_t m4 = 0x0F0F0F0Fu;
-      uint4 lo = make_uint4(nib_to_s8(q.x & m4), nib_to_s8(q.y & m4), nib_to_s8(q.z & m4),
-                            nib_to_s8(q.w & m4));
-      uint4 hi = make_uint4(nib_to_s8((q.x >> 4) & m4), nib_to_s8((q.y >> 4) & m4),
-                            nib_to_s8((q.z >> 4) & m4), nib_to_s8((q.w >> 4) & m4));
-      *reinterpret_cast<uint4*>(&sW[wb][wr][0]) = lo;
-      *reinterpret_cast<uint4*>(&sW[wb][wr][16]) = hi;
-      sDW[wb][wr] = dwv;
-      sCW[wb][wr] = -kMagic * dwv;
-      // token scales: thread -> (token row, stage block)
-      float dxv = 0.0f;
-      if (kb < nb && n0 + wr < B) dxv = xd[(int64_t)(n0 + wr) * nb + kb];
-      sDX[wb][wr] = dxv;
-    }
-    __syncthreads();
+    const bool more = kb0 + kKB < nb;
+    if (more) fetch(kb0 + kKB, fa, fw, fdw, fdx);  // in flight during this stage's compute
+    const GemmStage& sg = st[buf];
 
 #pragma unroll
     for (int blk = 0; blk < kKB; ++blk) {
-      const int kb = kb0 + blk;
-      if (kb < nb) {
+      if (kb0 + blk < nb) {
         v4i a[2], b[2];
         float dw[2], cw[2];
-        float dx[2][16];
 #pragma unroll
         for (int it = 0; it < 2; ++it)
-          a[it] = *reinterpret_cast<const v4i*>(&sA[blk][wt * 64 + it * 32 + l32][16 * h]);
+          a[it] = *reinterpret_cast<const v4i*>(&sg.a[blk][wt * 64 + it * 32 + l32][16 * h]);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           const int wrow = ww * 64 + jt * 32 + l32;
-          b[jt] = *reinterpret_cast<const v4i*>(&sW[blk][wrow][16 * h]);
-          dw[jt] = sDW[blk][wrow];
-          cw[jt] = sCW[blk][wrow];
+          b[jt] = *reinterpret_cast<const v4i*>(&sg.w[blk][wrow][16 * h]);
+          dw[jt] = sg.dw[blk][wrow];
+          cw[jt] = sg.cw[blk][wrow];
         }
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 v =
-                *reinterpret_cast<const float4*>(&sDX[blk][wt * 64 + it * 32 + 8 * g + 4 * h]);
-            dx[it][4 * g + 0] = v.x;
-            dx[it][4 * g + 1] = v.y;
-            dx[it][4 * g + 2] = v.z;
-            dx[it][4 * g + 3] = v.w;
-          }
+        // The four block products go to the matrix core first, into
+        // separate registers, so it works while the vector ALU rescales.
+        v16i Di[2][2];
+        v16f Fv[2][2];
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
-            const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[it], b[jt], seed, 0, 0, 0);
             // Reinterpret the whole result vector at once: hipcc (ROCm 7.2)
-            // miscompiles a per-element int -> float bit cast of an MFMA
+            // miscompiles a per-element int <-> float bit cast of an MFMA
             // result, propagating element 0 to every element.
-            const v16f Fv = __builtin_bit_cast(v16f, D);
+            Di[it][jt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[it], b[jt], seed, 0, 0, 0);
+            Fv[it][jt] = __builtin_bit_cast(v16f, Di[it][jt]);
+          }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          float dx[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wt * 64 + it * 32 + 8 * g + 4 * h]);
+            dx[4 * g + 0] = v.x;
+            dx[4 * g + 1] = v.y;
+            dx[4 * g + 2] = v.z;
+            dx[4 * g + 3] = v.w;
+          }
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float F = Fv[r];
-              const float t = __builtin_fmaf(F, dw[jt], cw[jt]);
-              acc[it][jt][r] = __builtin_fmaf(t, dx[it][r], acc[it][jt][r]);
+              const float t = __builtin_fmaf(Fv[it][jt][r], dw[jt], cw[jt]);
+              acc[it][jt][r] = __builtin_fmaf(t, dx[r], acc[it][jt][r]);
               if (WRITE_I) {
                 const int n = n0 + wt * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 const int m = m0 + ww * 64 + jt * 32 + l32;
-                if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb] = D[r] - kMagicBits;
+                if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = Di[it][jt][r] - kMagicBits;
               }
             }
           }
+        }
       }
     }
+    // The other buffer was last read in the previous stage, which every wave
+    // finished before the barrier that ended it.
+    if (more) store_stage(st[buf ^ 1], kb0 + kKB, fa, fw, fdw, fdx);
     __syncthreads();
+    buf ^= 1;
   }
 
 #pragma unroll
@@ -168,16 +254,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       }
 }
 
-hipError_t launch_gemm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
-                       const int8_t* xq, const float* xd, int64_t B, float* y, int32_t* I,
-                       hipStream_t s) {
-  const dim3 grid((unsigned)((M + kTM - 1) / kTM), (unsigned)((B + kTN - 1) / kTN));
-  if (I)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, qs, d, (int)M, (int)K,
-                       xq, xd, (int)B, y, I);
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, qs, d, (int)M, (int)K,
-                       xq, xd, (int)B, y, I);
+int64_t gemm_tiles(int64_t M, int64_t B) { return ((M + kTM - 1) / kTM) * ((B + kTN - 1) / kTN); }
+
+hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
+                       int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s) {
+  const dim3 grid((unsigned)n_tiles), block(kGemmThreads);
+  if (table) {
+    if (I) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
+                       (int)B, I);
+  } else if (I) {
+    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
+                       (int)B, I);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
+                       (int)B, I);
+  }
   return hipGetLastError();
 }
 

@@ -235,6 +235,25 @@ def test_group_build_layout_is_host_only():
     assert plan3.workspace_bytes == 0 and plan3.n_prologue == 0
 
 
+def test_group_build_tiled_layout():
+    """B > 8 takes the tiled route: one record per product with
+    ceil(M/128) * ceil(B/128) tiles, the long-K products' tiles first."""
+    WS = 1 << 20
+    a = _desc(M=300, K=2048)
+    b = _desc(M=130, K=8192, xq=None, xd=None, x=512, g=768)
+    c = _desc(M=128, K=8192, y=4096)
+    image, plan = _build([a, b, c], 300, WS, 300 * (8192 + 1024))
+    ta, tb, tc = 3 * 3, 2 * 3, 1 * 3
+    assert plan.n_records == 3 and plan.B == 300 and plan.n_windows == ta + tb + tc
+    recs = image[:plan.map_offset].view(np.int32).reshape(3, 24)
+    # records stay in the caller's order; win_begin follows the K-descending work order
+    assert recs[:, 19].tolist() == [ta, tb, tc]
+    assert recs[1, 18] == 0 and recs[2, 18] == tb and recs[0, 18] == tb + tc
+    assert image[plan.map_offset:plan.map_offset + 4 * plan.n_windows].view(np.int32).tolist() == \
+        [1] * tb + [2] * tc + [0] * ta
+    assert plan.n_prologue == 1 and plan.workspace_bytes == 300 * 8192 + 300 * 256 * 4
+
+
 def test_group_build_validation_is_host_only():
     bad = [
         ([_desc(K=100)], 1, q.Q4Q8_E_ARG),
@@ -244,7 +263,8 @@ def test_group_build_validation_is_host_only():
         ([_desc(xq=None, xd=None, x=512, g=None)], 1, q.Q4Q8_E_ARG),  # norm without g
         ([_desc(xq=None, xd=None, x=520, g=768)], 1, q.Q4Q8_E_ALIGN),
         ([_desc(flags=4)], 1, q.Q4Q8_E_ARG),
-        ([_desc()], 9, q.Q4Q8_E_UNSUPPORTED),                       # B beyond the streaming kernel
+        ([_desc()], 70000, q.Q4Q8_E_UNSUPPORTED),                   # B beyond a grouped launch
+        ([_desc(xq=None, xd=None, x=512, g=768, K=262144)], 300, q.Q4Q8_E_ARG),  # fp32 rows too long
         ([_desc(K=131072)], 1, q.Q4Q8_E_UNSUPPORTED),               # K beyond the register blocking
         ([_desc(xq=None, xd=None, x=512, g=768, K=32768)], 8, q.Q4Q8_E_UNSUPPORTED),
     ]
@@ -268,7 +288,7 @@ def test_group_launch_rejects_foreign_plans():
     _, good = _build([_desc()], 1)
     assert L.mul_mat_q4q8_group(None, ctypes.byref(good), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q4q8_group(ctypes.c_void_p(264), ctypes.byref(good), None) == q.Q4Q8_E_ALIGN
-    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 9)):
+    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 70000)):
         bad = q.GroupPlan.from_buffer_copy(good)
         setattr(bad, field, value)
         assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, field

@@ -193,3 +193,82 @@ def test_group_full_llama_8b_layer(B):
     torch.cuda.synchronize()
     for p, ref, m in zip(problems, refs, layer):
         assert_close(p["y"].cpu().numpy(), ref, f"B={B} {m.name}")
+
+
+@pytest.mark.parametrize("B", [9, 130, 300])
+def test_group_tiled_mixed(B):
+    """B > 8 takes the tiled MFMA route: ragged products with Q8 planes and
+    fp32 rows in one launch; every output against the oracle, and bit for bit
+    against the single-product calls (the same tile arithmetic)."""
+    dev = torch.device("cuda:0")
+    specs = [(200, 1408, "norm"), (130, 4096, "q8"), (64, 2080, "raw"), (257, 512, "norm")]
+    problems, refs = [], []
+    for i, (M, K, mode) in enumerate(specs):
+        qs, d = _weights(47, 2, i, M, K)
+        x = workloads.activation(47, 2, i, B, K)
+        g = workloads.norm_weight(47, 2, i, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        p = {"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y}
+        if mode == "q8":
+            xq, xd, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+            p.update(xq=to_dev(xq), xd=to_dev(xd))
+            ref, _ = oracle.mul_mat(qs, d, xq, xd, nthreads=16, want_y64=False)
+        elif mode == "norm":
+            p.update(x=to_dev(x), g=to_dev(g), eps=workloads.RMS_EPS)
+            ref = _ref(qs, d, x, g)
+        else:
+            p.update(x=to_dev(x), flags=q.Q8_NO_NORM)
+            ref = _ref(qs, d, x, None, no_norm=True)
+        problems.append(p)
+        refs.append(ref)
+    grp = q.Group(problems, B=B)
+    q.q4q8_dispatch_counts(reset=True)
+    grp()
+    torch.cuda.synchronize()
+    assert q.q4q8_dispatch_counts(reset=True)["gemm"] == 1
+    for p, ref in zip(problems, refs):
+        assert_close(p["y"].cpu().numpy(), ref, f"B={B} M={p['qs'].shape[0]}")
+        if "x" in p:
+            raw = p.get("flags", 0) == q.Q8_NO_NORM
+            xq, xd, _ = q.q8_quantize_rmsnorm(p["x"], None if raw else p["g"], workloads.RMS_EPS,
+                                              flags=p.get("flags", 0))
+        else:
+            xq, xd = p["xq"], p["xd"]
+        single = q.mul_mat_q4q8(p["qs"], p["d"], xq, xd)
+        torch.cuda.synchronize()
+        assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [512, 2048])
+def test_group_tiled_prefill_layer_sampled(T):
+    """A Llama-3-8B-shaped prefill layer (T tokens, all seven matrices, fp32
+    rows through the prologue pass) as one grouped tiled launch, the launch
+    the benchmark times; the oracle recomputes 40 sampled rows x 40 sampled
+    tokens of each matrix, including the last row and token."""
+    dev = torch.device("cuda:0")
+    layer = workloads.LLAMA_3_8B
+    rng = np.random.default_rng(T + 1)
+    xs = {s: workloads.activation(6, 0, s, T, K) for s, K in workloads.slot_k(layer).items()}
+    gs = {s: workloads.norm_weight(6, 0, s, K) for s, K in workloads.slot_k(layer).items()}
+    xs_d = {s: to_dev(v) for s, v in xs.items()}
+    gs_d = {s: to_dev(v) for s, v in gs.items()}
+    problems, ws = [], []
+    for mi, m in enumerate(layer):
+        w = workloads.weight(6, 0, mi, m.M, m.K)
+        qs, d = q.q4_quantize(to_dev(w))
+        y = torch.full((T, m.M), float("nan"), dtype=torch.float32, device=dev)
+        problems.append({"qs": qs, "d": d, "y": y, "x": xs_d[m.slot], "g": gs_d[m.slot],
+                         "eps": workloads.RMS_EPS})
+        ws.append(w)
+    grp = q.Group(problems, B=T)
+    grp()
+    torch.cuda.synchronize()
+    for p, w, m in zip(problems, ws, layer):
+        rows = np.sort(rng.choice(m.M, 40, replace=False))
+        toks = np.sort(rng.choice(T, 40, replace=False))
+        rows[-1], toks[-1] = m.M - 1, T - 1
+        qs_o, d_o = oracle.q4_quantize(w[rows])
+        xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(xs[m.slot][toks], gs[m.slot], workloads.RMS_EPS)
+        y_o, _ = oracle.mul_mat(qs_o, d_o, xq_o, xd_o, nthreads=16, want_y64=False)
+        y_s = p["y"].cpu().numpy()[np.ix_(toks, rows)]
+        assert_close(y_s, y_o, f"T={T} {m.name}")
