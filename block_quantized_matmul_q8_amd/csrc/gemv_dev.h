@@ -1,0 +1,382 @@
+// Device side of the streaming Q4 x Q8 matrix x vector kernel for gfx950:
+// the register blocking classes, the window / segment streaming loop and the
+// column policies.  gemv.hip builds the plain and grouped kernels on it,
+// moe.hip the expert-routed one.
+//
+// One persistent kernel serves a single product and a grouped launch over
+// many products (a device table of GemvProblem records plus a window ->
+// record map).  Per product segment of a workgroup:
+//   - lane l holds the activation codes of blocks kb0 + l, kb0 + l + 64, ...
+//     in registers for the whole segment; each row is streamed with one
+//     16-byte load per lane per 64 blocks (a whole 32-block, 1 KiB per wave
+//     load, fully coalesced), nibbles unpacked in registers, v_dot4_i32_i8 on
+//     the unsigned codes with the offset removed through the code sums
+//     (I = sum q x - 8 sum x, exact), fp32 fma for the block scale;
+//   - when B columns times the blocks per lane would not fit in registers,
+//     K is split over S = 2 or 4 waves that stream the same rows (wave part
+//     kp covers blocks kb0 = kp * 64 * J onwards); their per-row partial sums
+//     meet in LDS and are added in part order;
+//   - activations come either as Q8 planes (loaded straight into registers)
+//     or, for a single product, as fp32 x + norm weight g, in which case the
+//     workgroup runs the RMSNorm * g -> Q8 prologue itself (prologue_dev.h,
+//     bit-identical to the standalone prologue) and stages the codes through
+//     LDS;
+//   - RU rows are in flight per wave in each of two register buffers (one is
+//     computed while the other loads) and finished with one multi-row
+//     butterfly.
+// Column counts are padded to BT in {1, 2, 4, 8}; the true count B is a
+// launch argument (columns past B read nothing and store nothing).
+#pragma once
+
+#include "prologue_dev.h"
+
+namespace q4q8 {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr size_t kGemvMaxLds = 64 * 1024;
+
+// Butterfly sum of N values per lane over the 64 lanes.  Lane L returns the
+// total of value index L >> (6 - log2 N); each exchange step halves the
+// number of values a lane carries, so the cost is N - 1 + 6 - log2 N
+// shuffles instead of 6 N.
+template <int N>
+__device__ __forceinline__ float multi_reduce(float (&v)[N], int lane) {
+#pragma unroll
+  for (int s = N / 2, off = 32; s >= 1; s /= 2, off /= 2) {
+    const bool upper = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < s; ++i) {
+      // The empty asm pins both values in registers: otherwise the compiler
+      // folds the lane-dependent choice into a load from a selected address,
+      // which moves the array to scratch memory.
+      float a = v[i], b = v[i + s];
+      __asm__("" : "+v"(a), "+v"(b));
+      const float send = upper ? a : b;
+      const float keep = upper ? b : a;
+      v[i] = keep + __shfl_xor(send, off, kWave);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int off = 32 / N; off >= 1; off /= 2) r += __shfl_xor(r, off, kWave);
+  return r;
+}
+
+constexpr int ilog2_c(int n) { return n <= 1 ? 0 : 1 + ilog2_c(n / 2); }
+constexpr int pow2_ceil_c(int n) { return n <= 1 ? 1 : 2 * pow2_ceil_c((n + 1) / 2); }
+
+__device__ __forceinline__ int code_sum8(const i32x4 a, const i32x4 b) {
+  int s = 0;
+  s = __builtin_amdgcn_sdot4(a.x, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(a.y, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(a.z, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(b.x, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(b.y, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(b.z, 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(b.w, 0x01010101, s, false);
+  return 8 * s;
+}
+
+#ifndef Q4Q8_GEMV_ROWS_IN_FLIGHT
+#define Q4Q8_GEMV_ROWS_IN_FLIGHT 16  // 16-byte loads per lane in flight per row group
+#endif
+
+// Padded column count of the kernel instance serving B columns.
+__host__ __device__ constexpr int gemv_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+// Activation blocks (columns x blocks per lane) a lane may hold.
+__host__ __device__ constexpr int gemv_act_budget(int BT) { return BT <= 4 ? 8 : 16; }
+
+// Rows a wave keeps in flight per group for BT columns and J blocks per lane.
+__host__ __device__ constexpr int gemv_rows_per_wave(int BT, int J) {
+  return Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) > 0
+             ? Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4)
+             : 1;
+}
+
+// Register blocking class of a product: J blocks per lane, K split over S
+// waves (the smallest S whose blocks fit the register budget).  J == 0: the
+// streaming kernel does not serve the shape.
+struct GemvClass {
+  int J, S;
+};
+__host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
+  if (B < 1 || B > 8 || K < kQK) return {0, 0};
+  const int64_t nb = K / kQK;
+  const int BT = gemv_bt((int)B);
+  for (int S = 1; S <= 4; S *= 2) {
+    const int64_t per = (nb + 64 * S - 1) / (64 * S);
+    const int J = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+    if (J <= 8 && BT * J <= gemv_act_budget(BT)) return {J, S};
+  }
+  return {0, 0};
+}
+
+// Rows per window of the class serving K with column width BT (0: none).
+__host__ __device__ inline int gemv_window_rows_bt(int64_t K, int BT) {
+  const GemvClass c = gemv_class_of(K, BT);
+  if (c.J == 0) return 0;
+  return (kGemvWaves / c.S) * gemv_rows_per_wave(BT, c.J);
+}
+
+template <int BT, int J, int S>
+struct GemvShape {
+  static constexpr int RU = gemv_rows_per_wave(BT, J);
+  static constexpr int SLOTS = kGemvWaves / S;  // row groups per window
+  static constexpr int WIN = SLOTS * RU;        // rows per window
+  static constexpr int NV = RU * BT;            // values reduced per row group
+  static constexpr int NP = pow2_ceil_c(NV);
+  static constexpr int SHIFT = 6 - ilog2_c(NP);
+};
+constexpr int kMaxNP = 32;  // largest NP over all classes (checked below)
+
+// LDS exchange of the K-split partial sums: two parities x waves x values.
+struct SplitScratch {
+  float v[2][kGemvWaves][kMaxNP];
+};
+
+// Where column c of a segment reads its Q8 activation row and writes its
+// output row.  Dense: B consecutive rows of the product's own planes.
+struct DenseCols {
+  static constexpr bool kWeightsFirst = false;
+  const int8_t* xq;
+  const float* xd;
+  float* y;
+  int K, nb, M;
+  __device__ __forceinline__ DenseCols(const GemvProblem& P)
+      : xq(P.xq), xd(P.xd), y(P.y), K(P.K), nb(P.K >> 5), M(P.M) {}
+  __device__ __forceinline__ const int8_t* act(int c) const { return xq + (int64_t)c * K; }
+  __device__ __forceinline__ const float* scale(int c) const { return xd + (int64_t)c * nb; }
+  __device__ __forceinline__ float* out(int c) const { return y + (int64_t)c * M; }
+};
+
+// Routed (expert) columns: column c is the (token, slot) pair
+// list[beg + c] = t * top_k + s; its activation row is token t's (one row
+// per token) or pair p's (one row per token and slot), its output row is
+// pair p's in y [T][top_k][M].
+struct RoutedCols {
+  static constexpr bool kWeightsFirst = true;
+  const int8_t* xq;
+  const float* xd;
+  float* y;
+  const int32_t* list;
+  int beg, K, nb, M, top_k, per_slot;
+  __device__ __forceinline__ int pair(int c) const { return list[beg + c]; }
+  __device__ __forceinline__ int64_t xrow(int c) const {
+    const int p = pair(c);
+    return per_slot ? (int64_t)p : (int64_t)(p / top_k);
+  }
+  __device__ __forceinline__ const int8_t* act(int c) const { return xq + xrow(c) * K; }
+  __device__ __forceinline__ const float* scale(int c) const { return xd + xrow(c) * nb; }
+  __device__ __forceinline__ float* out(int c) const { return y + (int64_t)pair(c) * M; }
+};
+
+// Streams windows [wl0, wl1) of product P (window i = rows i*WIN .. +WIN;
+// the waves of row slot rs take the RU rows at rs*RU of each window, wave
+// part kp its share of K) with J blocks per lane.  `parity` alternates over
+// every compute of the workgroup (also across products) so that a K-split
+// exchange never overwrites values a slower wave has yet to read.
+template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols>
+__device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& cols, int B, int wl0, int wl1,
+                                             unsigned char* smem, SplitScratch* split, int& parity,
+                                             int32_t* __restrict__ Iout) {
+  using Sh = GemvShape<BT, J, S>;
+  constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT;
+  static_assert(NP <= kMaxNP, "split scratch too small");
+  static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rs = wave / S, kp = wave % S;
+  const int kb0 = kp * kWave * J;
+  const int M = P.M, K = P.K, nb = K >> 5;
+  const int64_t row_bytes = K >> 1;
+
+  // Loads are unconditional, from addresses clamped into the segment's rows
+  // (so an overrun re-reads a row just loaded, from cache, and never touches
+  // rows another workgroup streams) and the block range: a guarded or masked
+  // load becomes a branch that waits for its own data, which would serialise
+  // the rows a wave keeps in flight.  Nothing needs masking: blocks past nb
+  // meet zeroed activation registers (their product is exactly 0) and rows
+  // past the segment are never stored.  Scales stay raw fp16 bits until used,
+  // so no conversion waits on a prefetch.  Weights and scales are read once:
+  // non-temporal loads keep them from displacing reusable lines.
+  const int row_last = min(M, wl1 * WIN) - 1;
+  auto load_group = [&](int row0, u32x4 (&w)[RU][J], uint32_t (&dw)[RU][J]) {
+#pragma unroll
+    for (int r = 0; r < RU; ++r) {
+      const int rowc = min(row0 + r, row_last);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int bc = min(kb0 + lane + kWave * j, nb - 1);
+        w[r][j] = __builtin_nontemporal_load(
+            &gptr(reinterpret_cast<const u32x4*>(P.qs))[rowc * (row_bytes / 16) + bc]);
+        dw[r][j] = __builtin_nontemporal_load(&gptr(P.d)[(int64_t)rowc * nb + bc]);
+      }
+    }
+  };
+
+  u32x4 wA[RU][J], wB[RU][J];
+  uint32_t dA[RU][J], dB[RU][J];
+  i32x4 xa[BT][J], xb[BT][J];
+  float xdr[BT][J];
+  int xsr[BT][J];
+  if constexpr (!FOLD) {
+    // Q8 planes: the activation loads go first (they are small and mostly
+    // L2-resident), then the first two windows; loads complete in issue
+    // order, so the first compute waits for the activations and window A
+    // only while window B is already in flight.  Routed columns first look
+    // their rows up in the routing list (two dependent reads), so there the
+    // weight windows are requested before that lookup.
+    if constexpr (Cols::kWeightsFirst) {
+      load_group(wl0 * WIN + rs * RU, wA, dA);
+      load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
+    }
+#pragma unroll
+    for (int c = 0; c < BT; ++c)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int cc = min(c, B - 1);
+        const int bc = min(kb0 + lane + kWave * j, nb - 1);
+        const Q4Q8_GLOBAL i32x4* src =
+            gptr(reinterpret_cast<const i32x4*>(cols.act(cc) + (int64_t)bc * kQK));
+        xa[c][j] = src[0];
+        xb[c][j] = src[1];
+        xdr[c][j] = gptr(cols.scale(cc))[bc];
+      }
+    if constexpr (!Cols::kWeightsFirst) {
+      load_group(wl0 * WIN + rs * RU, wA, dA);
+      load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
+    }
+#pragma unroll
+    for (int c = 0; c < BT; ++c)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const bool valid = c < B && kb0 + lane + kWave * j < nb;
+        const i32x4 zero = {0, 0, 0, 0};
+        xa[c][j] = valid ? xa[c][j] : zero;
+        xb[c][j] = valid ? xb[c][j] : zero;
+        xdr[c][j] = valid ? xdr[c][j] : 0.0f;
+        xsr[c][j] = code_sum8(xa[c][j], xb[c][j]);
+      }
+  } else {
+    // Folded-in prologue: window A is requested first, then the whole
+    // workgroup quantises the activation rows (prologue_dev.h, the
+    // register/butterfly form of the same steps) and stages the codes
+    // through LDS; window B follows.
+    load_group(wl0 * WIN + rs * RU, wA, dA);
+    int8_t* sx = reinterpret_cast<int8_t*>(smem);                  // [B][K]
+    float* sxd = reinterpret_cast<float*>(smem + (size_t)B * K);   // [B][nb]
+    int* sxs = reinterpret_cast<int*>(sxd + B * nb);               // [B][nb]
+    float* groups = reinterpret_cast<float*>(sxs + B * nb);        // [8]
+    const bool raw = P.mode == kModeRaw;
+    for (int c = 0; c < B; ++c)
+      wg_q8_row_fast(P.x + (int64_t)c * K, P.g, K, P.eps, raw, sx + (size_t)c * K, sxd + c * nb,
+                     sxs + c * nb, groups, tid);
+#pragma unroll
+    for (int c = 0; c < BT; ++c)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int b = lane + kWave * j;
+        if (c < B && b < nb) {
+          const i32x4* src = reinterpret_cast<const i32x4*>(sx + (size_t)c * K + (size_t)b * kQK);
+          xa[c][j] = src[0];
+          xb[c][j] = src[1];
+          xdr[c][j] = sxd[c * nb + b];
+          xsr[c][j] = 8 * sxs[c * nb + b];
+        } else {
+          xa[c][j] = i32x4{0, 0, 0, 0};
+          xb[c][j] = i32x4{0, 0, 0, 0};
+          xdr[c][j] = 0.0f;
+          xsr[c][j] = 0;
+        }
+      }
+    load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
+  }
+
+  // The column a lane stores is fixed for the segment (value index
+  // lane >> SHIFT of every row group), so its output row is looked up once.
+  const int my_k = lane >> SHIFT, my_c = my_k % BT;
+  float* const my_out = cols.out(min(my_c, B - 1));
+
+  // One row group: block sums, scale, multi-row reduction, store (through
+  // the part exchange when K is split).
+  auto compute_group = [&](int row0, const u32x4 (&w)[RU][J], const uint32_t (&dw)[RU][J]) {
+    float acc[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int r = 0; r < RU; ++r) {
+        const float dwf = f16_bits_to_f32((uint16_t)dw[r][j]);
+#pragma unroll
+        for (int c = 0; c < BT; ++c) {
+          const int I = dot_block(w[r][j], xa[c][j], xb[c][j]) - xsr[c][j];
+          acc[r * BT + c] = __builtin_fmaf((float)I, dwf * xdr[c][j], acc[r * BT + c]);
+          if (WRITE_I) {
+            const int b = kb0 + lane + kWave * j;
+            const int row = row0 + r;
+            if (c < B && b < nb && row <= row_last) Iout[((int64_t)c * M + row) * nb + b] = I;
+          }
+        }
+      }
+    const float v = multi_reduce<NP>(acc, lane);
+    const int k = my_k, c = my_c;
+    const bool holder = (lane & ((1 << SHIFT) - 1)) == 0 && k < NV;
+    const int row = row0 + k / BT;
+    if constexpr (S == 1) {
+      if (holder && c < B && row <= row_last) gptr_w(my_out)[row] = v;
+    } else {
+      if (holder) split->v[parity][wave][k] = v;
+      __syncthreads();
+      if (kp == 0 && holder && c < B && row <= row_last) {
+        float t = v;
+#pragma unroll
+        for (int q = 1; q < S; ++q) t += split->v[parity][wave + q][k];
+        gptr_w(my_out)[row] = t;
+      }
+      parity ^= 1;
+    }
+  };
+
+  // Ping-pong over two register buffers: while one window is computed the
+  // other is in flight; a buffer is refilled right after it is consumed.
+  for (int wi = wl0; wi < wl1; wi += 2) {
+    const int r0 = wi * WIN + rs * RU;
+    compute_group(r0, wA, dA);
+    load_group(r0 + 2 * WIN, wA, dA);
+    if (wi + 1 >= wl1) break;
+    compute_group(r0 + WIN, wB, dB);
+    load_group(r0 + 3 * WIN, wB, dB);
+  }
+}
+
+
+// Calls f.template operator()<J, S>() for the blocking class (J, S) of
+// column width BT; every class gemv_class_of can return for BT is listed.
+template <int BT, typename F>
+__host__ __device__ __forceinline__ void dispatch_class(int J, int S, F&& f) {
+  if constexpr (BT == 1) {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 1 && J == 4) f.template operator()<4, 1>();
+    if (S == 1 && J == 8) f.template operator()<8, 1>();
+    if (S == 2 && J == 8) f.template operator()<8, 2>();
+    if (S == 4 && J == 8) f.template operator()<8, 4>();
+  } else if constexpr (BT == 2) {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 1 && J == 4) f.template operator()<4, 1>();
+    if (S == 2 && J == 4) f.template operator()<4, 2>();
+    if (S == 4 && J == 4) f.template operator()<4, 4>();
+  } else {
+    if (S == 1 && J == 1) f.template operator()<1, 1>();
+    if (S == 1 && J == 2) f.template operator()<2, 1>();
+    if (S == 2 && J == 2) f.template operator()<2, 2>();
+    if (S == 4 && J == 2) f.template operator()<2, 4>();
+  }
+}
+
+
+}  // namespace q4q8

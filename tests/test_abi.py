@@ -99,7 +99,7 @@ def test_mul_mat_id_validation():
     L = q.lib()
     p = _v(256)
     ws = q.mul_mat_id_q4q8_workspace(64, 16, 8)
-    assert ws >= 4 * (64 + 1 + 2 * 16 * 8) and ws % 16 == 0
+    assert ws >= 4 * (64 + 1 + 2 * 16 * 8 + 64 + 4) and ws % 16 == 0
     # n_x_slots neither 1 nor top_k
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 3, p, 16, 8, p, p, ws, None) == q.Q4Q8_E_ARG
     # top_k out of range, E out of range

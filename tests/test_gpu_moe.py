@@ -91,3 +91,32 @@ def test_full_moe_decode():
         y = _gpu(qs, d, xq, xd, ids)
         y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=16)
         assert_close(y, y_o, name)
+
+
+@pytest.mark.parametrize("E,M,K,T,top_k,S", [
+    (2, 70, 512, 20, 1, 1),        # ~10 pairs per expert: two passes of up to 8 pairs
+    (3, 33, 4096, 9, 2, 2),        # K band 4096, one row per (token, slot)
+    (4, 20, 8224, 6, 3, 1),        # K band 16384 (split over waves), ragged block count
+    (5, 48, 7168, 13, 5, 5),       # K band 8192
+])
+def test_expert_loads_and_k_bands(E, M, K, T, top_k, S):
+    _, qs, d = _experts(34, E, M, K)
+    xq, xd = _acts(34, T, S, K)
+    ids = workloads.expert_ids(34, T, E, top_k)
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(y, y_o, ids, E)
+
+
+def test_many_bad_ids():
+    """Half of the pairs carry ids outside [0, E): their rows are NaN, the
+    others are computed as usual."""
+    E, M, K, T, top_k = 5, 40, 1408, 12, 4
+    _, qs, d = _experts(35, E, M, K)
+    xq, xd = _acts(35, T, 1, K)
+    ids = workloads.expert_ids(35, T, E, top_k)
+    ids[::2, :] = -1
+    ids[1, 3] = E + 3
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(y, y_o, ids, E)
