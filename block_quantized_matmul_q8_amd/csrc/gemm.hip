@@ -41,7 +41,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 128;  // weight rows per workgroup
 constexpr int kTN = 128;  // tokens per workgroup
-constexpr int kKB = 4;    // 32-blocks per stage
+constexpr int kIT = kTN / 64;  // 32-token MFMA tiles per wave
+constexpr int kNA = kTN / 32;  // 16-byte activation chunks per thread per stage
+constexpr int kNBuf = 2;       // LDS stage buffers
+constexpr int kKB = 4;             // 32-blocks per stage
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
 
@@ -62,7 +65,7 @@ template <bool WRITE_I, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
     int n_tiles, int B, int32_t* __restrict__ Iout) {
-  __shared__ __align__(16) GemmStage st[2];
+  __shared__ __align__(16) GemmStage st[kNBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave >> 1, ww = wave & 1;
@@ -97,9 +100,9 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
   // c = 256 i + tid is row c / 4, block c % 4; scales: row / token tid / 2,
   // blocks 2 (tid % 2) and 2 (tid % 2) + 1 (read one value each: d rows are
   // only 2-byte aligned).
-  auto fetch = [&](int kb0, i32x4 (&a)[4], u32x4 (&w)[2], uint32_t (&dw)[2], float (&dx)[2]) {
+  auto fetch = [&](int kb0, i32x4 (&a)[kNA], u32x4 (&w)[2], uint32_t (&dw)[2], float (&dx)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
       const int n = min(n0 + c / 8, B - 1);
       const int blk = min(kb0 + (c % 8) / 2, nb - 1);
@@ -119,14 +122,14 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     for (int e = 0; e < 2; ++e) {
       const int blk = min(kb0 + 2 * (tid % 2) + e, nb - 1);
       dw[e] = gptr(d)[(int64_t)m * nb + blk];
-      dx[e] = gptr(xd)[(int64_t)n * nb + blk];
+      if (tid / 2 < kTN) dx[e] = gptr(xd)[(int64_t)n * nb + blk];
     }
   };
 
-  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[4], const u32x4 (&w)[2],
+  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[kNA], const u32x4 (&w)[2],
                          const uint32_t (&dwb)[2], const float (&dxv)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
       *reinterpret_cast<i32x4*>(&sg.a[(c % 8) / 2][c / 8][16 * (c % 2)]) = a[i];
     }
@@ -150,13 +153,13 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
       const float dwf = (row_ok && blk_ok) ? f16_bits_to_f32((uint16_t)dwb[e]) : 0.0f;
       sg.dw[blk][r] = dwf;
       sg.cw[blk][r] = -kMagic * dwf;
-      sg.dx[blk][r] = (tok_ok && blk_ok) ? dxv[e] : 0.0f;
+      if (r < kTN) sg.dx[blk][r] = (tok_ok && blk_ok) ? dxv[e] : 0.0f;
     }
   };
 
-  float acc[2][2][16];
+  float acc[kIT][2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kIT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -165,28 +168,35 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = kMagicBits;
 
-  i32x4 fa[4];
+  i32x4 fa[kNA];
   u32x4 fw[2];
   uint32_t fdw[2];
   float fdx[2];
   fetch(0, fa, fw, fdw, fdx);
-  store_stage(st[0], 0, fa, fw, fdw, fdx);
-  __syncthreads();
+  if constexpr (kNBuf == 2) {
+    store_stage(st[0], 0, fa, fw, fdw, fdx);
+    __syncthreads();
+  }
 
   int buf = 0;
   for (int kb0 = 0; kb0 < nb; kb0 += kKB) {
     const bool more = kb0 + kKB < nb;
+    if constexpr (kNBuf == 1) {
+      __syncthreads();  // the previous stage has been read
+      store_stage(st[0], kb0, fa, fw, fdw, fdx);
+      __syncthreads();
+    }
     if (more) fetch(kb0 + kKB, fa, fw, fdw, fdx);  // in flight during this stage's compute
-    const GemmStage& sg = st[buf];
+    const GemmStage& sg = st[kNBuf == 2 ? buf : 0];
 
 #pragma unroll
     for (int blk = 0; blk < kKB; ++blk) {
       if (kb0 + blk < nb) {
-        v4i a[2], b[2];
+        v4i a[kIT], b[2];
         float dw[2], cw[2];
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
-          a[it] = *reinterpret_cast<const v4i*>(&sg.a[blk][wt * 64 + it * 32 + l32][16 * h]);
+        for (int it = 0; it < kIT; ++it)
+          a[it] = *reinterpret_cast<const v4i*>(&sg.a[blk][wt * (kTN / 2) + it * 32 + l32][16 * h]);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           const int wrow = ww * 64 + jt * 32 + l32;
@@ -196,10 +206,10 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
         }
         // The four block products go to the matrix core first, into
         // separate registers, so it works while the vector ALU rescales.
-        v16i Di[2][2];
-        v16f Fv[2][2];
+        v16i Di[kIT][2];
+        v16f Fv[kIT][2];
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
+        for (int it = 0; it < kIT; ++it)
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             // Reinterpret the whole result vector at once: hipcc (ROCm 7.2)
@@ -209,11 +219,11 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
             Fv[it][jt] = __builtin_bit_cast(v16f, Di[it][jt]);
           }
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
+        for (int it = 0; it < kIT; ++it) {
           float dx[16];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wt * 64 + it * 32 + 8 * g + 4 * h]);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wt * (kTN / 2) + it * 32 + 8 * g + 4 * h]);
             dx[4 * g + 0] = v.x;
             dx[4 * g + 1] = v.y;
             dx[4 * g + 2] = v.z;
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
               const float t = __builtin_fmaf(Fv[it][jt][r], dw[jt], cw[jt]);
               acc[it][jt][r] = __builtin_fmaf(t, dx[r], acc[it][jt][r]);
               if (WRITE_I) {
-                const int n = n0 + wt * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int n = n0 + wt * (kTN / 2) + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 const int m = m0 + ww * 64 + jt * 32 + l32;
                 if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = Di[it][jt][r] - kMagicBits;
               }
@@ -235,20 +245,22 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
         }
       }
     }
-    // The other buffer was last read in the previous stage, which every wave
-    // finished before the barrier that ended it.
-    if (more) store_stage(st[buf ^ 1], kb0 + kKB, fa, fw, fdw, fdx);
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (kNBuf == 2) {
+      // The other buffer was last read in the previous stage, which every
+      // wave finished before the barrier that ended it.
+      if (more) store_stage(st[buf ^ 1], kb0 + kKB, fa, fw, fdw, fdx);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
+  for (int it = 0; it < kIT; ++it)
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wt * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int n = n0 + wt * (kTN / 2) + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int m = m0 + ww * 64 + jt * 32 + l32;
         if (n < B && m < M) y[(int64_t)n * M + m] = acc[it][jt][r];
       }
