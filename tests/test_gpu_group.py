@@ -272,3 +272,30 @@ def test_group_tiled_prefill_layer_sampled(T):
         y_o, _ = oracle.mul_mat(qs_o, d_o, xq_o, xd_o, nthreads=16, want_y64=False)
         y_s = p["y"].cpu().numpy()[np.ix_(toks, rows)]
         assert_close(y_s, y_o, f"T={T} {m.name}")
+
+
+def test_full_decode_step_sampled():
+    """The benchmark's headline launch as it is timed: all 16 Llama-3.2-1B
+    layers (112 products, 64 fp32 activation rows with their norm weights) as
+    one grouped call, weights drawn on the device as in the benchmark.  The
+    oracle recomputes 12 sampled rows of every product (the last row
+    included) from the same weights and rows."""
+    import bench
+    dev = torch.device("cuda:0")
+    model = bench.DecodeModel(workloads.LLAMA_3_2_1B, 16, 1, 0, dev)
+    step, _ = bench.decode_1b_groups(model)
+    for m in (mm for layer in model.mats for mm in layer):
+        m["y"].fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for l in range(model.n_layers):
+        acts = {s: (x.cpu().numpy(), g.cpu().numpy()) for s, (x, g) in model.acts[l].items()}
+        for m in model.mats[l]:
+            rows = np.sort(rng.choice(m["M"], 12, replace=False))
+            rows[-1] = m["M"] - 1
+            qs = m["qs"].cpu().numpy()[rows]
+            d = m["d"].cpu().numpy().view(np.uint16)[rows]
+            x, g = acts[m["slot"]]
+            y_o = _ref(qs, d, x, g)
+            assert_close(m["y"].cpu().numpy()[:, rows], y_o, f"layer {l} {m['name']}")

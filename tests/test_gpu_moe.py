@@ -120,3 +120,15 @@ def test_many_bad_ids():
     y = _gpu(qs, d, xq, xd, ids)
     y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
     _check_rows(y, y_o, ids, E)
+
+
+def test_full_moe_stacked_gate_up():
+    """The benchmark's routed call as it is timed: gate and up of all 64
+    experts stacked into one [E][2 * 1408][2048] tensor, 16 tokens, top-8."""
+    cfg = workloads.MOE
+    ids = workloads.expert_ids(0, cfg.T, cfg.E, cfg.top_k)
+    _, qs, d = _experts(2, cfg.E, 2 * cfg.ffn, cfg.hidden)
+    xq, xd = _acts(2, cfg.T, 1, cfg.hidden)
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=16)
+    assert_close(y, y_o, "stacked gate/up")
