@@ -199,7 +199,7 @@ Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E,
                                 int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_k(K)) || (st = check_dims(M, T))) return st;
-  if (E <= 0 || E > 8192) return fail(Q4Q8_E_ARG, "E = %lld must be in [1, 8192]", (long long)E);
+  if (E <= 0 || E > 4096) return fail(Q4Q8_E_ARG, "E = %lld must be in [1, 4096]", (long long)E);
   if (top_k <= 0 || top_k > 64) return fail(Q4Q8_E_ARG, "top_k = %lld must be in [1, 64]", (long long)top_k);
   if (n_x_slots != 1 && n_x_slots != top_k) return fail(Q4Q8_E_ARG, "n_x_slots must be 1 or top_k");
   if (T * top_k > 65536) return fail(Q4Q8_E_ARG, "T * top_k exceeds 65536");
@@ -213,6 +213,9 @@ Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E,
                 q4q8::moe_workspace_bytes(E, T, top_k));
   if (!q4q8::gemv_supported(1, K, 8))
     return fail(Q4Q8_E_UNSUPPORTED, "K = %lld too large for the routed kernel", (long long)K);
+  if (q4q8::moe_schedule_cost_bound(E, M, K, T * top_k) >= INT32_MAX)
+    return fail(Q4Q8_E_UNSUPPORTED, "M = %lld with E = %lld is too large for the routed schedule", (long long)M,
+                (long long)E);
   if ((st = check_device())) return st;
   g_counts[2].fetch_add(1, std::memory_order_relaxed);
   return launched(q4q8::launch_moe(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y, ws,

@@ -90,10 +90,8 @@ __host__ __device__ constexpr int gemv_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 
 __host__ __device__ constexpr int gemv_act_budget(int BT) { return BT <= 4 ? 8 : 16; }
 
 // Rows a wave keeps in flight per group for BT columns and J blocks per lane.
-__host__ __device__ constexpr int gemv_rows_per_wave(int BT, int J) {
-  return Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) > 0
-             ? Q4Q8_GEMV_ROWS_IN_FLIGHT / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4)
-             : 1;
+__host__ __device__ constexpr int gemv_rows_per_wave(int BT, int J, int rif = Q4Q8_GEMV_ROWS_IN_FLIGHT) {
+  return rif / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) > 0 ? rif / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) : 1;
 }
 
 // Register blocking class of a product: J blocks per lane, K split over S
@@ -115,15 +113,17 @@ __host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
 }
 
 // Rows per window of the class serving K with column width BT (0: none).
-__host__ __device__ inline int gemv_window_rows_bt(int64_t K, int BT) {
+__host__ __device__ inline int gemv_window_rows_bt(int64_t K, int BT, int rif = Q4Q8_GEMV_ROWS_IN_FLIGHT) {
   const GemvClass c = gemv_class_of(K, BT);
   if (c.J == 0) return 0;
-  return (kGemvWaves / c.S) * gemv_rows_per_wave(BT, c.J);
+  return (kGemvWaves / c.S) * gemv_rows_per_wave(BT, c.J, rif);
 }
 
-template <int BT, int J, int S>
+// rif: 16-byte loads per lane in flight per row group (fewer rows per wave
+// leave registers for a second workgroup per CU).
+template <int BT, int J, int S, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT>
 struct GemvShape {
-  static constexpr int RU = gemv_rows_per_wave(BT, J);
+  static constexpr int RU = gemv_rows_per_wave(BT, J, RIF);
   static constexpr int SLOTS = kGemvWaves / S;  // row groups per window
   static constexpr int WIN = SLOTS * RU;        // rows per window
   static constexpr int NV = RU * BT;            // values reduced per row group
@@ -178,11 +178,11 @@ struct RoutedCols {
 // part kp its share of K) with J blocks per lane.  `parity` alternates over
 // every compute of the workgroup (also across products) so that a K-split
 // exchange never overwrites values a slower wave has yet to read.
-template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols>
+template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT>
 __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& cols, int B, int wl0, int wl1,
                                              unsigned char* smem, SplitScratch* split, int& parity,
                                              int32_t* __restrict__ Iout) {
-  using Sh = GemvShape<BT, J, S>;
+  using Sh = GemvShape<BT, J, S, RIF>;
   constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT;
   static_assert(NP <= kMaxNP, "split scratch too small");
   static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");

@@ -7,13 +7,12 @@
 // only: an expert that no token selected is never visited.
 //
 // Workspace layout (int32): offsets[E + 1] | list[n] | rank[n] | sel[E] |
-// ctl[4], n = T * top_k.
+// costp[E + 1] | ctl[4], n = T * top_k.
 //   list holds, grouped by expert, the flat (token, slot) index t * top_k + s
 //   of every routed pair; the order inside a group is not fixed, and does not
 //   matter because every output element is computed independently.
-//   sel lists the selected experts, those with the most pairs first; ctl[0]
-//   is the number of work items of the streaming launch, ctl[1] the counter
-//   its workgroups take items from.
+//   sel lists the selected experts in expert order, costp the prefix of their
+//   streaming costs (costp[i] = cost of sel[0..i)); ctl[0] is their number.
 #include <mutex>
 
 #include "gemv_dev.h"
@@ -22,29 +21,79 @@ namespace q4q8 {
 
 constexpr int kRouteThreads = 1024;
 
-constexpr int kMoeChunk = 4;  // windows per work item of the streaming launch (2, 6, 8 measured slower)
-
 size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
   const size_t n = (size_t)(T * top_k);
-  const size_t words = (size_t)E + 1 + 2 * n + (size_t)E + 4;
+  const size_t words = (size_t)E + 1 + 2 * n + (size_t)E + (size_t)E + 1 + 4;
   return (words * sizeof(int32_t) + 15) & ~(size_t)15;
+}
+
+// Relative cost of streaming one window of an expert with c routed pairs:
+// the pairs are taken up to 8 per pass, and a pass of width 1 / 2 / 4 / 8
+// costs about 16 / 16 / 21 / 33 units (the routed kernel's measured time per
+// window at each width, every expert of a 64-expert layer taking that width).
+constexpr int kMoeMaxWindowCost = 33;
+__host__ __device__ inline int moe_window_cost(int c) {
+  int cost = 0;
+  for (int c0 = 0; c0 < c; c0 += 8) {
+    const int nc = min(8, c - c0);
+    cost += nc <= 2 ? 16 : nc <= 4 ? 21 : kMoeMaxWindowCost;
+  }
+  return cost;
+}
+
+// In-place exclusive scan of v[0..count) by all kRouteThreads threads, total
+// into v[count]: a contiguous chunk per thread, a shuffle scan within each
+// wave, one thread over the wave totals (wave_tot: kRouteThreads / 64 ints).
+__device__ void block_exclusive_scan(int* v, int count, int* wave_tot, int tid) {
+  const int per = (count + kRouteThreads - 1) / kRouteThreads;
+  const int lo = min(count, tid * per), hi = min(count, lo + per);
+  int sum = 0;
+  for (int e = lo; e < hi; ++e) sum += v[e];
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wave_tot[wv] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < kRouteThreads / 64; ++w) {
+      const int c = wave_tot[w];
+      wave_tot[w] = run;
+      run += c;
+    }
+    v[count] = run;
+  }
+  __syncthreads();
+  int run = wave_tot[wv] + incl - sum;
+  for (int e = lo; e < hi; ++e) {
+    const int c = v[e];
+    v[e] = run;
+    run += c;
+  }
+  __syncthreads();
 }
 
 // Routing: one workgroup.  Pass 1 reads every id once: a valid pair takes
 // its rank within its expert (LDS atomics), an invalid one is written to the
 // tail of `list` (valid pairs fill it from the front, so the two never
-// meet).  The per-expert counts are scanned in chunks (a thread per chunk,
-// a shuffle scan per wave, one thread over the wave totals), the pairs are
-// scattered into the
+// meet).  Block scans give the per-expert offsets, the selected experts'
+// indices and the prefix of their streaming costs; the pairs are scattered
+// into the
 // grouped list, and the rows of invalid pairs are filled with quiet NaNs.
-// LDS: counts[E + 1] | wave totals[kRouteThreads / 64].
+// LDS: counts, selected indices, cost prefix (E + 1 each) | wave totals.
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int M, int chunks, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ids, int n, int E, int n_win, int32_t* __restrict__ offsets,
     int32_t* __restrict__ list, int32_t* __restrict__ rank, int32_t* __restrict__ sel,
-    int32_t* __restrict__ ctl, float* __restrict__ y) {
+    int32_t* __restrict__ costp, int32_t* __restrict__ ctl, int M, float* __restrict__ y) {
   extern __shared__ int lds[];
-  int* cnt = lds;                         // E + 1
-  int* chunk = lds + E + 1;               // kRouteThreads / 64
+  int* cnt = lds;                                // E + 1: counts, then offsets
+  int* sidx = cnt + E + 1;                       // E + 1: selected index
+  int* cpre = sidx + E + 1;                      // E + 1: cost prefix
+  int* wave_tot = cpre + E + 1;                  // kRouteThreads / 64
   __shared__ int n_bad;
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += kRouteThreads) cnt[e] = 0;
@@ -58,63 +107,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
       list[n - 1 - atomicAdd(&n_bad, 1)] = i;
   }
   __syncthreads();
-  // exclusive scan of cnt[0..E) into cnt, total into cnt[E]: chunk sums per
-  // thread, an inclusive scan of them within each wave (shuffles), the wave
-  // totals scanned by one thread, then each chunk scanned from its offset
-  const int per = (E + kRouteThreads - 1) / kRouteThreads;
-  const int lo = min(E, tid * per), hi = min(E, lo + per);
-  int sum = 0;
-  for (int e = lo; e < hi; ++e) sum += cnt[e];
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  if (lane == 63) chunk[wv] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < kRouteThreads / 64; ++w) {
-      const int c = chunk[w];
-      chunk[w] = run;
-      run += c;
-    }
-    cnt[E] = run;
-  }
-  __syncthreads();
-  int run = chunk[wv] + incl - sum;
-  for (int e = lo; e < hi; ++e) {
+  for (int e = tid; e < E; e += kRouteThreads) {
     const int c = cnt[e];
-    cnt[e] = run;
-    run += c;
+    sidx[e] = c > 0 ? 1 : 0;
+    cpre[e] = c > 0 ? n_win * moe_window_cost(c) : 0;
   }
   __syncthreads();
+  block_exclusive_scan(cnt, E, wave_tot, tid);
+  block_exclusive_scan(sidx, E, wave_tot, tid);
+  block_exclusive_scan(cpre, E, wave_tot, tid);
   for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = cnt[e];
-  // Selected experts, heaviest class first (5+ pairs, 3-4, 2, 1): the work
-  // items of an expert with many pairs cost the most, so they start first.
-  __shared__ int cls_n[4], cls_at[4];
-  if (tid < 4) cls_n[tid] = 0;
-  __syncthreads();
+  // Selected experts in expert order with the prefix of their costs.
   for (int e = tid; e < E; e += kRouteThreads) {
-    const int c = cnt[e + 1] - cnt[e];
-    if (c > 0) atomicAdd(&cls_n[c >= 5 ? 0 : c >= 3 ? 1 : c == 2 ? 2 : 3], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int at = 0;
-    for (int k = 0; k < 4; ++k) {
-      cls_at[k] = at;
-      at += cls_n[k];
+    if (cnt[e + 1] > cnt[e]) {
+      sel[sidx[e]] = e;
+      costp[sidx[e]] = cpre[e];
     }
-    ctl[0] = at * chunks;  // work items
-    ctl[1] = 0;            // item counter
   }
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) {
-    const int c = cnt[e + 1] - cnt[e];
-    if (c > 0) sel[atomicAdd(&cls_at[c >= 5 ? 0 : c >= 3 ? 1 : c == 2 ? 2 : 3], 1)] = e;
+  if (tid == 0) {
+    costp[sidx[E]] = cpre[E];
+    ctl[0] = sidx[E];
   }
   for (int i = tid; i < n; i += kRouteThreads) {
     const int e = ids[i];
@@ -129,49 +141,79 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   }
 }
 
+// 16-byte weight loads each lane keeps in flight per row group, per column
+// width (1, 2, 4, 8 routed pairs per pass) and K band.  One kernel instance
+// holds the segments of all four widths, so its register allocation is the
+// largest of theirs: 8 / 8 / 16 / 16 measured fastest for the 2048 band (the
+// wider passes need more bytes in flight, the narrow ones are held back by the
+// wide ones' registers), and the 16384 band keeps width 4 at 8 so that its
+// instance stays free of scratch spills.
+__host__ __device__ constexpr int moe_rif(int BT, int band) {
+  return BT <= 2 ? 8 : BT <= 4 ? (band >= 16384 ? 8 : 16) : 16;
+}
+
+// The power-of-two band of K whose blocking classes an instance compiles:
+// 2048, 4096, 8192 or 16384 (0: K too large).  Within a band every column
+// width has one class.
+static int moe_band(int64_t K) {
+  return K <= 2048 ? 2048 : K <= 4096 ? 4096 : K <= 8192 ? 8192 : K <= 16384 ? 16384 : 0;
+}
+
 // Rows per window of the routed launch: the largest streaming window over the
-// column widths an expert can take (1, 2, 4, 8 routed pairs per pass); every
-// width's window divides it (all are powers of two).
+// column widths; every width's window divides it (all are powers of two).
 static int moe_window_rows(int64_t K) {
+  const int band = moe_band(K);
   int u = 1;
   for (int bt = 1; bt <= 8; bt *= 2) {
-    const int w = gemv_window_rows_bt(K, bt);
+    const int w = gemv_window_rows_bt(band, bt, moe_rif(bt, band));
     if (w > u) u = w;
   }
   return u;
 }
 
-// Work items are (selected expert, chunk of kMoeChunk windows), heaviest
-// experts first; each workgroup takes the next item from the counter in the
-// workspace (one global atomic per item, requested one item ahead), so an
-// expert with many routed pairs does not hold back a fixed share of the
-// grid.  Every workgroup leaves once the counter passes the item count.
-// Per item the routed pairs are taken up to 8 at a time, each pass with the
-// narrowest column width that holds it.
-// KMAX: the power-of-two band of K (2048, 4096, 8192 or 16384); within a band
-// every column width has one blocking class, so each instance compiles four
-// segment variants only.
+// Static cost-balanced schedule: window j of selected expert i starts at
+// cost costp[i] + j * cost_i (cost_i = moe_window_cost of its pair count),
+// and workgroup g streams the windows whose start lies in its equal share
+// [C g / G, C (g + 1) / G) of the total cost C -- a contiguous run across
+// experts, so each workgroup keeps its windows in flight from one to the
+// next, and an expert with many routed pairs gets proportionally fewer
+// windows per workgroup.  Per expert the routed pairs are taken up to 8 at a
+// time, each pass with the narrowest column width that holds it.
+// KMAX: the band of K (moe_band), so each instance compiles four segment
+// variants only.
 template <int KMAX>
 __global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
     const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int M, int K,
     const int8_t* __restrict__ xq, const float* __restrict__ xd, int per_slot, int top_k,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ list, const int32_t* __restrict__ sel,
-    int32_t* __restrict__ ctl, float* __restrict__ y, int n_win, int chunks, int unit) {
+    const int32_t* __restrict__ costp, const int32_t* __restrict__ ctl, float* __restrict__ y, int n_win,
+    int unit) {
   __shared__ SplitScratch split;
-  __shared__ int s_item;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int nb = K >> 5;
-  const int n_items = ctl[0];
+  const int n_sel = ctl[0];
+  if (n_sel == 0) return;
+  const int64_t C = costp[n_sel];
+  const int64_t G = gridDim.x, g = blockIdx.x;
+  const int64_t c_lo = C * g / G, c_hi = C * (g + 1) / G;
+  // first selected expert whose cost range reaches past c_lo (wave-wide ballot)
+  int i = -1;
+  for (int base = 0; base < n_sel && i < 0; base += 64) {
+    const int k = base + lane;
+    const bool hit = k < n_sel && costp[k + 1] > c_lo;
+    const uint64_t mask = __ballot(hit);
+    if (mask) i = base + __builtin_ctzll(mask);
+  }
   int parity = 0;
-  if (tid == 0) s_item = atomicAdd(&ctl[1], 1);
-  __syncthreads();
-  int item = s_item;
-  while (item < n_items) {
-    __syncthreads();  // every wave has read s_item
-    if (tid == 0) s_item = atomicAdd(&ctl[1], 1);  // the next item, in flight meanwhile
-    const int e = sel[item / chunks];
-    const int wl0 = (item % chunks) * kMoeChunk, wl1 = min(n_win, wl0 + kMoeChunk);
+  for (; i >= 0 && i < n_sel && costp[i] < c_hi; ++i) {
+    const int e = sel[i];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+    const int64_t wc = moe_window_cost(cnt);
+    // windows of this expert whose start cost lies in [c_lo, c_hi)
+    const int64_t r_lo = c_lo - costp[i], r_hi = c_hi - costp[i];
+    const int wl0 = r_lo <= 0 ? 0 : (int)((r_lo + wc - 1) / wc);
+    const int wl1 = (int)min((int64_t)n_win, (r_hi + wc - 1) / wc);
+    if (wl0 >= wl1) continue;
     GemvProblem P;
     P.qs = qs + (int64_t)e * M * (K >> 1);
     P.d = d + (int64_t)e * M * nb;
@@ -202,9 +244,10 @@ __global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
       auto run = [&]<int BT>() {
         constexpr GemvClass cls = gemv_class_of(KMAX, BT);
         static_assert(cls.J != 0, "unsupported band");
-        const int f = unit / GemvShape<BT, cls.J, cls.S>::WIN;
-        gemv_segment<BT, cls.J, cls.S, false, false>(P, cols, nc, wl0 * f, wl1 * f, nullptr, &split, parity,
-                                                     nullptr);
+        constexpr int RIF = moe_rif(BT, KMAX);
+        const int f = unit / GemvShape<BT, cls.J, cls.S, RIF>::WIN;
+        gemv_segment<BT, cls.J, cls.S, false, false, RoutedCols, RIF>(P, cols, nc, wl0 * f, wl1 * f, nullptr,
+                                                                      &split, parity, nullptr);
       };
       if (nc == 1)
         run.template operator()<1>();
@@ -215,9 +258,13 @@ __global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
       else
         run.template operator()<8>();
     }
-    __syncthreads();  // s_item holds the next item
-    item = s_item;
   }
+}
+
+int64_t moe_schedule_cost_bound(int64_t E, int64_t M, int64_t K, int64_t n) {
+  const int unit = moe_window_rows(K);
+  const int64_t n_win = (M + unit - 1) / unit;
+  return n_win * kMoeMaxWindowCost * ((n + 7) / 8 + E);
 }
 
 hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
@@ -228,13 +275,13 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
   int32_t* list = offsets + E + 1;
   int32_t* rank = list + n;
   int32_t* sel = rank + n;
-  int32_t* ctl = sel + E;
+  int32_t* costp = sel + E;
+  int32_t* ctl = costp + E + 1;
   const int unit = moe_window_rows(K);
   const int64_t n_win = (M + unit - 1) / unit;
-  const int chunks = (int)((n_win + kMoeChunk - 1) / kMoeChunk);
-  const size_t route_lds = ((size_t)E + 1 + kRouteThreads / 64) * sizeof(int);
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)M, chunks,
-                     offsets, list, rank, sel, ctl, y);
+  const size_t route_lds = (3 * ((size_t)E + 1) + kRouteThreads / 64) * sizeof(int);
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)n_win,
+                     offsets, list, rank, sel, costp, ctl, (int)M, y);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   auto go = [&](auto kernel) {
@@ -254,20 +301,17 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
       }
     }
     int64_t grid = resident;
-    if (grid > E * chunks) grid = E * chunks;
+    if (grid > E * n_win) grid = E * n_win;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kGemvThreads), 0, s, qs, d, (int)M, (int)K, xq, xd,
-                       n_x_slots == 1 ? 0 : 1, (int)top_k, offsets, list, sel, ctl, y, (int)n_win, chunks, unit);
+                       n_x_slots == 1 ? 0 : 1, (int)top_k, offsets, list, sel, costp, ctl, y, (int)n_win, unit);
   };
-  if (K <= 2048)
-    go(moe_stream_kernel<2048>);
-  else if (K <= 4096)
-    go(moe_stream_kernel<4096>);
-  else if (K <= 8192)
-    go(moe_stream_kernel<8192>);
-  else if (K <= 16384)
-    go(moe_stream_kernel<16384>);
-  else
-    return hipErrorInvalidValue;
+  switch (moe_band(K)) {
+    case 2048: go(moe_stream_kernel<2048>); break;
+    case 4096: go(moe_stream_kernel<4096>); break;
+    case 8192: go(moe_stream_kernel<8192>); break;
+    case 16384: go(moe_stream_kernel<16384>); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -213,9 +213,13 @@ int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan* plan, void*
  *       bytes, 16-byte aligned, owned by the caller; its contents on entry do
  *       not matter and on exit are unspecified.  Calls that share a workspace
  *       must be ordered on one stream.
- *   1 <= E <= 8192, T * top_k <= 65536, top_k <= 64, K <= 16384.
+ *   1 <= E <= 4096, T * top_k <= 65536, top_k <= 64, K <= 16384; M times
+ *   (E + T * top_k / 8) must stay below about 2^31 / 33 / rows-per-window
+ *   (Q4Q8_E_UNSUPPORTED otherwise; no expert layer comes near it).
  * Each selected expert's weights are streamed once per call (its routed
- * pairs taken up to 8 at a time); the routing runs on the device.
+ * pairs taken up to 8 at a time); the routing runs on the device, and the
+ * selected experts' row windows are split over the grid in equal shares of
+ * estimated streaming cost.
  */
 size_t mul_mat_id_q4q8_workspace(int64_t E, int64_t T, int64_t top_k);
 int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,

@@ -99,12 +99,19 @@ def test_mul_mat_id_validation():
     L = q.lib()
     p = _v(256)
     ws = q.mul_mat_id_q4q8_workspace(64, 16, 8)
-    assert ws >= 4 * (64 + 1 + 2 * 16 * 8 + 64 + 4) and ws % 16 == 0
+    # offsets[E + 1] | list[n] | rank[n] | sel[E] | cost prefix[E + 1] | control[4]
+    assert ws >= 4 * (64 + 1 + 2 * 16 * 8 + 64 + 65 + 4) and ws % 16 == 0
     # n_x_slots neither 1 nor top_k
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 3, p, 16, 8, p, p, ws, None) == q.Q4Q8_E_ARG
     # top_k out of range, E out of range
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, p, 16, 0, p, p, ws, None) == q.Q4Q8_E_ARG
     assert L.mul_mat_id_q4q8(p, p, 0, 128, 256, p, p, 1, p, 16, 8, p, p, ws, None) == q.Q4Q8_E_ARG
+    ws_big = q.mul_mat_id_q4q8_workspace(4097, 16, 8)
+    assert L.mul_mat_id_q4q8(p, p, 4097, 128, 256, p, p, 1, p, 16, 8, p, p, ws_big, None) == q.Q4Q8_E_ARG
+    # a schedule whose total cost would overflow int32 is refused before any device call
+    ws_4k = q.mul_mat_id_q4q8_workspace(4096, 16, 8)
+    assert L.mul_mat_id_q4q8(p, p, 4096, 1 << 30, 256, p, p, 1, p, 16, 8, p, p, ws_4k,
+                             None) == q.Q4Q8_E_UNSUPPORTED
     # workspace too small
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, p, 16, 8, p, p, ws - 16, None) == q.Q4Q8_E_ARG
     # misaligned workspace
