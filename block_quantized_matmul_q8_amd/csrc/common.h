@@ -80,13 +80,13 @@ __device__ __forceinline__ float sqrt_rn(float x) {
   return y;
 }
 
-// Exact int32 block product sum_j q_j * x_j of one Q4 block (16 bytes of
+// Exact int32 block product s0 + sum_j q_j * x_j of one Q4 block (16 bytes of
 // packed unsigned codes) with one Q8 block (two int4 of codes).
-__device__ __forceinline__ int dot_block(const u32x4 w, const i32x4 xa, const i32x4 xb) {
+__device__ __forceinline__ int dot_block(const u32x4 w, const i32x4 xa, const i32x4 xb, int s0 = 0) {
   // lo nibbles of byte j = code j (pairs with x codes 0..15 = xa);
   // hi nibbles of byte j = code j+16 (pairs with x codes 16..31 = xb).
   const uint32_t m = 0x0F0F0F0Fu;
-  int s = 0;
+  int s = s0;
   s = __builtin_amdgcn_sdot4((int)(w.x & m), xa.x, s, false);
   s = __builtin_amdgcn_sdot4((int)(w.y & m), xa.y, s, false);
   s = __builtin_amdgcn_sdot4((int)(w.z & m), xa.z, s, false);

@@ -257,7 +257,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
         xa[c][j] = valid ? xa[c][j] : zero;
         xb[c][j] = valid ? xb[c][j] : zero;
         xdr[c][j] = valid ? xdr[c][j] : 0.0f;
-        xsr[c][j] = code_sum8(xa[c][j], xb[c][j]);
+        xsr[c][j] = kMagicBits - code_sum8(xa[c][j], xb[c][j]);
       }
   } else {
     // Folded-in prologue: window A is requested first, then the whole
@@ -283,12 +283,12 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
           xa[c][j] = src[0];
           xb[c][j] = src[1];
           xdr[c][j] = sxd[c * nb + b];
-          xsr[c][j] = 8 * sxs[c * nb + b];
+          xsr[c][j] = kMagicBits - 8 * sxs[c * nb + b];
         } else {
           xa[c][j] = i32x4{0, 0, 0, 0};
           xb[c][j] = i32x4{0, 0, 0, 0};
           xdr[c][j] = 0.0f;
-          xsr[c][j] = 0;
+          xsr[c][j] = kMagicBits;
         }
       }
     load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
@@ -301,6 +301,11 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
 
   // One row group: block sums, scale, multi-row reduction, store (through
   // the part exchange when K is split).
+  // The block sum is accumulated onto kMagicBits - 8 sum x (xsr holds that
+  // seed), so its bits read as the float 1.5 * 2^23 + I (exact: |I| < 2^22)
+  // and I * d_w comes out of one fma against -1.5 * 2^23 * d_w (exact: 2 + 11
+  // significant bits) with a single rounding -- no integer subtract, no
+  // conversion, and the column's d_x is applied by a second fma.
   auto compute_group = [&](int row0, const u32x4 (&w)[RU][J], const uint32_t (&dw)[RU][J]) {
     float acc[NP];
 #pragma unroll
@@ -310,11 +315,14 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
 #pragma unroll
       for (int r = 0; r < RU; ++r) {
         const float dwf = f16_bits_to_f32((uint16_t)dw[r][j]);
+        const float cwf = -kMagic * dwf;
 #pragma unroll
         for (int c = 0; c < BT; ++c) {
-          const int I = dot_block(w[r][j], xa[c][j], xb[c][j]) - xsr[c][j];
-          acc[r * BT + c] = __builtin_fmaf((float)I, dwf * xdr[c][j], acc[r * BT + c]);
+          const int Fb = dot_block(w[r][j], xa[c][j], xb[c][j], xsr[c][j]);
+          const float t = __builtin_fmaf(__builtin_bit_cast(float, Fb), dwf, cwf);
+          acc[r * BT + c] = __builtin_fmaf(t, xdr[c][j], acc[r * BT + c]);
           if (WRITE_I) {
+            const int I = Fb - kMagicBits;
             const int b = kb0 + lane + kWave * j;
             const int row = row0 + r;
             if (c < B && b < nb && row <= row_last) Iout[((int64_t)c * M + row) * nb + b] = I;
