@@ -98,6 +98,17 @@ __device__ __forceinline__ int dot_block(const u32x4 w, const i32x4 xa, const i3
   return s;
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// fences global memory, which makes every wave wait for all of its global
+// loads in flight -- a streaming kernel would drain its prefetch at every
+// exchange.  Here the fences are limited to the local (LDS) address space, so
+// the barrier waits for this wave's LDS accesses and nothing else.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
       if (holder && c < B && row <= row_last) gptr_w(my_out)[row] = v;
     } else {
       if (holder) split->v[parity][wave][k] = v;
-      __syncthreads();
+      lds_barrier();
       if (kp == 0 && holder && c < B && row <= row_last) {
         float t = v;
 #pragma unroll
