@@ -46,10 +46,11 @@ def _load():
     lib.orc_mul_mat.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
     lib.orc_mul_mat_mt.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, i32]
     lib.orc_mul_mat_id.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, i32]
+    lib.orc_moe_expert_sum.argtypes = [vp, vp, i64, i64, i64, vp]
     for name in ("orc_f32_to_f16_array", "orc_f16_to_f32_array", "orc_q4_quantize",
                  "orc_q4_unpack_codes", "orc_rmsnorm", "orc_mul_rows", "orc_q8_quantize",
                  "orc_q8_quantize_rmsnorm", "orc_block_dots", "orc_mul_mat", "orc_mul_mat_mt",
-                 "orc_mul_mat_id"):
+                 "orc_mul_mat_id", "orc_moe_expert_sum"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -206,6 +207,22 @@ def mul_mat_id(qs, d, xq, xd, ids, nthreads=1):
     _load().orc_mul_mat_id(_p(qs), _p(d), E, M, K, _p(xq), _p(xd), n_x_slots, _p(ids), T, top_k,
                            _p(y), int(nthreads))
     return y
+
+
+def moe_expert_sum(y, w=None):
+    """Expert-plane sum: y f32 [T][top_k][M], w f32 [T][top_k] or None ->
+    out f32 [T][M], the in-order chain of fp32 products and sums."""
+    y = _c(y, np.float32)
+    T, top_k, M = y.shape
+    if top_k < 1:
+        raise ValueError("top_k must be >= 1")
+    if w is not None:
+        w = _c(w, np.float32)
+        if w.shape != (T, top_k):
+            raise ValueError("shape mismatch")
+    out = np.empty((T, M), dtype=np.float32)
+    _load().orc_moe_expert_sum(_p(y), _p(w), T, top_k, M, _p(out))
+    return out
 
 
 def dequantize_q4(qs, d, K):

@@ -389,3 +389,16 @@ void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                            yrow, NULL, nthreads);
         }
 }
+
+void orc_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M, float* out) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t m = 0; m < M; ++m) {
+            float acc = 0.0f;
+            for (int64_t s = 0; s < top_k; ++s) {
+                const float yv = y[(t * top_k + s) * M + m];
+                const float v = w ? w[t * top_k + s] * yv : yv;
+                acc = (s == 0) ? v : acc + v;
+            }
+            out[t * M + m] = acc;
+        }
+}

@@ -103,6 +103,18 @@ void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                     const int8_t* xq, const float* xd, int64_t n_x_slots,
                     const int32_t* ids, int64_t T, int64_t top_k, float* y, int nthreads);
 
+/* Sum of the expert planes of a MUL_MAT_ID result.  The page "llama.cpp
+ * b10981发布：OpenVINO后端优化有状态解码与GPU MoE推理" describes the expert
+ * planes being added by a chain of ADD ops (and a reordered reduction of that
+ * chain drifting in f32).  Each plane is first scaled by its routing weight
+ * (a MUL), then the chain runs over the slots in order:
+ *   v_s = fl(w[t][s] * y[t][s][m])              (w == NULL: v_s = y[t][s][m])
+ *   out[t][m] = fl(...fl(fl(v_0 + v_1) + v_2)... + v_{top_k-1})
+ * one fp32 rounding per product and per sum, no fused multiply-add.  A NaN
+ * plane (an invalid expert id) makes the output NaN.  y [T][top_k][M],
+ * w [T][top_k], out [T][M]; top_k >= 1. */
+void orc_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,9 @@ products are exact), the fp32 forward error bound of a length-nb sum, the
 K-block permutation invariance of the exact integer sums, the offset
 identity sum (q-8) x = sum q x - 8 sum x, and, for the expert-routed product,
 a loop of plain products, the E = 1 / top_k = 1 reduction and NaN rows for
-bad ids.
+bad ids.  The expert-plane sum is pinned by an example whose value depends on
+the summation order, exact integer sums, the correctly rounded single
+product, and the fp32 error bound of the chain against an fp64 sum.
 """
 import numpy as np
 import pytest
@@ -181,3 +183,47 @@ def test_expert_ids_distinct_and_in_range():
     assert ids.shape == (16, 8) and ids.dtype == np.int32
     assert ids.min() >= 0 and ids.max() < 64
     assert all(len(set(r.tolist())) == 8 for r in ids)
+
+
+def test_expert_sum_follows_the_add_chain_order():
+    # 1 + 2^-24 + 2^-24: the in-order chain rounds twice back to 1, while adding
+    # the two small planes first gives 1 + 2^-23 (exact)
+    y = np.array([[[1.0], [U], [U]]], dtype=np.float32)
+    assert oracle.moe_expert_sum(y)[0, 0] == np.float32(1.0)
+    assert oracle.moe_expert_sum(np.ascontiguousarray(y[:, ::-1]))[0, 0] == np.float32(1.0 + 2 * U)
+
+
+def test_expert_sum_exact_on_integers():
+    g = np.random.default_rng(11)
+    T, top_k, M = 5, 8, 33
+    yi = g.integers(-1000, 1001, size=(T, top_k, M))
+    wi = g.integers(-8, 9, size=(T, top_k))
+    out = oracle.moe_expert_sum(yi.astype(np.float32), wi.astype(np.float32))
+    assert np.array_equal(out.astype(np.int64), np.einsum("tsm,ts->tm", yi, wi))
+    out1 = oracle.moe_expert_sum(yi.astype(np.float32))
+    assert np.array_equal(out1.astype(np.int64), yi.sum(axis=1))
+
+
+def test_expert_sum_single_slot_is_the_rounded_product():
+    g = np.random.default_rng(12)
+    y = g.standard_normal((4, 1, 50)).astype(np.float32)
+    w = g.standard_normal((4, 1)).astype(np.float32)
+    exact = y.astype(np.float64) * w.astype(np.float64)[:, :, None]   # exact in fp64
+    assert np.array_equal(oracle.moe_expert_sum(y, w), exact[:, 0].astype(np.float32))
+
+
+def test_expert_sum_error_bound_and_nan_planes():
+    T, top_k, M = 16, 8, 300
+    g = np.random.default_rng(13)
+    y = g.standard_normal((T, top_k, M)).astype(np.float32)
+    w = workloads.expert_weights(3, T, top_k)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6) and (w > 0).all()
+    out = oracle.moe_expert_sum(y, w).astype(np.float64)
+    terms = y.astype(np.float64) * w.astype(np.float64)[:, :, None]
+    ref = terms.sum(axis=1)
+    n = 2 * top_k
+    bound = n * U / (1 - n * U) * np.abs(terms).sum(axis=1)
+    assert np.all(np.abs(out - ref) <= bound)
+    y[3, 5, :] = np.nan
+    out = oracle.moe_expert_sum(y, w)
+    assert np.all(np.isnan(out[3])) and np.all(np.isfinite(np.delete(out, 3, axis=0)))

@@ -24,6 +24,7 @@ KIND_WEIGHT = 0
 KIND_ACT = 1
 KIND_NORM = 2
 KIND_IDS = 3
+KIND_ROUTE_W = 4
 
 WEIGHT_SIGMA = 0.02
 NORM_SIGMA = 0.1
@@ -56,6 +57,15 @@ def expert_ids(seed: int, T: int, E: int, top_k: int) -> np.ndarray:
     top_k distinct experts, uniform without replacement.  int32 [T][top_k]."""
     g = rng(seed, 0, 0, KIND_IDS)
     return np.stack([g.permutation(E)[:top_k] for _ in range(T)]).astype(np.int32)
+
+
+def expert_weights(seed: int, T: int, top_k: int) -> np.ndarray:
+    """Routing weights of the selected experts: per token, a softmax of
+    top_k standard-normal logits (drawn in float32, exponentiated and
+    normalised in float64, stored as float32).  f32 [T][top_k]."""
+    z = rng(seed, 0, 0, KIND_ROUTE_W).standard_normal((T, top_k), dtype=np.float32).astype(np.float64)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 def weight_device(seed: int, layer: int, matrix: int, M: int, K: int, device, sigma: float = WEIGHT_SIGMA):
