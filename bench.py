@@ -494,9 +494,19 @@ def bench_moe(args, dev):
     for qs, d, xq, xd, y, ws, M, K, S in mats:
         nbytes += distinct * q4_bytes(M, K) + cfg.T * S * K * 9 // 8 + cfg.T * cfg.top_k * M * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # the weighted expert-plane sum of the down projection's planes
+    y_down = mats[1][4]
+    w = torch.from_numpy(wl.expert_weights(0, cfg.T, cfg.top_k)).to(dev)
+    out = torch.empty((cfg.T, cfg.hidden), dtype=torch.float32, device=dev)
+    ms_sum = per_launch_ms(lambda: q.moe_expert_sum_f32(y_down, w, out=out), 20)
+    sum_bytes = cfg.T * cfg.top_k * (cfg.hidden + 1) * 4 + cfg.T * cfg.hidden * 4
     return {"GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
             "distinct_experts": distinct, "bytes": nbytes,
-            "launches": "2 routed calls (stacked gate/up, down), each a routing kernel + a streaming kernel"}
+            "launches": "2 routed calls (stacked gate/up, down), each a routing kernel + a streaming kernel",
+            "expert_sum": {"us": round(ms_sum * 1e3, 2), "GB/s": round(sum_bytes / (ms_sum * 1e-3) / 1e9, 1),
+                           "bytes": sum_bytes,
+                           "what": "weighted in-order sum of the down projection's 8 expert planes, "
+                                   "[16][8][2048] -> [16][2048], one launch"}}
 
 
 def cpu_baseline(model, seconds=10.0):

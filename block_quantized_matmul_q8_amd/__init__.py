@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
     L.mul_mat_id_q4q8_workspace.restype = sz
     L.mul_mat_id_q4q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
     L.mul_mat_q4q8_rmsnorm.argtypes = [vp, vp, i64, i64, vp, vp, f32, u32, i64, vp, vp]
+    L.moe_expert_sum_f32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.q4q8_group_build.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int32, i64, vp, sz, vp, sz,
                                    ctypes.POINTER(GroupPlan)]
     L.mul_mat_q4q8_group.argtypes = [vp, ctypes.POINTER(GroupPlan), vp]
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
                  "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
-                 "q4q8_group_build", "mul_mat_q4q8_group"):
+                 "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -359,6 +360,29 @@ def mul_mat_id_q4q8(qs, d, xq, xd, ids, y=None, ws=None, stream=None):
            lib().mul_mat_id_q4q8(_ptr(qs), _ptr(d), E, M, K, _ptr(xq), _ptr(xd), S, _ptr(ids), T, top_k, _ptr(y),
                                  _ptr(ws), ws.numel(), _stream(stream, qs.device)))
     return y
+
+
+def moe_expert_sum_f32(y, w=None, out=None, stream=None):
+    """Expert-plane sum: y f32 [T][top_k][M] (a mul_mat_id_q4q8 result),
+    w f32 [T][top_k] routing weights or None -> out f32 [T][M], the in-order
+    chain of fp32 products and sums."""
+    _need(y, "y", (torch.float32,), 3)
+    T, top_k, M = y.shape
+    if w is not None:
+        _need(w, "w", (torch.float32,), 2)
+        if tuple(w.shape) != (T, top_k):
+            raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=y.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (T, M):
+        raise ValueError("shape mismatch")
+    for t, name in ((y, "y"), (w, "w"), (out, "out")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check("moe_expert_sum_f32",
+           lib().moe_expert_sum_f32(_ptr(y), _ptr(w), T, top_k, M, _ptr(out), _stream(stream, y.device)))
+    return out
 
 
 def q4q8_set_path(path: int) -> None:

@@ -223,6 +223,26 @@ Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E,
                   "mul_mat_id_q4q8");
 }
 
+Q4Q8_EXPORT int moe_expert_sum_f32(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M,
+                                   float* out, void* stream) {
+  if (T < 0 || M < 0 || top_k < 1 || top_k > 64)
+    return fail(Q4Q8_E_ARG, "T = %lld, M = %lld must be >= 0 and top_k = %lld in [1, 64]", (long long)T,
+                (long long)M, (long long)top_k);
+  if (T > 65535) return fail(Q4Q8_E_ARG, "T = %lld exceeds 65535", (long long)T);
+  if (M > INT32_MAX / 2) return fail(Q4Q8_E_ARG, "M exceeds 2^30");
+  if (T == 0 || M == 0) return ok();
+  if (!y || !out) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(y, 4) || !aligned(out, 4) || (w && !aligned(w, 4)))
+    return fail(Q4Q8_E_ALIGN, "y, w, out must be 4-byte aligned");
+  const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uintptr_t)(T * top_k * M) * 4;
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (uintptr_t)(T * M) * 4;
+  if (o0 < y1 && y0 < o1) return fail(Q4Q8_E_ARG, "out must not overlap y");
+  int st;
+  if ((st = check_device())) return st;
+  return launched(q4q8::launch_moe_expert_sum(y, w, T, top_k, M, out, static_cast<hipStream_t>(stream)),
+                  "moe_expert_sum_f32");
+}
+
 Q4Q8_EXPORT int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
                                      const float* x, const float* g, float eps, uint32_t flags, int64_t B,
                                      float* y, void* stream) {

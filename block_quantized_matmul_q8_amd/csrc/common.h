@@ -183,6 +183,8 @@ Q4Q8_HIDDEN int64_t gemm_tiles(int64_t M, int64_t B);
 Q4Q8_HIDDEN hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
                                    int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s);
 Q4Q8_HIDDEN size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+Q4Q8_HIDDEN hipError_t launch_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k,
+                                             int64_t M, float* out, hipStream_t s);
 // Upper bound of the routed launch's total schedule cost (it must fit int32).
 Q4Q8_HIDDEN int64_t moe_schedule_cost_bound(int64_t E, int64_t M, int64_t K, int64_t n);
 Q4Q8_HIDDEN hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M,

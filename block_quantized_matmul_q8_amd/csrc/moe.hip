@@ -315,4 +315,36 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
   return hipGetLastError();
 }
 
+// Expert-plane sum after MUL_MAT_ID ("llama.cpp b10981发布：OpenVINO后端优化
+// 有状态解码与GPU MoE推理": the planes are added by a chain of ADD ops, and a
+// reordered reduction drifts in f32).  out[t][m] is the in-order chain over
+// the slots of fl(w[t][s] * y[t][s][m]), one rounding per product and per sum
+// and no contraction, so it equals that chain bit for bit.  Thread per
+// element; a workgroup covers 256 consecutive m of one token, so the weights
+// of the token are uniform and the plane reads are coalesced.
+constexpr int kSumThreads = 256;
+
+__global__ __launch_bounds__(kSumThreads) void moe_expert_sum_kernel(const float* __restrict__ y,
+                                                                    const float* __restrict__ w, int top_k,
+                                                                    int64_t M, float* __restrict__ out) {
+  const int64_t t = blockIdx.y;
+  const int64_t m = (int64_t)blockIdx.x * kSumThreads + threadIdx.x;
+  if (m >= M) return;
+  const float* yp = y + t * top_k * M + m;
+  float acc = 0.0f;
+  for (int s = 0; s < top_k; ++s) {
+    const float yv = gptr(yp)[(int64_t)s * M];
+    const float v = w ? __fmul_rn(gptr(w)[t * top_k + s], yv) : yv;
+    acc = s == 0 ? v : __fadd_rn(acc, v);
+  }
+  gptr_w(out)[t * M + m] = acc;
+}
+
+hipError_t launch_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M, float* out,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)((M + kSumThreads - 1) / kSumThreads), (unsigned)T);
+  hipLaunchKernelGGL(moe_expert_sum_kernel, grid, dim3(kSumThreads), 0, s, y, w, (int)top_k, M, out);
+  return hipGetLastError();
+}
+
 }  // namespace q4q8

@@ -226,6 +226,24 @@ int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                     const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
                     int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_expert_sum_f32 -- sum of the expert planes of a MUL_MAT_ID result.  The
+ * OpenVINO page ("llama.cpp b10981发布：OpenVINO后端优化有状态解码与GPU MoE推理")
+ * describes those planes being added by a chain of ADD ops after the routing
+ * weights are applied, and notes that a reordered f32 reduction of the chain
+ * drifts from the reference.  This call computes the chain in order:
+ *   out[t][m] = fl(...fl(v_0 + v_1)... + v_{top_k-1}),  v_s = fl(w[t][s] * y[t][s][m])
+ * (v_s = y[t][s][m] when w is null), one fp32 rounding per product and per
+ * sum, so the result is bit-identical to that chain.
+ *   y   [T][top_k][M] f32 device (e.g. mul_mat_id_q4q8's output), 4-byte aligned
+ *   w   [T][top_k] f32 device routing weights, or null
+ *   out [T][M] f32 device, must not overlap y
+ *   1 <= top_k <= 64, T <= 65535.  A NaN plane (invalid expert id) gives NaN.
+ * Async on `stream`.  Q4Q8_E_ARG / Q4Q8_E_ALIGN on invalid arguments.
+ */
+int moe_expert_sum_f32(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M, float* out,
+                       void* stream);
+
 /* ---------------------------------------------------------------------------
  * Test hooks (not for production use).  The GGML backend page's CUDA section
  * keeps switches that force one matrix route only for cross-checking; these

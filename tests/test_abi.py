@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_id_q4q8",
+    for n in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_id_q4q8", "moe_expert_sum_f32",
               "mul_mat_id_q4q8_workspace", "q4q8_last_error", "q4q8_set_path",
               "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_version"):
         assert n in names, n
@@ -118,6 +118,19 @@ def test_mul_mat_id_validation():
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, p, 16, 8, p, _v(260), ws, None) == q.Q4Q8_E_ALIGN
     # null ids
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, None, 16, 8, p, p, ws, None) == q.Q4Q8_E_ARG
+
+
+def test_moe_expert_sum_validation():
+    L = q.lib()
+    y, out = _v(256), _v(65536)
+    assert L.moe_expert_sum_f32(y, None, 4, 0, 16, out, None) == q.Q4Q8_E_ARG      # top_k < 1
+    assert L.moe_expert_sum_f32(y, None, 4, 65, 16, out, None) == q.Q4Q8_E_ARG     # top_k > 64
+    assert L.moe_expert_sum_f32(y, None, -1, 2, 16, out, None) == q.Q4Q8_E_ARG
+    assert L.moe_expert_sum_f32(None, None, 4, 2, 16, out, None) == q.Q4Q8_E_ARG
+    assert L.moe_expert_sum_f32(_v(258), None, 4, 2, 16, out, None) == q.Q4Q8_E_ALIGN
+    # out inside y's [T][top_k][M] planes
+    assert L.moe_expert_sum_f32(y, None, 4, 2, 16, _v(256 + 64), None) == q.Q4Q8_E_ARG
+    assert L.moe_expert_sum_f32(None, None, 0, 2, 16, None, None) == q.Q4Q8_OK      # empty: no device use
 
 
 def test_empty_problems_are_noops_without_device():

@@ -132,3 +132,45 @@ def test_full_moe_stacked_gate_up():
     y = _gpu(qs, d, xq, xd, ids)
     y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=16)
     assert_close(y, y_o, "stacked gate/up")
+
+
+def _sum_gpu(y, w):
+    out = q.moe_expert_sum_f32(to_dev(y), None if w is None else to_dev(w))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,top_k,M", [(16, 8, 2048), (3, 1, 5), (7, 5, 300), (1, 64, 257), (2, 3, 70000)])
+def test_expert_sum_bit_exact(T, top_k, M):
+    g = np.random.default_rng(40 + top_k)
+    y = (g.standard_normal((T, top_k, M)) * np.exp(g.uniform(-20, 20, size=(T, top_k, 1)))).astype(np.float32)
+    y[0, 0, :3] = [0.0, -0.0, 1e-45]
+    w = workloads.expert_weights(40, T, top_k)
+    for wv in (w, None):
+        out = _sum_gpu(y, wv)
+        ref = oracle.moe_expert_sum(y, wv)
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_expert_sum_of_routed_down_projection():
+    """The MoE down projection as the benchmark runs it (64 experts of
+    2048 x 1408, 16 tokens, top-8, one row per (token, slot)), followed by
+    the weighted expert-plane sum; a bad id makes its token's sum NaN."""
+    cfg = workloads.MOE
+    ids = workloads.expert_ids(0, cfg.T, cfg.E, cfg.top_k)
+    ids[5, 2] = cfg.E
+    _, qs, d = _experts(3, cfg.E, cfg.hidden, cfg.ffn)
+    xq, xd = _acts(3, cfg.T, cfg.top_k, cfg.ffn)
+    w = workloads.expert_weights(0, cfg.T, cfg.top_k)
+    y = q.mul_mat_id_q4q8(to_dev(qs), to_dev(d.view(np.int16)), to_dev(xq), to_dev(xd), to_dev(ids))
+    out = q.moe_expert_sum_f32(y, to_dev(w))
+    torch.cuda.synchronize()
+    y, out = y.cpu().numpy(), out.cpu().numpy()
+    # bit-exact against the chain over the GPU's own planes
+    assert np.array_equal(out.view(np.uint32), oracle.moe_expert_sum(y, w).view(np.uint32))
+    # and within tolerance of the oracle end to end (rows without the bad id)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=16)
+    out_o = oracle.moe_expert_sum(y_o, w)
+    assert np.all(np.isnan(out[5])) and np.all(np.isnan(out_o[5]))
+    keep = [t for t in range(cfg.T) if t != 5]
+    assert_close(out[keep], out_o[keep], "expert sum of the down projection")
