@@ -47,10 +47,11 @@ def _load():
     lib.orc_mul_mat_mt.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, i32]
     lib.orc_mul_mat_id.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, i32]
     lib.orc_moe_expert_sum.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.orc_q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp]
     for name in ("orc_f32_to_f16_array", "orc_f16_to_f32_array", "orc_q4_quantize",
                  "orc_q4_unpack_codes", "orc_rmsnorm", "orc_mul_rows", "orc_q8_quantize",
                  "orc_q8_quantize_rmsnorm", "orc_block_dots", "orc_mul_mat", "orc_mul_mat_mt",
-                 "orc_mul_mat_id", "orc_moe_expert_sum"):
+                 "orc_mul_mat_id", "orc_moe_expert_sum", "orc_q8_quantize_rmsnorm_add"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -150,6 +151,25 @@ def q8_quantize_rmsnorm(x, g, eps, no_norm=False):
     xs = np.empty((B, K // 32), dtype=np.int32)
     _load().orc_q8_quantize_rmsnorm(_p(x), B, K, _p(g), np.float32(eps), int(bool(no_norm)),
                                     _p(xq), _p(xd), _p(xs))
+    return xq, xd, xs
+
+
+def q8_quantize_rmsnorm_add(x, g, a, eps):
+    """RMS_NORM + MUL + ADD -> Q8: x f32 [B][K], g f32 [K], a f32 [K] (one
+    addend for every row) or [B][K] (one per row).  Returns xq i8 [B][K],
+    xd f32 [B][K/32], xs i32 [B][K/32]."""
+    x = _c(x, np.float32)
+    g = _c(g, np.float32)
+    a = _c(a, np.float32)
+    B, K = x.shape
+    _check_k(K)
+    if g.shape != (K,) or a.shape not in ((K,), (B, K)):
+        raise ValueError("shape mismatch")
+    stride = 0 if a.ndim == 1 else K
+    xq = np.empty((B, K), dtype=np.int8)
+    xd = np.empty((B, K // 32), dtype=np.float32)
+    xs = np.empty((B, K // 32), dtype=np.int32)
+    _load().orc_q8_quantize_rmsnorm_add(_p(x), B, K, _p(g), _p(a), stride, float(eps), _p(xq), _p(xd), _p(xs))
     return xq, xd, xs
 
 

@@ -270,6 +270,21 @@ void orc_q8_quantize_rmsnorm(const float* x, int64_t B, int64_t K, const float* 
     free(v);
 }
 
+void orc_q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g, const float* a,
+                                 int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs) {
+    float* t = (float*)malloc((size_t)(B * K) * sizeof(float));
+    float* v = (float*)malloc((size_t)(B * K) * sizeof(float));
+    orc_rmsnorm(x, B, K, eps, t, NULL);
+    orc_mul_rows(t, B, K, g, v);
+    for (int64_t b = 0; b < B; ++b) {
+        const float* ar = a + b * a_row_stride;
+        for (int64_t k = 0; k < K; ++k) v[b * K + k] = v[b * K + k] + ar[k];
+    }
+    orc_q8_quantize(v, B, K, xq, xd, xs);
+    free(t);
+    free(v);
+}
+
 /* ------------------------------------------------------------------ */
 /* Block integer dot: I = sum_j (q4_j - 8) * q8_j, exact in int32      */
 /* (|I| <= 32 * 8 * 127 = 32512).                                       */

@@ -103,6 +103,17 @@ void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                     const int8_t* xq, const float* xd, int64_t n_x_slots,
                     const int32_t* ids, int64_t T, int64_t top_k, float* y, int nthreads);
 
+/* RMS_NORM + MUL + ADD prologue.  The Metal fusion page ("llama.cpp
+ * b10909：Metal后端融合表重构...", its fusion-pattern counts) lists the
+ * RMS_NORM+MUL+ADD pattern beside RMS_NORM+MUL; reading: the three ops in that
+ * order, each rounded as its own op, then Q8:
+ *   v[b][k] = fl( fl( fl(x[b][k] * s_b) * g[k] ) + a_b[k] ),
+ * s_b the RMS scale of orc_rmsnorm, a_b = a + b * a_row_stride (stride 0: one
+ * [K] addend for every row; stride K: an addend row per row), then
+ * orc_q8_quantize(v). */
+void orc_q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g, const float* a,
+                                 int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs);
+
 /* Sum of the expert planes of a MUL_MAT_ID result.  The page "llama.cpp
  * b10981发布：OpenVINO后端优化有状态解码与GPU MoE推理" describes the expert
  * planes being added by a chain of ADD ops (and a reordered reduction of that

@@ -218,3 +218,59 @@ def test_golden_rmsnorm_examples_rederived_exactly(hand_examples):
         assert mod.bits(r["d"]) == hand_examples[name]["xd_bits"]
         assert r["v_times_id"] == hand_examples[name]["code"]
     assert mod.bits(mod.e5_y(mod.constant_row(1)["d"], hand_examples["E5"]["I"])) == hand_examples["E5"]["y_bits"]
+
+
+# --- RMS_NORM + MUL + ADD -> Q8 ---------------------------------------------
+
+@pytest.mark.parametrize("K", [32, 1408, 4096])
+def test_norm_add_zero_addend_is_rmsnorm(K):
+    """A zero addend leaves RMS_NORM+MUL -> Q8 unchanged, bit for bit."""
+    x = workloads.activation(4, 1, 0, 3, K)
+    g = workloads.norm_weight(4, 1, 0, K)
+    a = np.zeros(K, dtype=np.float32)
+    for u, w in zip(oracle.q8_quantize_rmsnorm_add(x, g, a, 1e-5), oracle.q8_quantize_rmsnorm(x, g, 1e-5)):
+        assert np.array_equal(u, w)
+
+
+@pytest.mark.parametrize("K", [64, 2048])
+def test_norm_add_equals_unfused(K):
+    """Fused RMS_NORM+MUL+ADD == rmsnorm -> multiply by g -> an fp32 add (numpy's
+    IEEE single add) -> q8_quantize, bit for bit, for one addend per row and one
+    shared addend."""
+    x = workloads.activation(5, 1, 0, 4, K)
+    g = workloads.norm_weight(5, 1, 0, K)
+    a_rows = workloads.activation(5, 2, 0, 4, K)
+    t, _ = oracle.rmsnorm(x, 1e-5)
+    v = oracle.mul_rows(t, g)
+    for a in (a_rows, a_rows[1]):
+        ref = oracle.q8_quantize((v + a).astype(np.float32))
+        got = oracle.q8_quantize_rmsnorm_add(x, g, a, 1e-5)
+        for u, w in zip(got, ref):
+            assert np.array_equal(u, w)
+
+
+def test_norm_add_hand_example(hand_examples):
+    """E5 (K = 32, x = 1, g = 1, eps = 1e-5: s = 1 - 84 * 2^-24) with the
+    addend -s on the first 16 elements and 0.25 on the last 16.  The ADD comes
+    after the norm and the MUL: the first half cancels exactly to 0, the second
+    half is s + 0.25 = 1.25 - 42 * 2^-23 (exact).  So codes are 0 and 127, and
+    d = fl(v / 127).  Adding before the norm would give entirely different
+    codes."""
+    e5 = hand_examples["E5"]
+    s = np.uint32(int(e5["s_bits"], 16)).view(np.float32)
+    a = np.concatenate([np.full(16, -s, dtype=np.float32), np.full(16, 0.25, dtype=np.float32)])
+    xq, xd, xs = oracle.q8_quantize_rmsnorm_add(np.ones((1, 32), np.float32), np.ones(32, np.float32), a, 1e-5)
+    v = np.float32(1.25 - 42 * 2.0 ** -23)
+    assert np.float32(s) + np.float32(0.25) == v                  # the sum is exact
+    assert xq[0, :16].tolist() == [0] * 16 and xq[0, 16:].tolist() == [127] * 16
+    assert xd[0, 0] == np.float32(v) / np.float32(127.0) and xs[0, 0] == 16 * 127
+
+
+def test_norm_add_shared_addend_equals_repeated_rows():
+    K, B = 512, 3
+    x = workloads.activation(6, 1, 0, B, K)
+    g = workloads.norm_weight(6, 1, 0, K)
+    a = workloads.activation(6, 2, 0, 1, K)[0]
+    for u, w in zip(oracle.q8_quantize_rmsnorm_add(x, g, a, 1e-5),
+                    oracle.q8_quantize_rmsnorm_add(x, g, np.tile(a, (B, 1)), 1e-5)):
+        assert np.array_equal(u, w)
