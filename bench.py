@@ -459,6 +459,35 @@ def bench_prefill(args, dev):
     return out
 
 
+def bench_prologues(args, dev):
+    """The standalone activation prologues on Llama-3-8B-shaped rows
+    (K = 4096): RMS_NORM+MUL -> Q8 and RMS_NORM+MUL+ADD -> Q8 (one addend row
+    per input row), per launch.  Bytes: x (and the addend) read, g read once,
+    codes and scales written."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    K = 4096
+    out = {}
+    for B in (1, 8):
+        x = wl.activation_device(6, 0, 0, B, K, dev)
+        a = wl.activation_device(6, 1, 0, B, K, dev)
+        g = wl.norm_weight_device(6, 0, 0, K, dev)
+        xq = torch.empty((B, K), dtype=torch.int8, device=dev)
+        xd = torch.empty((B, K // 32), dtype=torch.float32, device=dev)
+        ms_n = per_launch_ms(lambda: q.q8_quantize_rmsnorm(x, g, wl.RMS_EPS, xq=xq, xd=xd), 20)
+        ms_a = per_launch_ms(lambda: q.q8_quantize_rmsnorm_add(x, g, a, wl.RMS_EPS, xq=xq, xd=xd), 20)
+        b_n = B * K * 4 + K * 4 + B * K * 9 // 8
+        b_a = b_n + B * K * 4
+        out[f"B={B}"] = {"rmsnorm_mul_q8": {"us": round(ms_n * 1e3, 2), "GB/s": round(b_n / (ms_n * 1e-3) / 1e9, 1)},
+                         "rmsnorm_mul_add_q8": {"us": round(ms_a * 1e3, 2),
+                                                "GB/s": round(b_a / (ms_a * 1e-3) / 1e9, 1)}}
+    out["note"] = "one workgroup per row: latency-bound (a few us), not bandwidth-bound"
+    return out
+
+
 def bench_moe(args, dev):
     """MUL_MAT_ID decode (64 experts, 16 tokens, top-8).  Gate and up share
     the routing and each token's row, so they are one stacked expert tensor
@@ -586,6 +615,8 @@ def main():
         print("[bench] prefill done", file=sys.stderr, flush=True)
         report["moe"] = bench_moe(args, dev)
         print("[bench] moe done", file=sys.stderr, flush=True)
+        report["prologues"] = bench_prologues(args, dev)
+        print("[bench] prologues done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         report["cpu_baseline"] = cpu_baseline(model, args.cpu_seconds)
     else:

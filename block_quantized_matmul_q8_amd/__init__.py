@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
     L.mul_mat_id_q4q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
     L.mul_mat_q4q8_rmsnorm.argtypes = [vp, vp, i64, i64, vp, vp, f32, u32, i64, vp, vp]
     L.moe_expert_sum_f32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    L.q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp, vp]
     L.q4q8_group_build.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int32, i64, vp, sz, vp, sz,
                                    ctypes.POINTER(GroupPlan)]
     L.mul_mat_q4q8_group.argtypes = [vp, ctypes.POINTER(GroupPlan), vp]
@@ -92,7 +93,7 @@ def lib() -> ctypes.CDLL:
     L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
                  "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
-                 "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32"):
+                 "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32", "q8_quantize_rmsnorm_add"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -169,6 +170,41 @@ def q8_quantize_rmsnorm(x, g, eps, flags=0, xq=None, xd=None, xs=None, want_xs=F
     _check("q8_quantize_rmsnorm",
            lib().q8_quantize_rmsnorm(_ptr(x), B, K, _ptr(g), ctypes.c_float(eps), flags, _ptr(xq), _ptr(xd),
                                      _ptr(xs), _stream(stream, x.device)))
+    return xq, xd, xs
+
+
+def q8_quantize_rmsnorm_add(x, g, a, eps, xq=None, xd=None, xs=None, want_xs=False, stream=None):
+    """RMS_NORM + MUL + ADD -> Q8: x f32 [B][K], g f32 [K], a f32 [K] (one
+    addend for every row) or [B][K] -> (xq i8 [B][K], xd f32 [B][K/32],
+    xs i32 [B][K/32] or None)."""
+    _need(x, "x", (torch.float32,), 2)
+    _need(g, "g", (torch.float32,), 1)
+    _need(a, "a", (torch.float32,))
+    B, K = x.shape
+    if tuple(a.shape) == (K,):
+        stride = 0
+    elif tuple(a.shape) == (B, K):
+        stride = K
+    else:
+        raise ValueError("a must be [K] or [B][K]")
+    for t, name in ((x, "x"), (g, "g"), (a, "a")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if xq is None:
+        xq = torch.empty((B, K), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((B, K // QK), dtype=torch.float32, device=x.device)
+    if xs is None and want_xs:
+        xs = torch.empty((B, K // QK), dtype=torch.int32, device=x.device)
+    _need(xq, "xq", (torch.int8,))
+    _need(xd, "xd", (torch.float32,))
+    if xs is not None:
+        _need(xs, "xs", (torch.int32,))
+    if xq.numel() != B * K or xd.numel() != B * (K // QK):
+        raise ValueError("xq / xd shape does not match x")
+    _check("q8_quantize_rmsnorm_add",
+           lib().q8_quantize_rmsnorm_add(_ptr(x), B, K, _ptr(g), _ptr(a), stride, ctypes.c_float(eps), _ptr(xq),
+                                         _ptr(xd), _ptr(xs), _stream(stream, x.device)))
     return xq, xd, xs
 
 

@@ -177,6 +177,27 @@ Q4Q8_EXPORT int q8_quantize_rmsnorm(const float* x, int64_t B, int64_t K, const 
                   "q8_quantize_rmsnorm");
 }
 
+Q4Q8_EXPORT int q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g, const float* a,
+                                        int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs,
+                                        void* stream) {
+  int st;
+  if ((st = check_k(K)) || (st = check_dims(1, B))) return st;
+  if (K > q4q8::kMaxPrologueK) return fail(Q4Q8_E_ARG, "K = %lld exceeds %d", (long long)K, q4q8::kMaxPrologueK);
+  if (a_row_stride != 0 && a_row_stride != K)
+    return fail(Q4Q8_E_ARG, "a_row_stride = %lld must be 0 or K", (long long)a_row_stride);
+  if (B == 0) return ok();
+  if (!x || !g || !a || !xq || !xd) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(a, 16) || !aligned(xq, 16) || !aligned(xd, 4) ||
+      (xs && !aligned(xs, 4)))
+    return fail(Q4Q8_E_ALIGN, "x, g, a, xq must be 16-byte aligned; xd, xs 4-byte");
+  if (!(eps >= 0.0f)) return fail(Q4Q8_E_ARG, "eps must be >= 0");
+  if ((st = check_device())) return st;
+  g_counts[3].fetch_add(1, std::memory_order_relaxed);
+  return launched(q4q8::launch_q8_rmsnorm(x, B, K, g, eps, false, xq, xd, xs, static_cast<hipStream_t>(stream), a,
+                                          a_row_stride),
+                  "q8_quantize_rmsnorm_add");
+}
+
 Q4Q8_EXPORT int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
                              const float* xd, int64_t B, float* y, void* stream) {
   return matmul_common(qs, d, M, K, xq, xd, B, y, nullptr, stream);

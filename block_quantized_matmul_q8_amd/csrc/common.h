@@ -170,9 +170,11 @@ Q4Q8_HIDDEN hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem
 // Launchers: enqueue on `s`, return the launch status.
 Q4Q8_HIDDEN hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
                                           uint16_t* d, hipStream_t s);
+// a: addend rows (RMS_NORM+MUL+ADD; row b at a + b * a_row_stride) or null.
 Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g,
                                          float eps, bool no_norm, int8_t* xq, float* xd,
-                                         int32_t* xs, hipStream_t s);
+                                         int32_t* xs, hipStream_t s, const float* a = nullptr,
+                                         int64_t a_row_stride = 0);
 Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B,
                                              int64_t max_k, hipStream_t s);
 // Tiles (128 weight rows x 128 tokens) of one product on the tiled route.

@@ -99,7 +99,8 @@ constexpr int kPrologueThreads = 256;
 
 __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
     const float* __restrict__ x, int K, const float* __restrict__ g, float eps, int no_norm,
-    int P, int8_t* __restrict__ xq, float* __restrict__ xd, int32_t* __restrict__ xs) {
+    int P, int8_t* __restrict__ xq, float* __restrict__ xd, int32_t* __restrict__ xs,
+    const float* __restrict__ a, int64_t a_row_stride) {
   extern __shared__ float red[];  // 2 * P floats (long rows only)
   __shared__ float s_slot;
   __shared__ float groups[8];
@@ -107,9 +108,10 @@ __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
   const int64_t row = blockIdx.x;
   const float* xr = x + row * (int64_t)K;
   const int tid = threadIdx.x;
+  const float* ar = a ? a + row * a_row_stride : nullptr;
   if (K <= kFastPrologueK) {
     wg_q8_row_fast(xr, g, K, eps, no_norm != 0, xq + row * (int64_t)K, xd + row * nb,
-                   xs ? xs + row * nb : nullptr, groups, tid);
+                   xs ? xs + row * nb : nullptr, groups, tid, ar);
     return;
   }
   const float s = no_norm ? 1.0f : wg_rms_scale(xr, K, eps, P, red, &s_slot, tid, kPrologueThreads);
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
     uint32_t packed[8];
     float dd;
     int sum;
-    q8_block_codes(xr, g, b, s, no_norm != 0, packed, dd, sum);
+    q8_block_codes(xr, g, b, s, no_norm != 0, packed, dd, sum, ar);
     uint4* dst = reinterpret_cast<uint4*>(xq + row * (int64_t)K + b * kQK);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -127,11 +129,12 @@ __global__ __launch_bounds__(kPrologueThreads) void rmsnorm_q8_kernel(
 }
 
 hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g, float eps,
-                             bool no_norm, int8_t* xq, float* xd, int32_t* xs, hipStream_t s) {
+                             bool no_norm, int8_t* xq, float* xd, int32_t* xs, hipStream_t s,
+                             const float* a, int64_t a_row_stride) {
   const int P = next_pow2_int((int)(K / kQK));
   const size_t lds = (no_norm || K <= kFastPrologueK) ? 0 : 2 * (size_t)P * sizeof(float);
   hipLaunchKernelGGL(rmsnorm_q8_kernel, dim3((unsigned)B), dim3(kPrologueThreads), lds, s, x,
-                     (int)K, g, eps, no_norm ? 1 : 0, P, xq, xd, xs);
+                     (int)K, g, eps, no_norm ? 1 : 0, P, xq, xd, xs, a, a_row_stride);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 //   pairwise, adjacent pairs, level by level (p[i] = p[2i] + p[2i+1]);
 //   s    = 1 / sqrt(ssq / K + eps);
 //   v_j  = (x_j * s) * g_j   (or v = x when the norm is skipped);
+//   with an addend row a (RMS_NORM+MUL+ADD): v_j = ((x_j * s) * g_j) + a_j;
 //   per 32-block: d = amax(|v|) / 127, id = 1 / d (0 if d == 0),
 //   q_j = roundf(v_j * id) (halves away from zero), clamped to [-127, 127].
 // The two roundings in v keep the fused RMS_NORM+MUL equal to the unfused
@@ -73,9 +74,10 @@ __device__ __forceinline__ float wg_rms_scale(const float* __restrict__ xr, int 
 
 // Q8 codes of block b of one row: packed[8] holds the 32 int8 codes in index
 // order (4 per dword, little-endian), d the fp32 scale, sum the code sum.
+// ar: the row's addend (RMS_NORM+MUL+ADD) or null.
 __device__ __forceinline__ void q8_block_codes(const float* __restrict__ xr, const float* __restrict__ g,
                                                int b, float s, bool no_norm, uint32_t (&packed)[8],
-                                               float& d, int& sum) {
+                                               float& d, int& sum, const float* __restrict__ ar = nullptr) {
   float v[kQK];
   load_block32(xr + b * kQK, v);
   if (!no_norm) {
@@ -83,6 +85,12 @@ __device__ __forceinline__ void q8_block_codes(const float* __restrict__ xr, con
     load_block32(g + b * kQK, gv);
 #pragma unroll
     for (int j = 0; j < kQK; ++j) v[j] = __fmul_rn(__fmul_rn(v[j], s), gv[j]);
+  }
+  if (ar) {
+    float av[kQK];
+    load_block32(ar + b * kQK, av);
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) v[j] = __fadd_rn(v[j], av[j]);
   }
   float amax = 0.0f;
 #pragma unroll
@@ -118,13 +126,14 @@ __device__ __forceinline__ void q8_block_codes(const float* __restrict__ xr, con
 //   - each thread quantises its blocks from the registers it holds.
 // Writes codes to sx [K] (int8), scales to sxd [nb] and, when sxs is not
 // null, code sums to sxs [nb] (LDS or global memory); `groups` is LDS scratch
-// of 8 floats.  Ends with a barrier.
+// of 8 floats; ar: the row's addend (RMS_NORM+MUL+ADD) or null.  Ends with a
+// barrier.
 constexpr int kFastPrologueK = 16384;
 
 __device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
                                                const float* __restrict__ g, int K, float eps,
                                                bool raw, int8_t* sx, float* sxd, int* sxs,
-                                               float* groups, int tid) {
+                                               float* groups, int tid, const float* __restrict__ ar = nullptr) {
   constexpr int kThreads = 256;
   const int nb = K / kQK;
   const int lane = tid & 63, wave = tid >> 6;
@@ -179,6 +188,12 @@ __device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
       float v[kQK];
 #pragma unroll
       for (int j = 0; j < kQK; ++j) v[j] = raw ? xv[h][j] : __fmul_rn(__fmul_rn(xv[h][j], s), gv[h][j]);
+      if (ar) {
+        float av[kQK];
+        load_block32(ar + b * kQK, av);
+#pragma unroll
+        for (int j = 0; j < kQK; ++j) v[j] = __fadd_rn(v[j], av[j]);
+      }
       float amax = 0.0f;
 #pragma unroll
       for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));

@@ -103,6 +103,22 @@ int q8_quantize_rmsnorm(const float* x, int64_t B, int64_t K, const float* g, fl
                         uint32_t flags, int8_t* xq, float* xd, int32_t* xs, void* stream);
 
 /*
+ * q8_quantize_rmsnorm_add -- activation prologue RMS_NORM + MUL + ADD + Q8.
+ * The Metal fusion page ("llama.cpp b10909：Metal后端融合表重构，修复约5% token
+ * 生成性能回退", its fusion-pattern counts) lists RMS_NORM+MUL+ADD beside
+ * RMS_NORM+MUL.  Per row: s as for q8_quantize_rmsnorm, then
+ *   v = ((x * s) * g) + a_row        (three fp32 roundings, in this order)
+ * and the same per-block Q8 quantisation; codes, scales and code sums are
+ * bit-exact results of those steps.
+ *   a  addend: a_row_stride == 0 -> one [K] row for every input row,
+ *      a_row_stride == K -> [B][K], row b at a + b * K; 16-byte aligned
+ *   other arguments as q8_quantize_rmsnorm (no flags: the norm is applied)
+ *   K <= 131072.
+ */
+int q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g, const float* a,
+                            int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs, void* stream);
+
+/*
  * mul_mat_q4q8 -- y = W x for M x K Q4 weights and B Q8 activation columns of
  * length K.  Route (section "CUDA：mmvq、mmq、cublas 三条矩阵路" of the GGML
  * backend page): small B takes the streaming matrix x vector kernel (the mmvq

@@ -25,6 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_id_q4q8", "moe_expert_sum_f32",
+              "q8_quantize_rmsnorm_add",
               "mul_mat_id_q4q8_workspace", "q4q8_last_error", "q4q8_set_path",
               "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_version"):
         assert n in names, n
@@ -118,6 +119,18 @@ def test_mul_mat_id_validation():
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, p, 16, 8, p, _v(260), ws, None) == q.Q4Q8_E_ALIGN
     # null ids
     assert L.mul_mat_id_q4q8(p, p, 64, 128, 256, p, p, 1, None, 16, 8, p, p, ws, None) == q.Q4Q8_E_ARG
+
+
+def test_q8_quantize_rmsnorm_add_validation():
+    L = q.lib()
+    p = _v(256)
+    eps = ctypes.c_float(1e-5)
+    assert L.q8_quantize_rmsnorm_add(p, 2, 48, p, p, 0, eps, p, p, None, None) == q.Q4Q8_E_ARG     # K % 32
+    assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, p, 32, eps, p, p, None, None) == q.Q4Q8_E_ARG    # stride
+    assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, None, 0, eps, p, p, None, None) == q.Q4Q8_E_ARG  # null a
+    assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, _v(264), 64, eps, p, p, None, None) == q.Q4Q8_E_ALIGN
+    assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, p, 0, ctypes.c_float(-1.0), p, p, None, None) == q.Q4Q8_E_ARG
+    assert L.q8_quantize_rmsnorm_add(None, 0, 64, None, None, 0, eps, None, None, None, None) == q.Q4Q8_OK
 
 
 def test_moe_expert_sum_validation():

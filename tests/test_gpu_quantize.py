@@ -2,6 +2,7 @@
 scales and code sums (Q4 weight planes; fused RMSNorm * g -> Q8 prologue)."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads
@@ -97,3 +98,22 @@ def test_prologue_empty_batch():
     g = torch.ones(64, dtype=torch.float32, device="cuda:0")
     xq, xd, _ = q.q8_quantize_rmsnorm(x, g, 1e-5)
     assert xq.shape == (0, 64) and xd.shape == (0, 2)
+
+
+@pytest.mark.parametrize("B,K", [(1, 32), (3, 2048), (8, 4096), (2, 8224), (2, 16384), (2, 16416), (1, 131072)])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_q8_rmsnorm_add_bit_exact(B, K, per_row):
+    """RMS_NORM + MUL + ADD -> Q8: codes, scales and code sums equal the
+    oracle bit for bit, for a shared [K] addend and one addend row per row,
+    in both the register form (K <= 16384) and the LDS-tree form."""
+    x = workloads.activation(50, 1, 0, B, K)
+    g = workloads.norm_weight(50, 1, 0, K)
+    a = workloads.activation(50, 2, 0, B, K)
+    if not per_row:
+        a = a[0].copy()
+    xq, xd, xs = q.q8_quantize_rmsnorm_add(to_dev(x), to_dev(g), to_dev(a), workloads.RMS_EPS, want_xs=True)
+    torch.cuda.synchronize()
+    oq, od, os_ = oracle.q8_quantize_rmsnorm_add(x, g, a, workloads.RMS_EPS)
+    assert np.array_equal(xq.cpu().numpy(), oq)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), od.view(np.uint32))
+    assert np.array_equal(xs.cpu().numpy(), os_)
