@@ -48,10 +48,14 @@ def _load():
     lib.orc_mul_mat_id.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, i32]
     lib.orc_moe_expert_sum.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.orc_q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp]
+    lib.orc_silu_array.argtypes = [vp, i64, vp]
+    lib.orc_exp_q_array.argtypes = [vp, i64, vp]
+    lib.orc_q8_quantize_swiglu.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
     for name in ("orc_f32_to_f16_array", "orc_f16_to_f32_array", "orc_q4_quantize",
                  "orc_q4_unpack_codes", "orc_rmsnorm", "orc_mul_rows", "orc_q8_quantize",
                  "orc_q8_quantize_rmsnorm", "orc_block_dots", "orc_mul_mat", "orc_mul_mat_mt",
-                 "orc_mul_mat_id", "orc_moe_expert_sum", "orc_q8_quantize_rmsnorm_add"):
+                 "orc_mul_mat_id", "orc_moe_expert_sum", "orc_q8_quantize_rmsnorm_add",
+                 "orc_silu_array", "orc_exp_q_array", "orc_q8_quantize_swiglu"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -170,6 +174,38 @@ def q8_quantize_rmsnorm_add(x, g, a, eps):
     xd = np.empty((B, K // 32), dtype=np.float32)
     xs = np.empty((B, K // 32), dtype=np.int32)
     _load().orc_q8_quantize_rmsnorm_add(_p(x), B, K, _p(g), _p(a), stride, float(eps), _p(xq), _p(xd), _p(xs))
+    return xq, xd, xs
+
+
+def exp_q(t):
+    """The fixed fp32 exponential of the SwiGLU prologue (see the header)."""
+    t = np.ascontiguousarray(np.asarray(t, dtype=np.float32))
+    out = np.empty_like(t)
+    _load().orc_exp_q_array(_p(t), t.size, _p(out))
+    return out
+
+
+def silu(g):
+    """silu(g) = g / (1 + exp_q(-g)), fp32, elementwise."""
+    g = np.ascontiguousarray(np.asarray(g, dtype=np.float32))
+    out = np.empty_like(g)
+    _load().orc_silu_array(_p(g), g.size, _p(out))
+    return out
+
+
+def q8_quantize_swiglu(gate, up):
+    """SwiGLU -> Q8: gate, up f32 [B][F] -> (xq i8 [B][F], xd f32 [B][F/32],
+    xs i32 [B][F/32]) of h = fl(silu(gate) * up)."""
+    gate = _c(gate, np.float32)
+    up = _c(up, np.float32)
+    if gate.shape != up.shape or gate.ndim != 2:
+        raise ValueError("shape mismatch")
+    B, F = gate.shape
+    _check_k(F)
+    xq = np.empty((B, F), dtype=np.int8)
+    xd = np.empty((B, F // 32), dtype=np.float32)
+    xs = np.empty((B, F // 32), dtype=np.int32)
+    _load().orc_q8_quantize_swiglu(_p(gate), _p(up), B, F, F, _p(xq), _p(xd), _p(xs))
     return xq, xd, xs
 
 

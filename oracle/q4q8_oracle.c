@@ -417,3 +417,63 @@ void orc_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k
             out[t * M + m] = acc;
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU -> Q8 (see the header for the fixed exponential).             */
+/* ------------------------------------------------------------------ */
+
+static float bits_to_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+float orc_exp_q(float t) {
+    if (t != t) return t;
+    if (t > 88.0f) return INFINITY;
+    if (t < -17.0f) return 0.0f;
+    const float l2e = bits_to_f32(0x3fb8aa3bu);
+    const float ln2_hi = bits_to_f32(0x3f317200u);
+    const float ln2_lo = bits_to_f32(0x35bfbe8eu);
+    /* C_k = fp32 nearest 1 / k!, k = 7 .. 2 */
+    const float c7 = bits_to_f32(0x39500d01u), c6 = bits_to_f32(0x3ab60b61u), c5 = bits_to_f32(0x3c088889u);
+    const float c4 = bits_to_f32(0x3d2aaaabu), c3 = bits_to_f32(0x3e2aaaabu), c2 = 0.5f;
+    const float nf = rintf(t * l2e);
+    const float hi = nf * ln2_hi;
+    const float lo = nf * ln2_lo;
+    const float r = (t - hi) - lo;
+    float c = c7;
+    c = c * r + c6;
+    c = c * r + c5;
+    c = c * r + c4;
+    c = c * r + c3;
+    c = c * r + c2;
+    c = c * r + 1.0f;
+    const float p = c * r + 1.0f;
+    const int n = (int)nf;
+    const float scale = bits_to_f32((uint32_t)(n + 127) << 23);
+    return p * scale;
+}
+
+float orc_silu(float g) {
+    const float e = orc_exp_q(-g);
+    return g / (1.0f + e);
+}
+
+void orc_silu_array(const float* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_silu(in[i]);
+}
+
+void orc_exp_q_array(const float* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_q(in[i]);
+}
+
+void orc_q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride,
+                            int8_t* xq, float* xd, int32_t* xs) {
+    float* h = (float*)malloc((size_t)(B * F) * sizeof(float));
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t k = 0; k < F; ++k)
+            h[b * F + k] = orc_silu(gate[b * row_stride + k]) * up[b * row_stride + k];
+    orc_q8_quantize(h, B, F, xq, xd, xs);
+    free(h);
+}

@@ -114,6 +114,30 @@ void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
 void orc_q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g, const float* a,
                                  int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs);
 
+/* SwiGLU -> Q8, the producer of the down projection's input.  The OpenVINO
+ * page ("llama.cpp b10981发布...") handles the GLU op swiglu (with clamp) and
+ * its f16 rounding drift; the op is silu(gate) * up.  Because the Q8 codes
+ * must be bit-exact, the exponential is fixed here as an fp32 algorithm
+ * (Cody-Waite argument reduction by ln 2 with a split constant, a degree-7
+ * Taylor polynomial in Horner form, exact scaling by 2^n; every step one
+ * fp32 rounding, no fused multiply-add):
+ *   exp_q(t): NaN -> NaN; t > 88 -> +inf; t < -17 -> 0 (then 1 + e == 1 in
+ *     fp32 anyway);  n = rint(fl(t * L2E)) (nearest even),
+ *     r = fl(fl(t - fl(n * LN2_HI)) - fl(n * LN2_LO)),
+ *     c = C7, then c = fl(fl(c * r) + C_k) for k = 6..1, p = fl(fl(c * r) + 1),
+ *     e = p * 2^n (exact: n in [-25, 127], the result stays normal);
+ *     L2E = 0x3fb8aa3b, LN2_HI = 0x3f317200 (8 trailing zero bits, so n * LN2_HI
+ *     is exact), LN2_LO = 0x35bfbe8e, C_k = fp32(1 / k!) (C1 = 1).
+ *   silu(g) = fl(g / fl(1 + exp_q(-g)));  h = fl(silu(gate) * up);
+ * then orc_q8_quantize of h.  Rows: gate + b * row_stride, up + b * row_stride
+ * (row_stride >= F; a stacked [B][2F] gate|up buffer uses row_stride = 2F). */
+float orc_exp_q(float t);
+float orc_silu(float g);
+void orc_silu_array(const float* in, int64_t n, float* out);
+void orc_exp_q_array(const float* in, int64_t n, float* out);
+void orc_q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride,
+                            int8_t* xq, float* xd, int32_t* xs);
+
 /* Sum of the expert planes of a MUL_MAT_ID result.  The page "llama.cpp
  * b10981发布：OpenVINO后端优化有状态解码与GPU MoE推理" describes the expert
  * planes being added by a chain of ADD ops (and a reordered reduction of that
