@@ -484,7 +484,17 @@ def bench_prologues(args, dev):
         out[f"B={B}"] = {"rmsnorm_mul_q8": {"us": round(ms_n * 1e3, 2), "GB/s": round(b_n / (ms_n * 1e-3) / 1e9, 1)},
                          "rmsnorm_mul_add_q8": {"us": round(ms_a * 1e3, 2),
                                                 "GB/s": round(b_a / (ms_a * 1e-3) / 1e9, 1)}}
-    out["note"] = "one workgroup per row: latency-bound (a few us), not bandwidth-bound"
+    # SwiGLU -> Q8 from a stacked gate|up buffer: the MoE down projection's
+    # 16 x 8 slot rows of 1408, and one Llama-3-8B decode row of 14336
+    for name, rows, F in (("swiglu_q8 moe 128x1408", 128, 1408), ("swiglu_q8 8b 1x14336", 1, 14336)):
+        buf = wl.activation_device(7, 0, 0, rows, 2 * F, dev)
+        xq = torch.empty((rows, F), dtype=torch.int8, device=dev)
+        xd = torch.empty((rows, F // 32), dtype=torch.float32, device=dev)
+        ms = per_launch_ms(lambda: q.q8_quantize_swiglu(buf[:, :F], buf[:, F:], xq=xq, xd=xd), 20)
+        nbytes = rows * F * 8 + rows * F * 9 // 8
+        out[name] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    out["note"] = ("norm prologues: one workgroup per row, latency-bound (a few us); "
+                   "swiglu_q8: one thread per 32-block, no row reduction")
     return out
 
 

@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
     L.mul_mat_q4q8_rmsnorm.argtypes = [vp, vp, i64, i64, vp, vp, f32, u32, i64, vp, vp]
     L.moe_expert_sum_f32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp, vp]
+    L.q8_quantize_swiglu.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
     L.q4q8_group_build.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int32, i64, vp, sz, vp, sz,
                                    ctypes.POINTER(GroupPlan)]
     L.mul_mat_q4q8_group.argtypes = [vp, ctypes.POINTER(GroupPlan), vp]
@@ -93,7 +94,8 @@ def lib() -> ctypes.CDLL:
     L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
                  "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
-                 "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32", "q8_quantize_rmsnorm_add"):
+                 "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32", "q8_quantize_rmsnorm_add",
+                 "q8_quantize_swiglu"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -116,7 +118,7 @@ def _stream(stream, device):
     return ctypes.c_void_p(int(stream))
 
 
-def _need(t, name, dtypes, ndim=None):
+def _need(t, name, dtypes, ndim=None, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if t.device.type != "cuda":
@@ -125,7 +127,7 @@ def _need(t, name, dtypes, ndim=None):
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
@@ -205,6 +207,36 @@ def q8_quantize_rmsnorm_add(x, g, a, eps, xq=None, xd=None, xs=None, want_xs=Fal
     _check("q8_quantize_rmsnorm_add",
            lib().q8_quantize_rmsnorm_add(_ptr(x), B, K, _ptr(g), _ptr(a), stride, ctypes.c_float(eps), _ptr(xq),
                                          _ptr(xd), _ptr(xs), _stream(stream, x.device)))
+    return xq, xd, xs
+
+
+def q8_quantize_swiglu(gate, up, xq=None, xd=None, xs=None, want_xs=False, stream=None):
+    """SwiGLU -> Q8: gate, up f32 [B][F] views with unit element stride and the
+    same row stride (e.g. the two halves of a stacked [B][2F] gate|up buffer)
+    -> (xq i8 [B][F], xd f32 [B][F/32], xs i32 [B][F/32] or None)."""
+    _need(gate, "gate", (torch.float32,), 2, contiguous=False)
+    _need(up, "up", (torch.float32,), 2, contiguous=False)
+    if tuple(gate.shape) != tuple(up.shape):
+        raise ValueError("gate and up shapes differ")
+    B, F = gate.shape
+    if gate.stride(1) != 1 or up.stride(1) != 1 or (B > 1 and gate.stride(0) != up.stride(0)):
+        raise ValueError("gate and up need unit element stride and one common row stride")
+    row_stride = gate.stride(0) if B > 1 else F
+    if xq is None:
+        xq = torch.empty((B, F), dtype=torch.int8, device=gate.device)
+    if xd is None:
+        xd = torch.empty((B, F // QK), dtype=torch.float32, device=gate.device)
+    if xs is None and want_xs:
+        xs = torch.empty((B, F // QK), dtype=torch.int32, device=gate.device)
+    _need(xq, "xq", (torch.int8,))
+    _need(xd, "xd", (torch.float32,))
+    if xs is not None:
+        _need(xs, "xs", (torch.int32,))
+    if xq.numel() != B * F or xd.numel() != B * (F // QK):
+        raise ValueError("xq / xd shape does not match gate")
+    _check("q8_quantize_swiglu",
+           lib().q8_quantize_swiglu(_ptr(gate), _ptr(up), B, F, row_stride, _ptr(xq), _ptr(xd), _ptr(xs),
+                                    _stream(stream, gate.device)))
     return xq, xd, xs
 
 

@@ -198,6 +198,23 @@ Q4Q8_EXPORT int q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, co
                   "q8_quantize_rmsnorm_add");
 }
 
+Q4Q8_EXPORT int q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride,
+                                   int8_t* xq, float* xd, int32_t* xs, void* stream) {
+  int st;
+  if ((st = check_k(F)) || (st = check_dims(1, B))) return st;
+  if (row_stride < F || row_stride % 4)
+    return fail(Q4Q8_E_ARG, "row_stride = %lld must be >= F and a multiple of 4", (long long)row_stride);
+  if (B * (F / 32) > (int64_t)INT32_MAX * 64) return fail(Q4Q8_E_ARG, "B * F too large");
+  if (B == 0) return ok();
+  if (!gate || !up || !xq || !xd) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(xq, 16) || !aligned(xd, 4) || (xs && !aligned(xs, 4)))
+    return fail(Q4Q8_E_ALIGN, "gate, up, xq must be 16-byte aligned; xd, xs 4-byte");
+  if ((st = check_device())) return st;
+  g_counts[3].fetch_add(1, std::memory_order_relaxed);
+  return launched(q4q8::launch_swiglu_q8(gate, up, B, F, row_stride, xq, xd, xs, static_cast<hipStream_t>(stream)),
+                  "q8_quantize_swiglu");
+}
+
 Q4Q8_EXPORT int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
                              const float* xd, int64_t B, float* y, void* stream) {
   return matmul_common(qs, d, M, K, xq, xd, B, y, nullptr, stream);

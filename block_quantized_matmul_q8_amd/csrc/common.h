@@ -175,6 +175,8 @@ Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, c
                                          float eps, bool no_norm, int8_t* xq, float* xd,
                                          int32_t* xs, hipStream_t s, const float* a = nullptr,
                                          int64_t a_row_stride = 0);
+Q4Q8_HIDDEN hipError_t launch_swiglu_q8(const float* gate, const float* up, int64_t B, int64_t F,
+                                        int64_t row_stride, int8_t* xq, float* xd, int32_t* xs, hipStream_t s);
 Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B,
                                              int64_t max_k, hipStream_t s);
 // Tiles (128 weight rows x 128 tokens) of one product on the tiled route.

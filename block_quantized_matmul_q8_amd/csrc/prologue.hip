@@ -138,6 +138,42 @@ hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* 
   return hipGetLastError();
 }
 
+// SwiGLU -> Q8 (the producer of the down projection's input): one thread
+// per (row, 32-block); h = fl(silu(gate) * up), then the Q8 block rule.
+// Rows of gate and up start row_stride floats apart (a stacked [B][2F]
+// gate|up buffer: gate = buffer, up = buffer + F, row_stride = 2F).
+__global__ __launch_bounds__(256) void swiglu_q8_kernel(const float* __restrict__ gate,
+                                                        const float* __restrict__ up, int64_t B, int64_t F,
+                                                        int64_t row_stride, int8_t* __restrict__ xq,
+                                                        float* __restrict__ xd, int32_t* __restrict__ xs) {
+  const int64_t nb = F / kQK;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * nb) return;
+  const int64_t row = idx / nb, b = idx - row * nb;
+  float gv[kQK], uv[kQK], v[kQK];
+  load_block32(gate + row * row_stride + b * kQK, gv);
+  load_block32(up + row * row_stride + b * kQK, uv);
+#pragma unroll
+  for (int j = 0; j < kQK; ++j) v[j] = __fmul_rn(silu_q(gv[j]), uv[j]);
+  uint32_t packed[8];
+  float d;
+  int sum;
+  q8_pack_block(v, packed, d, sum);
+  u32x4* dst = reinterpret_cast<u32x4*>(xq + row * F + b * kQK);
+  gptr_w(dst)[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  gptr_w(dst)[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+  gptr_w(xd)[row * nb + b] = d;
+  if (xs) gptr_w(xs)[row * nb + b] = sum;
+}
+
+hipError_t launch_swiglu_q8(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride,
+                            int8_t* xq, float* xd, int32_t* xs, hipStream_t s) {
+  const int64_t n = B * (F / kQK);
+  hipLaunchKernelGGL(swiglu_q8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gate, up, B, F,
+                     row_stride, xq, xd, xs);
+  return hipGetLastError();
+}
+
 // Prologue pass of a grouped launch: workgroup (j, c) quantises row c of the
 // fp32 input of job j into the job's Q8 planes, in the register form for
 // rows of up to 16384 elements and the LDS-tree form beyond (dynamic LDS of

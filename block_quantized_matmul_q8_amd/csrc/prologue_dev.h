@@ -72,6 +72,30 @@ __device__ __forceinline__ float wg_rms_scale(const float* __restrict__ xr, int 
   return *s_slot;
 }
 
+// The Q8 block rule on 32 values: d = amax(|v|) / 127, id = 1 / d (0 for an
+// all-zero block), q = roundf(v * id) clamped to [-127, 127].  packed[8]
+// holds the codes in index order (4 per dword, little-endian), sum their sum.
+__device__ __forceinline__ void q8_pack_block(const float (&v)[kQK], uint32_t (&packed)[8], float& d, int& sum) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  d = __fdiv_rn(amax, 127.0f);
+  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
+      qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+      sum += qi;
+      word |= ((uint32_t)qi & 0xFFu) << (8 * k);
+    }
+    packed[i] = word;
+  }
+}
+
 // Q8 codes of block b of one row: packed[8] holds the 32 int8 codes in index
 // order (4 per dword, little-endian), d the fp32 scale, sum the code sum.
 // ar: the row's addend (RMS_NORM+MUL+ADD) or null.
@@ -92,25 +116,40 @@ __device__ __forceinline__ void q8_block_codes(const float* __restrict__ xr, con
 #pragma unroll
     for (int j = 0; j < kQK; ++j) v[j] = __fadd_rn(v[j], av[j]);
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  d = __fdiv_rn(amax, 127.0f);
-  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
-  sum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
-      qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-      sum += qi;
-      word |= ((uint32_t)qi & 0xFFu) << (8 * k);
-    }
-    packed[i] = word;
-  }
+  q8_pack_block(v, packed, d, sum);
 }
+
+// SwiGLU producer: a fixed fp32 exponential, so that the Q8 codes of
+// silu(gate) * up are reproducible bit for bit.  W. J. Cody and W. Waite's
+// argument reduction (t = n ln2 + r, ln2 split into a high part with 8
+// trailing zero bits, so n * ln2_hi is exact), exp(r) by its degree-7 Taylor
+// polynomial in Horner form (coefficients the fp32 values nearest 1/k!), and
+// exact scaling by 2^n.  Every step is one fp32 rounding; no fused
+// multiply-add.  Domain [-17, 88]: below it 1 + exp(t) == 1 in fp32 anyway
+// (0 is returned), above it +inf.  Maximal error about 1.2 ulp.
+__device__ __forceinline__ float exp_q(float t) {
+  if (t != t) return t;
+  if (t > 88.0f) return __builtin_inff();
+  if (t < -17.0f) return 0.0f;
+  const float l2e = __builtin_bit_cast(float, 0x3fb8aa3bu);
+  const float ln2_hi = __builtin_bit_cast(float, 0x3f317200u);
+  const float ln2_lo = __builtin_bit_cast(float, 0x35bfbe8eu);
+  const float nf = rintf(__fmul_rn(t, l2e));
+  const float r = __fadd_rn(__fadd_rn(t, -__fmul_rn(nf, ln2_hi)), -__fmul_rn(nf, ln2_lo));
+  float c = __builtin_bit_cast(float, 0x39500d01u);                       // 1/7!
+  c = __fadd_rn(__fmul_rn(c, r), __builtin_bit_cast(float, 0x3ab60b61u));  // 1/6!
+  c = __fadd_rn(__fmul_rn(c, r), __builtin_bit_cast(float, 0x3c088889u));  // 1/5!
+  c = __fadd_rn(__fmul_rn(c, r), __builtin_bit_cast(float, 0x3d2aaaabu));  // 1/4!
+  c = __fadd_rn(__fmul_rn(c, r), __builtin_bit_cast(float, 0x3e2aaaabu));  // 1/3!
+  c = __fadd_rn(__fmul_rn(c, r), 0.5f);
+  c = __fadd_rn(__fmul_rn(c, r), 1.0f);
+  const float p = __fadd_rn(__fmul_rn(c, r), 1.0f);
+  const float scale = __builtin_bit_cast(float, (uint32_t)((int)nf + 127) << 23);
+  return __fmul_rn(p, scale);
+}
+
+// silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float silu_q(float g) { return __fdiv_rn(g, __fadd_rn(1.0f, exp_q(-g))); }
 
 // The same prologue for one row, latency-optimised for a workgroup that
 // folds it into a product kernel (K <= 16384, i.e. at most 2 blocks per
@@ -194,25 +233,10 @@ __device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
 #pragma unroll
         for (int j = 0; j < kQK; ++j) v[j] = __fadd_rn(v[j], av[j]);
       }
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      const float d = __fdiv_rn(amax, 127.0f);
-      const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
-      int sum = 0;
+      float d;
+      int sum;
       uint32_t packed[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
-          qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-          sum += qi;
-          word |= ((uint32_t)qi & 0xFFu) << (8 * k);
-        }
-        packed[i] = word;
-      }
+      q8_pack_block(v, packed, d, sum);
       u32x4* dst = reinterpret_cast<u32x4*>(sx + (size_t)b * kQK);
       dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
       dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};

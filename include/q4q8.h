@@ -119,6 +119,24 @@ int q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g
                             int64_t a_row_stride, float eps, int8_t* xq, float* xd, int32_t* xs, void* stream);
 
 /*
+ * q8_quantize_swiglu -- SwiGLU -> Q8, the producer of the down projection's
+ * input.  The OpenVINO page ("llama.cpp b10981发布：OpenVINO后端优化有状态解码
+ * 与GPU MoE推理") handles the GLU op swiglu and its rounding drift; the op is
+ * silu(gate) * up.  Per element h = fl(silu(gate) * up) with
+ * silu(g) = fl(g / fl(1 + exp_q(-g))), exp_q a fixed fp32 algorithm (Cody-Waite
+ * reduction by ln 2, degree-7 Taylor polynomial, exact 2^n scaling; domain
+ * [-17, 88], 0 below, +inf above; about 1.2 ulp), so that the Q8 codes, scales
+ * and code sums of h (the q8_quantize_rmsnorm block rule) are bit-exact.
+ *   gate, up  rows of F f32, row b at gate + b * row_stride and up + b * row_stride
+ *             (a stacked [B][2F] gate|up buffer: up = gate + F, row_stride = 2F);
+ *             16-byte aligned, row_stride >= F and a multiple of 4
+ *   xq [B][F] i8 (16-byte aligned), xd [B][F/32] f32, xs [B][F/32] i32 or NULL
+ * Outputs must not overlap the inputs.  Non-finite inputs give unspecified codes.
+ */
+int q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride, int8_t* xq,
+                       float* xd, int32_t* xs, void* stream);
+
+/*
  * mul_mat_q4q8 -- y = W x for M x K Q4 weights and B Q8 activation columns of
  * length K.  Route (section "CUDA：mmvq、mmq、cublas 三条矩阵路" of the GGML
  * backend page): small B takes the streaming matrix x vector kernel (the mmvq

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_id_q4q8", "moe_expert_sum_f32",
-              "q8_quantize_rmsnorm_add",
+              "q8_quantize_rmsnorm_add", "q8_quantize_swiglu",
               "mul_mat_id_q4q8_workspace", "q4q8_last_error", "q4q8_set_path",
               "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_version"):
         assert n in names, n
@@ -131,6 +131,17 @@ def test_q8_quantize_rmsnorm_add_validation():
     assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, _v(264), 64, eps, p, p, None, None) == q.Q4Q8_E_ALIGN
     assert L.q8_quantize_rmsnorm_add(p, 2, 64, p, p, 0, ctypes.c_float(-1.0), p, p, None, None) == q.Q4Q8_E_ARG
     assert L.q8_quantize_rmsnorm_add(None, 0, 64, None, None, 0, eps, None, None, None, None) == q.Q4Q8_OK
+
+
+def test_q8_quantize_swiglu_validation():
+    L = q.lib()
+    p = _v(256)
+    assert L.q8_quantize_swiglu(p, p, 2, 48, 48, p, p, None, None) == q.Q4Q8_E_ARG        # F % 32
+    assert L.q8_quantize_swiglu(p, p, 2, 64, 32, p, p, None, None) == q.Q4Q8_E_ARG        # stride < F
+    assert L.q8_quantize_swiglu(p, p, 2, 64, 66, p, p, None, None) == q.Q4Q8_E_ARG        # stride % 4
+    assert L.q8_quantize_swiglu(p, None, 2, 64, 64, p, p, None, None) == q.Q4Q8_E_ARG
+    assert L.q8_quantize_swiglu(p, _v(264), 2, 64, 128, p, p, None, None) == q.Q4Q8_E_ALIGN
+    assert L.q8_quantize_swiglu(None, None, 0, 64, 64, None, None, None, None) == q.Q4Q8_OK
 
 
 def test_moe_expert_sum_validation():

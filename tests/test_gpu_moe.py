@@ -174,3 +174,44 @@ def test_expert_sum_of_routed_down_projection():
     assert np.all(np.isnan(out[5])) and np.all(np.isnan(out_o[5]))
     keep = [t for t in range(cfg.T) if t != 5]
     assert_close(out[keep], out_o[keep], "expert sum of the down projection")
+
+
+def test_moe_chain_gate_up_swiglu_down_sum():
+    """A whole routed FFN on the MoE shape: stacked gate/up routed product ->
+    SwiGLU -> Q8 of every (token, slot) row -> routed down product -> weighted
+    expert sum.  Each GPU stage is checked against the oracle stage applied to
+    the GPU's own input (codes bit-exact, fp32 outputs within tolerance), and
+    the end result against the oracle chain."""
+    cfg = workloads.MOE
+    ids = workloads.expert_ids(1, cfg.T, cfg.E, cfg.top_k)
+    w = workloads.expert_weights(1, cfg.T, cfg.top_k)
+    _, qs_gu, d_gu = _experts(4, cfg.E, 2 * cfg.ffn, cfg.hidden)
+    _, qs_dn, d_dn = _experts(5, cfg.E, cfg.hidden, cfg.ffn)
+    xq, xd = _acts(4, cfg.T, 1, cfg.hidden)
+    y_gu = q.mul_mat_id_q4q8(to_dev(qs_gu), to_dev(d_gu.view(np.int16)), to_dev(xq), to_dev(xd), to_dev(ids))
+    rows = y_gu.view(cfg.T * cfg.top_k, 2 * cfg.ffn)
+    hq, hd, _ = q.q8_quantize_swiglu(rows[:, :cfg.ffn], rows[:, cfg.ffn:])
+    y_dn = q.mul_mat_id_q4q8(to_dev(qs_dn), to_dev(d_dn.view(np.int16)), hq.view(cfg.T, cfg.top_k, cfg.ffn),
+                             hd.view(cfg.T, cfg.top_k, cfg.ffn // 32), to_dev(ids))
+    out = q.moe_expert_sum_f32(y_dn, to_dev(w))
+    torch.cuda.synchronize()
+    y_gu_h = y_gu.cpu().numpy()
+    # SwiGLU codes bit-exact on the GPU's own gate/up planes
+    g_h = y_gu_h[:, :, :cfg.ffn].reshape(-1, cfg.ffn).copy()
+    u_h = y_gu_h[:, :, cfg.ffn:].reshape(-1, cfg.ffn).copy()
+    oq, od, _ = oracle.q8_quantize_swiglu(g_h, u_h)
+    assert np.array_equal(hq.cpu().numpy(), oq) and np.array_equal(hd.cpu().numpy(), od)
+    # the end-to-end chain against the oracle chain
+    y_gu_o = oracle.mul_mat_id(qs_gu, d_gu, xq, xd, ids, nthreads=16)
+    assert_close(y_gu_h, y_gu_o, "gate/up")
+    g_o = y_gu_o[:, :, :cfg.ffn].reshape(-1, cfg.ffn).copy()
+    u_o = y_gu_o[:, :, cfg.ffn:].reshape(-1, cfg.ffn).copy()
+    hq_o, hd_o, _ = oracle.q8_quantize_swiglu(g_o, u_o)
+    y_dn_o = oracle.mul_mat_id(qs_dn, d_dn, hq_o.reshape(cfg.T, cfg.top_k, cfg.ffn),
+                               hd_o.reshape(cfg.T, cfg.top_k, cfg.ffn // 32), ids, nthreads=16)
+    out_o = oracle.moe_expert_sum(y_dn_o, w)
+    # the GPU's gate/up differ from the oracle's by fp32 summation order, which
+    # can move a Q8 code by one step; the end result is compared normwise with
+    # the quantisation-level tolerance of one extra Q8 rounding (2^-8 relative)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - out_o).max() / np.abs(out_o).max()
+    assert err < 2e-3, err

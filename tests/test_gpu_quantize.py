@@ -117,3 +117,31 @@ def test_q8_rmsnorm_add_bit_exact(B, K, per_row):
     assert np.array_equal(xq.cpu().numpy(), oq)
     assert np.array_equal(xd.cpu().numpy().view(np.uint32), od.view(np.uint32))
     assert np.array_equal(xs.cpu().numpy(), os_)
+
+
+def _swiglu_inputs(seed, B, F):
+    # gates spread over silu's whole range: both clamps of the exponential,
+    # the saturated region and small values
+    gate = (workloads.activation(seed, 3, 0, B, F) * np.float32(12.0)).astype(np.float32)
+    gate[0, :8] = [0.0, -0.0, 17.0, -17.0, 88.0, -88.0, 200.0, -200.0]
+    up = workloads.activation(seed, 4, 0, B, F)
+    return gate, up
+
+
+@pytest.mark.parametrize("B,F", [(1, 32), (8, 1408), (3, 2048), (1, 14336), (128, 1408)])
+@pytest.mark.parametrize("stacked", [False, True])
+def test_q8_swiglu_bit_exact(B, F, stacked):
+    """SwiGLU -> Q8: codes, scales and code sums equal the oracle bit for bit,
+    from separate gate / up planes and from one stacked [B][2F] buffer."""
+    gate, up = _swiglu_inputs(60, B, F)
+    if stacked:
+        buf = to_dev(np.concatenate([gate, up], axis=1))
+        g_dev, u_dev = buf[:, :F], buf[:, F:]
+    else:
+        g_dev, u_dev = to_dev(gate), to_dev(up)
+    xq, xd, xs = q.q8_quantize_swiglu(g_dev, u_dev, want_xs=True)
+    torch.cuda.synchronize()
+    oq, od, os_ = oracle.q8_quantize_swiglu(gate, up)
+    assert np.array_equal(xq.cpu().numpy(), oq)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), od.view(np.uint32))
+    assert np.array_equal(xs.cpu().numpy(), os_)
