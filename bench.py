@@ -29,6 +29,8 @@ Also reported in the same JSON line (not part of value):
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-extras]
        python bench.py --kernel-only 10      (launches for rocprofv3 runs)
+       python bench.py --gemm-only 10        (prefill GEMM launches for rocprofv3 runs)
+       python bench.py --moe-only 10         (routed MoE launches for rocprofv3 runs)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (traffic summary)
 """
 from __future__ import annotations
@@ -337,6 +339,69 @@ def kernel_only(n, dev):
           flush=True)
 
 
+def gemm_only(n, dev):
+    """Launch sequence for profiler runs of the prefill GEMM: the Llama-3-8B
+    layer's seven products as one grouped tiled launch over Q8 planes of
+    T = 2048 tokens, n times."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    T = 2048
+    layer = wl.LLAMA_3_8B
+    probs = []
+    planes = {}
+    for slot, K in wl.slot_k(layer).items():
+        x = wl.activation_device(2, 0, slot, T, K, dev)
+        g = wl.norm_weight_device(2, 0, slot, K, dev)
+        planes[slot] = q.q8_quantize_rmsnorm(x, g, 1e-5)[:2]
+    for mi, m in enumerate(layer):
+        w = wl.weight_device(2, 0, mi, m.M, m.K, dev)
+        qs, d = q.q4_quantize(w)
+        del w
+        y = torch.empty((T, m.M), dtype=torch.float32, device=dev)
+        probs.append({"qs": qs, "d": d, "y": y, "xq": planes[m.slot][0], "xd": planes[m.slot][1]})
+    gemm = q.Group(probs, B=T)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        gemm()
+    torch.cuda.synchronize()
+    ops = 2 * T * sum(m.M * m.K for m in layer)
+    print(f"[gemm-only] {n} grouped prefill launches, T={T}, {ops} int8 ops each", flush=True)
+
+
+def moe_only(n, dev):
+    """Launch sequence for profiler runs of the routed MoE step (stacked
+    gate/up and down routed calls on the 64-expert, 16-token, top-8 shape),
+    n times."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    cfg = wl.MOE
+    ids = torch.from_numpy(wl.expert_ids(0, cfg.T, cfg.E, cfg.top_k)).to(dev)
+    calls = []
+    for i, (M, K, S) in enumerate(((2 * cfg.ffn, cfg.hidden, 1), (cfg.hidden, cfg.ffn, cfg.top_k))):
+        w = wl.weight_device(3, 0, i, cfg.E * M, K, dev)
+        qs, d = q.q4_quantize(w)
+        del w
+        x = wl.activation_device(3, 0, i, cfg.T * S, K, dev)
+        g = wl.norm_weight_device(3, 0, i, K, dev)
+        xq, xd, _ = q.q8_quantize_rmsnorm(x, g, 1e-5)
+        y = torch.empty((cfg.T, cfg.top_k, M), dtype=torch.float32, device=dev)
+        ws = torch.empty(q.mul_mat_id_q4q8_workspace(cfg.E, cfg.T, cfg.top_k), dtype=torch.uint8, device=dev)
+        calls.append((qs.view(cfg.E, M, K // 2), d.view(cfg.E, M, K // 32), xq.view(cfg.T, S, K),
+                      xd.view(cfg.T, S, K // 32), y, ws))
+    torch.cuda.synchronize()
+    for _ in range(n):
+        for qs, d, xq, xd, y, ws in calls:
+            q.mul_mat_id_q4q8(qs, d, xq, xd, ids, y=y, ws=ws)
+    torch.cuda.synchronize()
+    print(f"[moe-only] {n} MoE steps (2 routed calls each)", flush=True)
+
+
 def pmc_summary(fetch_dir, write_dir):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the streaming kernel,
     scaled by what the same counters read for the 256 MiB copy."""
@@ -588,6 +653,10 @@ def main():
     ap.add_argument("--skip-extras", action="store_true", help="only the headline step and its roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--gemm-only", type=int, default=0, metavar="N",
+                    help="launch N grouped prefill GEMMs (T=2048, Llama-3-8B layer) and exit")
+    ap.add_argument("--moe-only", type=int, default=0, metavar="N",
+                    help="launch N routed MoE steps and exit")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="launch N steps and N streaming passes (after a calibration copy) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -614,6 +683,12 @@ def main():
 
     if args.kernel_only:
         kernel_only(args.kernel_only, dev)
+        return
+    if args.gemm_only:
+        gemm_only(args.gemm_only, dev)
+        return
+    if args.moe_only:
+        moe_only(args.moe_only, dev)
         return
     report = {}
     model = bench_decode_1b(args, dev, report)
