@@ -48,6 +48,9 @@ def _load():
     lib.orc_mul_mat_id.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, i32]
     lib.orc_moe_expert_sum.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.orc_q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp]
+    lib.orc_q8w_quantize.argtypes = [vp, i64, i64, vp, vp]
+    lib.orc_block_dots_q8w.argtypes = [vp, i64, i64, vp, i64, vp]
+    lib.orc_mul_mat_q8w_mt.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, i32]
     lib.orc_silu_array.argtypes = [vp, i64, vp]
     lib.orc_exp_q_array.argtypes = [vp, i64, vp]
     lib.orc_q8_quantize_swiglu.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
@@ -55,7 +58,8 @@ def _load():
                  "orc_q4_unpack_codes", "orc_rmsnorm", "orc_mul_rows", "orc_q8_quantize",
                  "orc_q8_quantize_rmsnorm", "orc_block_dots", "orc_mul_mat", "orc_mul_mat_mt",
                  "orc_mul_mat_id", "orc_moe_expert_sum", "orc_q8_quantize_rmsnorm_add",
-                 "orc_silu_array", "orc_exp_q_array", "orc_q8_quantize_swiglu"):
+                 "orc_silu_array", "orc_exp_q_array", "orc_q8_quantize_swiglu", "orc_q8w_quantize",
+                 "orc_block_dots_q8w", "orc_mul_mat_q8w_mt"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -279,6 +283,51 @@ def moe_expert_sum(y, w=None):
     out = np.empty((T, M), dtype=np.float32)
     _load().orc_moe_expert_sum(_p(y), _p(w), T, top_k, M, _p(out))
     return out
+
+
+def q8w_quantize(w):
+    """Q8_0 weights: w f32 [M][K] -> (qw i8 [M][K], d u16 [M][K/32])."""
+    w = _c(w, np.float32)
+    M, K = w.shape
+    _check_k(K)
+    qw = np.empty((M, K), dtype=np.int8)
+    d = np.empty((M, K // 32), dtype=np.uint16)
+    _load().orc_q8w_quantize(_p(w), M, K, _p(qw), _p(d))
+    return qw, d
+
+
+def block_dots_q8w(qw, xq):
+    """Exact block sums sum_j qw_j x_j: int32 [B][M][K/32]."""
+    qw = _c(qw, np.int8)
+    xq = _c(xq, np.int8)
+    M, K = qw.shape
+    B = xq.shape[0]
+    _check_k(K)
+    I = np.empty((B, M, K // 32), dtype=np.int32)
+    _load().orc_block_dots_q8w(_p(qw), M, K, _p(xq), B, _p(I))
+    return I
+
+
+def mul_mat_q8w(qw, d, xq, xd, nthreads=1, want_y64=True):
+    """Q8_0 W [M][K] times Q8 x [B][K] -> (y f32 [B][M], y64 f64 [B][M] or None)."""
+    qw = _c(qw, np.int8)
+    d = _c(d, np.uint16)
+    xq = _c(xq, np.int8)
+    xd = _c(xd, np.float32)
+    M, K = qw.shape
+    B = xq.shape[0]
+    _check_k(K)
+    if d.shape != (M, K // 32) or xq.shape != (B, K) or xd.shape != (B, K // 32):
+        raise ValueError("shape mismatch")
+    y = np.empty((B, M), dtype=np.float32)
+    y64 = np.empty((B, M), dtype=np.float64) if want_y64 else None
+    _load().orc_mul_mat_q8w_mt(_p(qw), _p(d), M, K, _p(xq), _p(xd), B, _p(y), _p(y64), int(nthreads))
+    return y, y64
+
+
+def dequantize_q8w(qw, d):
+    """fp64 dequantised Q8_0 weights (q * f32(d)) [M][K] (exact in fp64)."""
+    return qw.astype(np.float64) * np.repeat(f16_bits_to_f32(d).astype(np.float64), 32, axis=1)
 
 
 def dequantize_q4(qs, d, K):

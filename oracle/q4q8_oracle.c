@@ -477,3 +477,96 @@ void orc_q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64
     orc_q8_quantize(h, B, F, xq, xd, xs);
     free(h);
 }
+
+/* ------------------------------------------------------------------ */
+/* Q8_0 weights (see the header).                                      */
+/* ------------------------------------------------------------------ */
+
+void orc_q8w_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d) {
+    const int64_t nb = K / QK;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* v = w + m * K + b * QK;
+            float amax = 0.0f;
+            for (int j = 0; j < QK; ++j) {
+                const float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            const float dd = amax / 127.0f;
+            const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+            for (int j = 0; j < QK; ++j) {
+                long qi = lroundf(v[j] * id);
+                if (qi > 127) qi = 127;
+                if (qi < -127) qi = -127;
+                qw[m * K + b * QK + j] = (int8_t)qi;
+            }
+            d[m * nb + b] = orc_f32_to_f16(dd);
+        }
+}
+
+static int32_t block_dot_q8w(const int8_t* w32, const int8_t* x32) {
+    int32_t sum = 0;
+    for (int j = 0; j < QK; ++j) sum += (int32_t)w32[j] * (int32_t)x32[j];
+    return sum;
+}
+
+void orc_block_dots_q8w(const int8_t* qw, int64_t M, int64_t K, const int8_t* xq, int64_t B, int32_t* I) {
+    const int64_t nb = K / QK;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t kb = 0; kb < nb; ++kb)
+                I[(b * M + m) * nb + kb] = block_dot_q8w(qw + m * K + kb * QK, xq + b * K + kb * QK);
+}
+
+static float out_element_q8w(const int8_t* w_row, const uint16_t* d_row, int64_t K, const int8_t* x_row,
+                             const float* xd_row, double* y64) {
+    const int64_t nb = K / QK;
+    float acc = 0.0f;
+    double acc64 = 0.0;
+    for (int64_t kb = 0; kb < nb; ++kb) {
+        const int32_t I = block_dot_q8w(w_row + kb * QK, x_row + kb * QK);
+        const float dw = orc_f16_to_f32(d_row[kb]);
+        const float c = dw * xd_row[kb];
+        const float t = (float)I * c;
+        acc = acc + t;
+        acc64 += (double)I * (double)dw * (double)xd_row[kb];
+    }
+    if (y64) *y64 = acc64;
+    return acc;
+}
+
+typedef struct {
+    const int8_t* qw;
+    const uint16_t* d;
+    int64_t M, K, B, m0, m1;
+    const int8_t* xq;
+    const float* xd;
+    float* y;
+    double* y64;
+} mm8_job;
+
+static void* mm8_worker(void* arg) {
+    const mm8_job* j = (const mm8_job*)arg;
+    const int64_t nb = j->K / QK;
+    for (int64_t b = 0; b < j->B; ++b)
+        for (int64_t m = j->m0; m < j->m1; ++m)
+            j->y[b * j->M + m] = out_element_q8w(j->qw + m * j->K, j->d + m * nb, j->K, j->xq + b * j->K,
+                                                 j->xd + b * nb, j->y64 ? &j->y64[b * j->M + m] : NULL);
+    return NULL;
+}
+
+void orc_mul_mat_q8w_mt(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                        const float* xd, int64_t B, float* y, double* y64, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > M) nthreads = (int)(M > 0 ? M : 1);
+    pthread_t* th = (pthread_t*)malloc((size_t)nthreads * sizeof(pthread_t));
+    mm8_job* jobs = (mm8_job*)malloc((size_t)nthreads * sizeof(mm8_job));
+    for (int t = 0; t < nthreads; ++t) {
+        mm8_job j = {qw, d, M, K, B, M * t / nthreads, M * (t + 1) / nthreads, xq, xd, y, y64};
+        jobs[t] = j;
+        pthread_create(&th[t], NULL, mm8_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+}

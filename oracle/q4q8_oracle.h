@@ -103,6 +103,23 @@ void orc_mul_mat_id(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                     const int8_t* xq, const float* xd, int64_t n_x_slots,
                     const int32_t* ids, int64_t T, int64_t top_k, float* y, int nthreads);
 
+/* Q8_0 weights: the second weight type of the contract.  The GGML backend
+ * page ("GGML：Backend 抽象与硬件加速", sections "Metal 与 Vulkan：默认路径和生
+ * 成路径" and "对照本栈") has the conversion bridge pick Q4_K or Q8_0 and new
+ * types appended to the type list, every backend kernel set learning each
+ * one.  Reading: 32-element blocks, an fp16 scale and 32 int8 codes; the block
+ * rule is the Q8 rule of the activations with the scale stored as fp16:
+ *   amax = max |w|; d = fl(amax / 127); id = fl(1 / d) (0 if d == 0);
+ *   q = roundf(fl(w * id)) (halves away from zero), clamped to [-127, 127];
+ *   stored scale fp16(d), nearest even; codes from the fp32 d (as for Q4).
+ * Planes: qw i8 [M][K] (block b of row m at m*K + 32b), d u16 [M][K/32].
+ * The product is the Q4 product with I = sum_j qw_j * x_j (exact in int32:
+ * |I| <= 32 * 127 * 127). */
+void orc_q8w_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d);
+void orc_block_dots_q8w(const int8_t* qw, int64_t M, int64_t K, const int8_t* xq, int64_t B, int32_t* I);
+void orc_mul_mat_q8w_mt(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                        const float* xd, int64_t B, float* y, double* y64, int nthreads);
+
 /* RMS_NORM + MUL + ADD prologue.  The Metal fusion page ("llama.cpp
  * b10909：Metal后端融合表重构...", its fusion-pattern counts) lists the
  * RMS_NORM+MUL+ADD pattern beside RMS_NORM+MUL; reading: the three ops in that
