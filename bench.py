@@ -524,6 +524,78 @@ def bench_prefill(args, dev):
     return out
 
 
+def q8_0_bytes(M, K):
+    return M * K * 17 // 16  # 32 int8 codes + one fp16 scale per 32 weights
+
+
+def bench_q8_0(args, dev):
+    """Q8_0 weights on the Llama-3-8B layer shapes, 4 layers (about 0.93 GB of
+    weights, past the on-die caches).  Decode at B = 1 and 8 over Q8 planes:
+    one grouped streaming launch over the 28 products (`GB/s`, over weights +
+    Q8 activations + fp32 outputs), and one launch per matrix captured in a
+    HIP graph (`per_matrix`).  Prefill at T = 2048: one grouped tiled launch
+    over the seven products of one layer."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    layer = wl.LLAMA_3_8B
+    n_layers = 4
+    mats = []
+    for l in range(n_layers):
+        for mi, m in enumerate(layer):
+            w = wl.weight_device(3, l, mi, m.M, m.K, dev)
+            qw, d = q.q8_0_quantize(w)
+            del w
+            mats.append((m, qw, d))
+    torch.cuda.synchronize()
+    out = {"layers": n_layers}
+    reps = max(5, args.steps // 2)
+    for B in (1, 8):
+        planes = {}
+        for slot, K in wl.slot_k(layer).items():
+            x = wl.activation_device(3, 0, slot, B, K, dev)
+            gw = wl.norm_weight_device(3, 0, slot, K, dev)
+            planes[slot] = q.q8_quantize_rmsnorm(x, gw, 1e-5)[:2]
+        ys = [torch.empty((B, m.M), dtype=torch.float32, device=dev) for m, _, _ in mats]
+        nbytes = sum(q8_0_bytes(m.M, m.K) + B * m.K * 9 // 8 + B * m.M * 4 for m, _, _ in mats)
+        grp = q.Group([{"qw": qw, "d": d, "y": y, "xq": planes[m.slot][0], "xd": planes[m.slot][1]}
+                       for (m, qw, d), y in zip(mats, ys)], B=B)
+        ms_grp = per_launch_ms(lambda: grp(), reps)
+
+        def step():
+            for (m, qw, d), y in zip(mats, ys):
+                q.mul_mat_q8_0_q8(qw, d, planes[m.slot][0], planes[m.slot][1], y=y)
+
+        g = capture(step)
+        ms, _ = time_graph(g, reps, 2)
+        out[f"B={B}"] = {"GB/s": round(nbytes / (ms_grp * 1e-3) / 1e9, 1), "ms_per_launch": round(ms_grp, 4),
+                         "hbm_frac": round(nbytes / (ms_grp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "route": "one grouped streaming launch over the 28 products",
+                         "per_matrix": {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
+                                        "launches": len(mats)}}
+        del g, grp, ys, planes
+    T = 2048
+    planes = {}
+    for slot, K in wl.slot_k(layer).items():
+        x = wl.activation_device(3, 0, slot, T, K, dev)
+        gw = wl.norm_weight_device(3, 0, slot, K, dev)
+        planes[slot] = q.q8_quantize_rmsnorm(x, gw, 1e-5)[:2]
+        del x
+    ys = [torch.empty((T, m.M), dtype=torch.float32, device=dev) for m, _, _ in mats[:7]]
+    gemm = q.Group([{"qw": qw, "d": d, "y": y, "xq": planes[m.slot][0], "xd": planes[m.slot][1]}
+                    for (m, qw, d), y in zip(mats[:7], ys)], B=T)
+    ms = per_launch_ms(lambda: gemm(), reps)
+    ops = 2 * T * sum(m.M * m.K for m in layer)
+    tops = ops / (ms * 1e-3) / 1e12
+    out[f"prefill_T={T}"] = {"TOPS": round(tops, 1), "frac_i8_peak": round(tops / I8_PEAK_TOPS, 4),
+                             "ms_per_layer": round(ms, 4), "launch": "one grouped tiled launch over the 7 products"}
+    del gemm, ys, planes, mats
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_prologues(args, dev):
     """The standalone activation prologues on Llama-3-8B-shaped rows
     (K = 4096): RMS_NORM+MUL -> Q8 and RMS_NORM+MUL+ADD -> Q8 (one addend row
@@ -702,6 +774,8 @@ def main():
         print("[bench] moe done", file=sys.stderr, flush=True)
         report["prologues"] = bench_prologues(args, dev)
         print("[bench] prologues done", file=sys.stderr, flush=True)
+        report["q8_0"] = bench_q8_0(args, dev)
+        print("[bench] q8_0 done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         report["cpu_baseline"] = cpu_baseline(model, args.cpu_seconds)
     else:

@@ -30,6 +30,7 @@ Q4Q8_E_LAUNCH = -4
 Q4Q8_E_UNSUPPORTED = -5
 
 Q8_NO_NORM = 1
+WEIGHTS_Q8_0 = 2  # Q4Q8_WEIGHTS_Q8_0: a group product with Q8_0 weights
 
 PATH_AUTO = 0
 PATH_GEMV = 1
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_sum_f32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp, vp]
     L.q8_quantize_swiglu.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
+    L.q8_0_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.mul_mat_q8_0_q8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
+    L.mul_mat_q8_0_q8_blocksums.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
     L.q4q8_group_build.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int32, i64, vp, sz, vp, sz,
                                    ctypes.POINTER(GroupPlan)]
     L.mul_mat_q4q8_group.argtypes = [vp, ctypes.POINTER(GroupPlan), vp]
@@ -95,7 +99,7 @@ def lib() -> ctypes.CDLL:
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
                  "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
                  "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32", "q8_quantize_rmsnorm_add",
-                 "q8_quantize_swiglu"):
+                 "q8_quantize_swiglu", "q8_0_quantize", "mul_mat_q8_0_q8", "mul_mat_q8_0_q8_blocksums"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -282,6 +286,65 @@ def mul_mat_q4q8_blocksums(qs, d, xq, xd, y=None, I=None, stream=None):
     return y, I
 
 
+def q8_0_quantize(w, qw=None, d=None, stream=None):
+    """fp32 W [M][K] -> Q8_0 planes (qw i8 [M][K], d int16 [M][K/32] fp16 bits)."""
+    _need(w, "w", (torch.float32,), 2)
+    M, K = w.shape
+    if qw is None:
+        qw = torch.empty((M, K), dtype=torch.int8, device=w.device)
+    if d is None:
+        d = torch.empty((M, max(K // QK, 0)), dtype=torch.int16, device=w.device)
+    _need(qw, "qw", (torch.int8,))
+    _need(d, "d", _F16_BITS)
+    if qw.numel() != M * K or d.numel() != M * (K // QK):
+        raise ValueError("qw / d shape does not match w")
+    _check("q8_0_quantize", lib().q8_0_quantize(_ptr(w), M, K, _ptr(qw), _ptr(d), _stream(stream, w.device)))
+    return qw, d
+
+
+def _matmul_shapes_q8_0(qw, d, xq, xd):
+    _need(qw, "qw", (torch.int8,), 2)
+    _need(d, "d", _F16_BITS, 2)
+    _need(xq, "xq", (torch.int8,), 2)
+    _need(xd, "xd", (torch.float32,), 2)
+    M, K = qw.shape
+    B = xq.shape[0]
+    if xq.shape[1] != K or d.shape != (M, K // QK) or xd.shape != (B, K // QK):
+        raise ValueError(f"shape mismatch: qw {tuple(qw.shape)} d {tuple(d.shape)} xq {tuple(xq.shape)} "
+                         f"xd {tuple(xd.shape)}")
+    return M, K, B
+
+
+def mul_mat_q8_0_q8(qw, d, xq, xd, y=None, stream=None):
+    """y f32 [B][M] = Q8_0 W [M][K] times Q8 x [B][K] (per column)."""
+    M, K, B = _matmul_shapes_q8_0(qw, d, xq, xd)
+    if y is None:
+        y = torch.empty((B, M), dtype=torch.float32, device=qw.device)
+    _need(y, "y", (torch.float32,))
+    if y.numel() != B * M:
+        raise ValueError("y shape does not match")
+    _check("mul_mat_q8_0_q8", lib().mul_mat_q8_0_q8(_ptr(qw), _ptr(d), M, K, _ptr(xq), _ptr(xd), B, _ptr(y),
+                                                    _stream(stream, qw.device)))
+    return y
+
+
+def mul_mat_q8_0_q8_blocksums(qw, d, xq, xd, y=None, I=None, stream=None):
+    """As mul_mat_q8_0_q8, also returning the exact block sums I i32 [B][M][K/32]."""
+    M, K, B = _matmul_shapes_q8_0(qw, d, xq, xd)
+    if y is None:
+        y = torch.empty((B, M), dtype=torch.float32, device=qw.device)
+    if I is None:
+        I = torch.empty((B, M, K // QK), dtype=torch.int32, device=qw.device)
+    _need(y, "y", (torch.float32,))
+    _need(I, "I", (torch.int32,))
+    if y.numel() != B * M or I.numel() != B * M * (K // QK):
+        raise ValueError("y / I shape does not match")
+    _check("mul_mat_q8_0_q8_blocksums",
+           lib().mul_mat_q8_0_q8_blocksums(_ptr(qw), _ptr(d), M, K, _ptr(xq), _ptr(xd), B, _ptr(y), _ptr(I),
+                                           _stream(stream, qw.device)))
+    return y, I
+
+
 def mul_mat_q4q8_rmsnorm(qs, d, x, g, eps, flags=0, y=None, stream=None):
     """y f32 [B][M] = Q4 W [M][K] times Q8(RMSNorm(x) * g) for fp32 x [B][K], the
     prologue folded into the product kernel (same codes as q8_quantize_rmsnorm)."""
@@ -347,7 +410,8 @@ def mul_mat_q4q8_group(table_dev, plan, stream=None):
 class Group:
     """A list of independent streaming products launched together.
 
-    Each product is given as keyword arguments: qs, d (weights), y (output),
+    Each product is given as keyword arguments: qs (Q4 codes) or qw (Q8_0
+    codes), d (weight scales), y (output),
     and either xq, xd (Q8 activations) or x with g / eps (fp32 activations
     that the group's prologue pass normalises and quantises; flags=Q8_NO_NORM
     skips the norm).  The tensors must stay alive and in place while the group
@@ -358,16 +422,24 @@ class Group:
         descs = []
         self._keep = []
         for i, p in enumerate(problems):
-            qs, d, y = p["qs"], p["d"], p["y"]
-            _need(qs, f"problems[{i}].qs", (torch.uint8,), 2)
-            M, half = qs.shape
-            K = 2 * half
+            d, y = p["d"], p["y"]
+            if p.get("qw") is not None:
+                qs = p["qw"]
+                _need(qs, f"problems[{i}].qw", (torch.int8,), 2)
+                M, K = qs.shape
+                wflag = WEIGHTS_Q8_0
+            else:
+                qs = p["qs"]
+                _need(qs, f"problems[{i}].qs", (torch.uint8,), 2)
+                M, half = qs.shape
+                K = 2 * half
+                wflag = 0
             _need(d, f"problems[{i}].d", _F16_BITS, 2)
             _need(y, f"problems[{i}].y", (torch.float32,), 2)
             if tuple(d.shape) != (M, K // 32) or tuple(y.shape) != (B, M):
                 raise ValueError(f"problems[{i}]: d must be ({M}, {K // 32}) and y ({B}, {M})")
             desc = GemvDesc(qs=qs.data_ptr(), d=d.data_ptr(), M=M, K=K, y=y.data_ptr(),
-                            eps=float(p.get("eps", 0.0)), flags=int(p.get("flags", 0)))
+                            eps=float(p.get("eps", 0.0)), flags=int(p.get("flags", 0)) | wflag)
             if p.get("xq") is not None:
                 _need(p["xq"], f"problems[{i}].xq", (torch.int8,), 2)
                 _need(p["xd"], f"problems[{i}].xd", (torch.float32,), 2)
@@ -387,7 +459,7 @@ class Group:
                     desc.g = p["g"].data_ptr()
             descs.append(desc)
             self._keep.append(p)
-        dev = device if device is not None else problems[0]["qs"].device
+        dev = device if device is not None else problems[0]["d"].device
         plan = q4q8_group_plan(descs, B)
         self.workspace = None
         if plan.workspace_bytes > 0:

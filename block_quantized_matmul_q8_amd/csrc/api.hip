@@ -103,8 +103,10 @@ q4q8::GemvProblem single_problem(const uint8_t* qs, const uint16_t* d, int64_t M
   return p;
 }
 
+// wf: weight format of qs (q4q8::WeightFormat); both routes serve both.
 int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
-                  const float* xd, int64_t B, float* y, int32_t* I, void* stream) {
+                  const float* xd, int64_t B, float* y, int32_t* I, void* stream,
+                  int wf = q4q8::kWeightQ4) {
   int st = check_matmul_args(qs, d, M, K, xq, xd, B, y);
   if (st) return st;
   if (I && !aligned(I, 4)) return fail(Q4Q8_E_ALIGN, "I misaligned");
@@ -127,10 +129,11 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
     p.xq = xq;
     p.xd = xd;
     p.mode = q4q8::kModeQ8;
-    const int win = q4q8::gemv_window_rows(K, B);
+    p.wf = wf;
+    const int win = q4q8::gemv_window_rows(K, B, wf);
     p.n_win = (int32_t)((M + win - 1) / win);
     g_counts[0].fetch_add(1, std::memory_order_relaxed);
-    return launched(q4q8::launch_gemv_table(p, nullptr, nullptr, p.n_win, K, B, false, I, s), "gemv");
+    return launched(q4q8::launch_gemv_table(p, nullptr, nullptr, p.n_win, K, B, false, I, s, wf), "gemv");
   }
   const int64_t tiles = q4q8::gemm_tiles(M, B);
   if (tiles > INT32_MAX || B > INT32_MAX)
@@ -138,9 +141,10 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
   q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
   p.xq = xq;
   p.xd = xd;
+  p.wf = wf;
   p.n_win = (int32_t)tiles;
   g_counts[1].fetch_add(1, std::memory_order_relaxed);
-  return launched(q4q8::launch_gemm(p, nullptr, nullptr, tiles, B, I, s), "gemm");
+  return launched(q4q8::launch_gemm(p, nullptr, nullptr, tiles, B, I, s, wf), "gemm");
 }
 
 }  // namespace
@@ -225,6 +229,31 @@ Q4Q8_EXPORT int mul_mat_q4q8_blocksums(const uint8_t* qs, const uint16_t* d, int
                                        void* stream) {
   if (!I && M > 0 && B > 0) return fail(Q4Q8_E_ARG, "null pointer argument (I)");
   return matmul_common(qs, d, M, K, xq, xd, B, y, I, stream);
+}
+
+Q4Q8_EXPORT int q8_0_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, void* stream) {
+  int st;
+  if ((st = check_k(K)) || (st = check_dims(M, 1))) return st;
+  if (M == 0) return ok();
+  if (!w || !qw || !d) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(w, 16) || !aligned(qw, 16) || !aligned(d, 2))
+    return fail(Q4Q8_E_ALIGN, "w/qw must be 16-byte aligned, d 2-byte");
+  if ((st = check_device())) return st;
+  return launched(q4q8::launch_q8w_quantize(w, M, K, qw, d, static_cast<hipStream_t>(stream)), "q8_0_quantize");
+}
+
+Q4Q8_EXPORT int mul_mat_q8_0_q8(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                                const float* xd, int64_t B, float* y, void* stream) {
+  return matmul_common(reinterpret_cast<const uint8_t*>(qw), d, M, K, xq, xd, B, y, nullptr, stream,
+                       q4q8::kWeightQ8);
+}
+
+Q4Q8_EXPORT int mul_mat_q8_0_q8_blocksums(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K,
+                                          const int8_t* xq, const float* xd, int64_t B, float* y, int32_t* I,
+                                          void* stream) {
+  if (!I && M > 0 && B > 0) return fail(Q4Q8_E_ARG, "null pointer argument (I)");
+  return matmul_common(reinterpret_cast<const uint8_t*>(qw), d, M, K, xq, xd, B, y, I, stream,
+                       q4q8::kWeightQ8);
 }
 
 Q4Q8_EXPORT size_t mul_mat_id_q4q8_workspace(int64_t E, int64_t T, int64_t top_k) {
@@ -336,7 +365,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (e.M == 0) continue;
     if (!e.qs || !e.d || !e.y) return fail(Q4Q8_E_ARG, "descriptor %d: null pointer", i);
     if (!aligned(e.qs, 16) || !aligned(e.d, 2) || !aligned(e.y, 4)) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
-    if (e.flags & ~Q8_NO_NORM) return fail(Q4Q8_E_ARG, "descriptor %d: unknown flags", i);
+    if (e.flags & ~(Q8_NO_NORM | Q4Q8_WEIGHTS_Q8_0)) return fail(Q4Q8_E_ARG, "descriptor %d: unknown flags", i);
     if (!tiled && !q4q8::gemv_supported(e.M, e.K, B))
       return fail(Q4Q8_E_UNSUPPORTED, "descriptor %d: K = %lld with B = %lld exceeds the streaming kernel", i,
                   (long long)e.K, (long long)B);
@@ -398,6 +427,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (e.M == 0) continue;
     q4q8::GemvProblem p = single_problem(e.qs, e.d, e.M, e.K, e.y);
     p.mode = q4q8::kModeQ8;
+    p.wf = (e.flags & Q4Q8_WEIGHTS_Q8_0) ? q4q8::kWeightQ8 : q4q8::kWeightQ4;
     if (e.xq) {
       p.xq = e.xq;
       p.xd = e.xd;
@@ -410,7 +440,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (tiled) {
       t = q4q8::gemm_tiles(e.M, B);
     } else {
-      const int win = q4q8::gemv_window_rows(e.K, B);
+      const int win = q4q8::gemv_window_rows(e.K, B, p.wf);
       t = (e.M + win - 1) / win;
     }
     tiles += t;

@@ -98,6 +98,22 @@ __device__ __forceinline__ int dot_block(const u32x4 w, const i32x4 xa, const i3
   return s;
 }
 
+// Exact int32 block product s0 + sum_j w_j * x_j of one Q8_0 weight block
+// (32 int8 codes in w0 = codes 0..15, w1 = codes 16..31) with one Q8 block.
+__device__ __forceinline__ int dot_block_q8(const u32x4 w0, const u32x4 w1, const i32x4 xa, const i32x4 xb,
+                                            int s0) {
+  int s = s0;
+  s = __builtin_amdgcn_sdot4((int)w0.x, xa.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)w0.y, xa.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)w0.z, xa.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)w0.w, xa.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)w1.x, xb.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)w1.y, xb.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)w1.z, xb.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)w1.w, xb.w, s, false);
+  return s;
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // fences global memory, which makes every wave wait for all of its global
 // loads in flight -- a streaming kernel would drain its prefetch at every
@@ -115,6 +131,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Weight block formats (qs of a GemvProblem): per 32-element block,
+// kWeightQ4 = 16 bytes of packed 4-bit codes (offset 8), kWeightQ8 = Q8_0,
+// 32 int8 codes; both with one fp16 scale per block in d.
+enum WeightFormat : int {
+  kWeightQ4 = 0,
+  kWeightQ8 = 1,
+};
+
 // One product of a (grouped) GEMV launch, as the kernel reads it.
 enum GemvMode : int32_t {
   kModeQ8 = 0,    // activations given as Q8 planes xq / xd
@@ -123,7 +147,7 @@ enum GemvMode : int32_t {
 };
 
 struct alignas(16) GemvProblem {
-  const uint8_t* qs;   // [M][K/2]
+  const uint8_t* qs;   // [M][K/2] Q4, or [M][K] Q8_0 (wf)
   const uint16_t* d;   // [M][K/32]
   const int8_t* xq;    // [B][K]       (kModeQ8)
   const float* xd;     // [B][K/32]    (kModeQ8)
@@ -136,7 +160,8 @@ struct alignas(16) GemvProblem {
   int32_t mode;
   int32_t win_begin;   // index of this problem's first window in the launch
   int32_t n_win;       // windows of this problem (ceil(M / window rows))
-  int32_t pad[2];
+  int32_t wf;          // weight format of qs (WeightFormat)
+  int32_t pad;
 };
 static_assert(sizeof(GemvProblem) == 96, "GemvProblem layout");
 
@@ -154,22 +179,27 @@ struct alignas(16) PrologueJob {
 };
 static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
 
+
 // Route selection helpers (host).
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
-// Rows per window (the unit a workgroup streams) for a product with K and B.
-Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B);
+// Rows per window (the unit a workgroup streams) for a product with K and B;
+// wf: weight format (WeightFormat).
+Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B, int wf = kWeightQ4);
 // Persistent launch over the products of a device `table`, window w of the
 // launch belonging to record map[w]; or, when table == nullptr, over the
 // single record `p`.  `n_windows` = total windows; `max_k` = largest K among
 // the products (selects the kernel instance and the LDS size).
 Q4Q8_HIDDEN hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table,
                                          const int32_t* map, int64_t n_windows, int64_t max_k,
-                                         int64_t B, bool any_fused, int32_t* I, hipStream_t s);
+                                         int64_t B, bool any_fused, int32_t* I, hipStream_t s,
+                                         int wf = kWeightQ4);
 
 // Launchers: enqueue on `s`, return the launch status.
 Q4Q8_HIDDEN hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
                                           uint16_t* d, hipStream_t s);
+Q4Q8_HIDDEN hipError_t launch_q8w_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d,
+                                           hipStream_t s);
 // a: addend rows (RMS_NORM+MUL+ADD; row b at a + b * a_row_stride) or null.
 Q4Q8_HIDDEN hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* g,
                                          float eps, bool no_norm, int8_t* xq, float* xd,
@@ -185,7 +215,8 @@ Q4Q8_HIDDEN int64_t gemm_tiles(int64_t M, int64_t B);
 // gemm_tiles(p.M, B)) or over the products of a device `table`, tile t of the
 // launch belonging to record tile_map[t] (its first tile is win_begin).
 Q4Q8_HIDDEN hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
-                                   int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s);
+                                   int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s,
+                                   int wf = kWeightQ4);
 Q4Q8_HIDDEN size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
 Q4Q8_HIDDEN hipError_t launch_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k,
                                              int64_t M, float* out, hipStream_t s);

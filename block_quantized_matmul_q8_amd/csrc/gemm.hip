@@ -26,6 +26,11 @@
 // barrier.  Loads are unconditional from clamped addresses; rows, tokens and
 // blocks past the end get zero scales, so they add exact zeros.
 //
+// Q8_0 weights (32 signed int8 codes and one fp16 scale per block) take the
+// same path: a stage then holds 128 bytes of codes per weight row, fetched as
+// four 16-byte pieces per thread and stored to LDS as they are (no unpack);
+// everything after the LDS stage is shared with the Q4 route.
+//
 // One launch serves one product or a group of products (a device table of
 // records plus a tile -> record map; the map lists the long-K products
 // first).  Tiles of a product are ordered weight-tile major (consecutive
@@ -61,29 +66,14 @@ struct GemmStage {
   float cw[kKB][kTM];        // -1.5 * 2^23 * dw
 };
 
-template <bool WRITE_I, bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
-    GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
-    int n_tiles, int B, int32_t* __restrict__ Iout) {
-  __shared__ __align__(16) GemmStage st[kNBuf];
-
+// Tile L of product P (its tiles start at P.win_begin): n_nt token tiles per
+// weight tile; st: the workgroup's LDS stage buffers.
+template <bool WRITE_I, int WF>
+__device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt, int B, GemmStage* st,
+                                          int32_t* __restrict__ Iout) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wt = wave >> 1, ww = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
-
-  // Tile of this workgroup.  The tile list is dealt to the XCDs (workgroup
-  // bid runs on XCD bid % 8) in chunks of n_nt consecutive tiles -- the token
-  // tiles of one weight tile -- round robin: a weight tile stays on one XCD
-  // (reused from its L2) while long and short products spread over all XCDs.
-  const int n_nt = (B + kTN - 1) / kTN;
-  const int bid = blockIdx.x;
-  const int span = kXcds * n_nt;
-  int L = bid;
-  if (bid < n_tiles / span * span) {
-    const int x = bid % kXcds, pos = bid / kXcds;
-    L = ((pos / n_nt) * kXcds + x) * n_nt + pos % n_nt;
-  }
-  const GemvProblem P = GROUPED ? table[tile_map[L]] : p0;
   const int M = P.M, K = P.K;
   const uint8_t* __restrict__ qs = P.qs;
   const uint16_t* __restrict__ d = P.d;
@@ -91,16 +81,18 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
   const float* __restrict__ xd = P.xd;
   float* __restrict__ y = P.y;
   const int nb = K / kQK;
-  const int64_t row_bytes = K / 2;
+  constexpr int kNW = WF == kWeightQ8 ? 4 : 2;  // 16-byte weight chunks per thread per stage
+  const int64_t row_bytes = WF == kWeightQ8 ? K : K / 2;
   const int lt = L - P.win_begin;
   const int m0 = (lt / n_nt) * kTM, n0 = (lt % n_nt) * kTN;
 
   // Thread -> data of a stage: activation chunk c = 256 i + tid is token
-  // c / 8, 16-byte piece c % 8 (two pieces per block); weight chunk
-  // c = 256 i + tid is row c / 4, block c % 4; scales: row / token tid / 2,
+  // c / 8, 16-byte piece c % 8 (two pieces per block); Q4 weight chunk
+  // c = 256 i + tid is row c / 4, block c % 4, Q8_0 weight chunk row c / 8,
+  // piece c % 8 like the activations; scales: row / token tid / 2,
   // blocks 2 (tid % 2) and 2 (tid % 2) + 1 (read one value each: d rows are
   // only 2-byte aligned).
-  auto fetch = [&](int kb0, i32x4 (&a)[kNA], u32x4 (&w)[2], uint32_t (&dw)[2], float (&dx)[2]) {
+  auto fetch = [&](int kb0, i32x4 (&a)[kNA], u32x4 (&w)[kNW], uint32_t (&dw)[2], float (&dx)[2]) {
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
@@ -109,12 +101,19 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
       a[i] = *gptr(reinterpret_cast<const i32x4*>(xq + (int64_t)n * K + (int64_t)blk * kQK + 16 * (c % 2)));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kNW; ++i) {
       const int c = 256 * i + tid;
-      const int m = min(m0 + c / 4, M - 1);
-      const int blk = min(kb0 + c % 4, nb - 1);
-      w[i] = __builtin_nontemporal_load(
-          gptr(reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * 16)));
+      if constexpr (WF == kWeightQ8) {
+        const int m = min(m0 + c / 8, M - 1);
+        const int blk = min(kb0 + (c % 8) / 2, nb - 1);
+        w[i] = __builtin_nontemporal_load(gptr(
+            reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * kQK + 16 * (c % 2))));
+      } else {
+        const int m = min(m0 + c / 4, M - 1);
+        const int blk = min(kb0 + c % 4, nb - 1);
+        w[i] = __builtin_nontemporal_load(
+            gptr(reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * 16)));
+      }
     }
     const int m = min(m0 + tid / 2, M - 1);
     const int n = min(n0 + tid / 2, B - 1);
@@ -126,23 +125,31 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     }
   };
 
-  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[kNA], const u32x4 (&w)[2],
+  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[kNA], const u32x4 (&w)[kNW],
                          const uint32_t (&dwb)[2], const float (&dxv)[2]) {
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
       *reinterpret_cast<i32x4*>(&sg.a[(c % 8) / 2][c / 8][16 * (c % 2)]) = a[i];
     }
-    const uint32_t m4 = 0x0F0F0F0Fu;
+    if constexpr (WF == kWeightQ8) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = 256 * i + tid;
-      const u32x4 qv = w[i];
-      const u32x4 lo = {nib_to_s8(qv.x & m4), nib_to_s8(qv.y & m4), nib_to_s8(qv.z & m4), nib_to_s8(qv.w & m4)};
-      const u32x4 hi = {nib_to_s8((qv.x >> 4) & m4), nib_to_s8((qv.y >> 4) & m4), nib_to_s8((qv.z >> 4) & m4),
-                        nib_to_s8((qv.w >> 4) & m4)};
-      *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][0]) = lo;
-      *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][16]) = hi;
+      for (int i = 0; i < kNW; ++i) {
+        const int c = 256 * i + tid;
+        *reinterpret_cast<u32x4*>(&sg.w[(c % 8) / 2][c / 8][16 * (c % 2)]) = w[i];
+      }
+    } else {
+      const uint32_t m4 = 0x0F0F0F0Fu;
+#pragma unroll
+      for (int i = 0; i < kNW; ++i) {
+        const int c = 256 * i + tid;
+        const u32x4 qv = w[i];
+        const u32x4 lo = {nib_to_s8(qv.x & m4), nib_to_s8(qv.y & m4), nib_to_s8(qv.z & m4), nib_to_s8(qv.w & m4)};
+        const u32x4 hi = {nib_to_s8((qv.x >> 4) & m4), nib_to_s8((qv.y >> 4) & m4), nib_to_s8((qv.z >> 4) & m4),
+                          nib_to_s8((qv.w >> 4) & m4)};
+        *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][0]) = lo;
+        *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][16]) = hi;
+      }
     }
     const int r = tid / 2;
     const bool row_ok = m0 + r < M, tok_ok = n0 + r < B;
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
   for (int r = 0; r < 16; ++r) seed[r] = kMagicBits;
 
   i32x4 fa[kNA];
-  u32x4 fw[2];
+  u32x4 fw[kNW];
   uint32_t fdw[2];
   float fdx[2];
   fetch(0, fa, fw, fdw, fdx);
@@ -266,12 +273,54 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
       }
 }
 
+
+// Q8_0 and Q4 tiles share the LDS stage layout; a grouped launch takes each
+// product's weight format from its record (uniform over a workgroup).
+template <bool WRITE_I, bool GROUPED, int WF = kWeightQ4>
+__global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
+    GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
+    int n_tiles, int B, int32_t* __restrict__ Iout) {
+  __shared__ __align__(16) GemmStage st[kNBuf];
+
+  // Tile of this workgroup.  The tile list is dealt to the XCDs (workgroup
+  // bid runs on XCD bid % 8) in chunks of n_nt consecutive tiles -- the token
+  // tiles of one weight tile -- round robin: a weight tile stays on one XCD
+  // (reused from its L2) while long and short products spread over all XCDs.
+  const int n_nt = (B + kTN - 1) / kTN;
+  const int bid = blockIdx.x;
+  const int span = kXcds * n_nt;
+  int L = bid;
+  if (bid < n_tiles / span * span) {
+    const int x = bid % kXcds, pos = bid / kXcds;
+    L = ((pos / n_nt) * kXcds + x) * n_nt + pos % n_nt;
+  }
+  if constexpr (GROUPED) {
+    const GemvProblem P = table[tile_map[L]];
+    if (P.wf == kWeightQ8)
+      gemm_tile<WRITE_I, kWeightQ8>(P, L, n_nt, B, st, Iout);
+    else
+      gemm_tile<WRITE_I, kWeightQ4>(P, L, n_nt, B, st, Iout);
+  } else {
+    gemm_tile<WRITE_I, WF>(p0, L, n_nt, B, st, Iout);
+  }
+}
+
 int64_t gemm_tiles(int64_t M, int64_t B) { return ((M + kTM - 1) / kTM) * ((B + kTN - 1) / kTN); }
 
 hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
-                       int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s) {
+                       int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s, int wf) {
   const dim3 grid((unsigned)n_tiles), block(kGemmThreads);
-  if (table) {
+  if (wf == kWeightQ8 && !table) {
+    if (I)
+      hipLaunchKernelGGL((gemm_kernel<true, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    else
+      hipLaunchKernelGGL((gemm_kernel<false, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    return hipGetLastError();
+  }
+  if (wf != kWeightQ4 && !table) return hipErrorInvalidValue;
+  if (table) {  // weight format per record
     if (I) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
                        (int)B, I);

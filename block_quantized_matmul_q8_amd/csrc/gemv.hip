@@ -36,7 +36,11 @@ enum GemvKind : int {
   kKindBlockSums = 3,  // one product, Q8 planes, per-block sums written out
 };
 
-template <int BT, int J, int S, int KIND>
+// WF: weight format of the single-product kinds (a grouped launch takes each
+// product's format from its record; the folded prologue serves Q4 weights); a
+// Q8_0 block is two loads, so it keeps half the rows in flight for the same
+// bytes in flight.
+template <int BT, int J, int S, int KIND, int WF = kWeightQ4>
 __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ win_map,
     int n_windows, int B, int32_t* __restrict__ Iout) {
@@ -59,7 +63,11 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
       const int wl0 = w - P.win_begin, wl1 = seg_end - P.win_begin;
       const GemvClass cls = gemv_class_of(P.K, BT);
       dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
-        gemv_segment<BT, JJ, SS, false, false>(P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
+        if (P.wf == kWeightQ8)
+          gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif_of(kWeightQ8), kWeightQ8>(
+              P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
+        else
+          gemv_segment<BT, JJ, SS, false, false>(P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
       });
       w = seg_end;
       P = Pn;
@@ -67,7 +75,8 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
     }
   } else {
     if (w_begin < w_end)
-      gemv_segment<BT, J, S, FOLD, WRITE_I>(p0, DenseCols(p0), B, w_begin, w_end, smem, &split, parity, Iout);
+      gemv_segment<BT, J, S, FOLD, WRITE_I, DenseCols, gemv_rif_of(WF), WF>(p0, DenseCols(p0), B, w_begin, w_end, smem,
+                                                                            &split, parity, Iout);
   }
 }
 
@@ -90,9 +99,9 @@ bool gemv_fused_supported(int64_t K, int64_t B) {
   return c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;
 }
 
-int gemv_window_rows(int64_t K, int64_t B) {
+int gemv_window_rows(int64_t K, int64_t B, int wf) {
   if (B < 1 || B > 8) return 0;
-  return gemv_window_rows_bt(K, gemv_bt((int)B));
+  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif_of(wf));
 }
 
 // Workgroups that can be resident at once for one kernel instance and LDS
@@ -121,21 +130,34 @@ static int64_t resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <int BT, int J, int S, int KIND>
+template <int BT, int J, int S, int KIND, int WF = kWeightQ4>
 static hipError_t launch_kind(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
                               int64_t n_windows, int B, size_t lds, int32_t* I, hipStream_t s) {
-  const void* k = (const void*)gemv_kernel<BT, J, S, KIND>;
+  const void* k = (const void*)gemv_kernel<BT, J, S, KIND, WF>;
   int64_t grid = resident_workgroups(k, lds);
   if (grid > n_windows) grid = n_windows;
-  hipLaunchKernelGGL((gemv_kernel<BT, J, S, KIND>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, p,
+  hipLaunchKernelGGL((gemv_kernel<BT, J, S, KIND, WF>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, p,
                      table, map, (int)n_windows, B, I);
   return hipGetLastError();
 }
 
 template <int BT>
 static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
-                            int64_t n_windows, int64_t max_k, int B, bool fold, int32_t* I, hipStream_t s) {
+                            int64_t n_windows, int64_t max_k, int B, bool fold, int32_t* I, hipStream_t s,
+                            int wf) {
   if (table) return launch_kind<BT, 1, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+  if (wf == kWeightQ8) {
+    if (fold) return hipErrorInvalidValue;
+    const GemvClass c = gemv_class_of(max_k, B);
+    hipError_t err = hipErrorInvalidValue;
+    dispatch_class<BT>(c.J, c.S, [&]<int JJ, int SS>() {
+      if (I)
+        err = launch_kind<BT, JJ, SS, kKindBlockSums, kWeightQ8>(p, nullptr, nullptr, n_windows, B, 0, I, s);
+      else
+        err = launch_kind<BT, JJ, SS, kKindSingle, kWeightQ8>(p, nullptr, nullptr, n_windows, B, 0, I, s);
+    });
+    return err;
+  }
   const GemvClass c = gemv_class_of(max_k, B);
   const size_t lds = fold ? fused_lds_bytes(max_k, B) : 0;
   hipError_t err = hipErrorInvalidValue;
@@ -157,14 +179,14 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
 
 hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
                              int64_t n_windows, int64_t max_k, int64_t B, bool any_fused, int32_t* I,
-                             hipStream_t s) {
-  if (table && (any_fused || I)) return hipErrorInvalidValue;  // grouped launches read Q8 planes
+                             hipStream_t s, int wf) {
+  if (table && (any_fused || I)) return hipErrorInvalidValue;  // grouped: Q8 planes, format per record
   if (gemv_class_of(max_k, B).J == 0) return hipErrorInvalidValue;
   switch (gemv_bt((int)B)) {
-    case 1: return launch_bt<1>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
-    case 2: return launch_bt<2>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
-    case 4: return launch_bt<4>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
-    default: return launch_bt<8>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s);
+    case 1: return launch_bt<1>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s, wf);
+    case 2: return launch_bt<2>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s, wf);
+    case 4: return launch_bt<4>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s, wf);
+    default: return launch_bt<8>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s, wf);
   }
 }
 

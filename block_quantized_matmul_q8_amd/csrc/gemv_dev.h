@@ -83,6 +83,12 @@ __device__ __forceinline__ int code_sum8(const i32x4 a, const i32x4 b) {
 #define Q4Q8_GEMV_ROWS_IN_FLIGHT 16  // 16-byte loads per lane in flight per row group
 #endif
 
+// Rows in flight of a weight format: a Q8_0 block takes two 16-byte loads
+// per lane, so half the rows keep the same bytes in flight.
+__host__ __device__ constexpr int gemv_rif_of(int wf) {
+  return wf == kWeightQ8 ? Q4Q8_GEMV_ROWS_IN_FLIGHT / 2 : Q4Q8_GEMV_ROWS_IN_FLIGHT;
+}
+
 // Padded column count of the kernel instance serving B columns.
 __host__ __device__ constexpr int gemv_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 
@@ -177,8 +183,11 @@ struct RoutedCols {
 // the waves of row slot rs take the RU rows at rs*RU of each window, wave
 // part kp its share of K) with J blocks per lane.  `parity` alternates over
 // every compute of the workgroup (also across products) so that a K-split
-// exchange never overwrites values a slower wave has yet to read.
-template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT>
+// exchange never overwrites values a slower wave has yet to read.  WF: the
+// weight format; a Q8_0 block is two loads, so the caller passes half the
+// rows in flight (RIF) for the same bytes in flight.
+template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT,
+          int WF = kWeightQ4>
 __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& cols, int B, int wl0, int wl1,
                                              unsigned char* smem, SplitScratch* split, int& parity,
                                              int32_t* __restrict__ Iout) {
@@ -186,11 +195,13 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
   constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT;
   static_assert(NP <= kMaxNP, "split scratch too small");
   static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");
+  static_assert(!FOLD || WF == kWeightQ4, "the folded prologue serves Q4 weights");
+  constexpr int NL = WF == kWeightQ8 ? 2 : 1;  // 16-byte loads per block and lane
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rs = wave / S, kp = wave % S;
   const int kb0 = kp * kWave * J;
   const int M = P.M, K = P.K, nb = K >> 5;
-  const int64_t row_bytes = K >> 1;
+  const int64_t row_bytes = WF == kWeightQ8 ? K : K >> 1;
 
   // Loads are unconditional, from addresses clamped into the segment's rows
   // (so an overrun re-reads a row just loaded, from cache, and never touches
@@ -202,21 +213,23 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
   // so no conversion waits on a prefetch.  Weights and scales are read once:
   // non-temporal loads keep them from displacing reusable lines.
   const int row_last = min(M, wl1 * WIN) - 1;
-  auto load_group = [&](int row0, u32x4 (&w)[RU][J], uint32_t (&dw)[RU][J]) {
+  auto load_group = [&](int row0, u32x4 (&w)[RU][J * NL], uint32_t (&dw)[RU][J]) {
 #pragma unroll
     for (int r = 0; r < RU; ++r) {
       const int rowc = min(row0 + r, row_last);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int bc = min(kb0 + lane + kWave * j, nb - 1);
-        w[r][j] = __builtin_nontemporal_load(
-            &gptr(reinterpret_cast<const u32x4*>(P.qs))[rowc * (row_bytes / 16) + bc]);
+#pragma unroll
+        for (int h = 0; h < NL; ++h)
+          w[r][j * NL + h] = __builtin_nontemporal_load(
+              &gptr(reinterpret_cast<const u32x4*>(P.qs))[rowc * (row_bytes / 16) + bc * NL + h]);
         dw[r][j] = __builtin_nontemporal_load(&gptr(P.d)[(int64_t)rowc * nb + bc]);
       }
     }
   };
 
-  u32x4 wA[RU][J], wB[RU][J];
+  u32x4 wA[RU][J * NL], wB[RU][J * NL];
   uint32_t dA[RU][J], dB[RU][J];
   i32x4 xa[BT][J], xb[BT][J];
   float xdr[BT][J];
@@ -257,7 +270,8 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
         xa[c][j] = valid ? xa[c][j] : zero;
         xb[c][j] = valid ? xb[c][j] : zero;
         xdr[c][j] = valid ? xdr[c][j] : 0.0f;
-        xsr[c][j] = kMagicBits - code_sum8(xa[c][j], xb[c][j]);
+        // Q4 codes are unsigned (offset 8): remove 8 * sum x through the seed
+        xsr[c][j] = WF == kWeightQ8 ? kMagicBits : kMagicBits - code_sum8(xa[c][j], xb[c][j]);
       }
   } else {
     // Folded-in prologue: window A is requested first, then the whole
@@ -301,12 +315,13 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
 
   // One row group: block sums, scale, multi-row reduction, store (through
   // the part exchange when K is split).
-  // The block sum is accumulated onto kMagicBits - 8 sum x (xsr holds that
-  // seed), so its bits read as the float 1.5 * 2^23 + I (exact: |I| < 2^22)
+  // The block sum is accumulated onto kMagicBits - 8 sum x for Q4 codes, onto
+  // kMagicBits for Q8_0 codes (xsr holds that seed), so its bits read as the
+  // float 1.5 * 2^23 + I (exact: |I| < 2^22 for both formats)
   // and I * d_w comes out of one fma against -1.5 * 2^23 * d_w (exact: 2 + 11
   // significant bits) with a single rounding -- no integer subtract, no
   // conversion, and the column's d_x is applied by a second fma.
-  auto compute_group = [&](int row0, const u32x4 (&w)[RU][J], const uint32_t (&dw)[RU][J]) {
+  auto compute_group = [&](int row0, const u32x4 (&w)[RU][J * NL], const uint32_t (&dw)[RU][J]) {
     float acc[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -318,7 +333,11 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
         const float cwf = -kMagic * dwf;
 #pragma unroll
         for (int c = 0; c < BT; ++c) {
-          const int Fb = dot_block(w[r][j], xa[c][j], xb[c][j], xsr[c][j]);
+          int Fb;
+          if constexpr (WF == kWeightQ8)
+            Fb = dot_block_q8(w[r][2 * j], w[r][2 * j + 1], xa[c][j], xb[c][j], xsr[c][j]);
+          else
+            Fb = dot_block(w[r][j], xa[c][j], xb[c][j], xsr[c][j]);
           const float t = __builtin_fmaf(__builtin_bit_cast(float, Fb), dwf, cwf);
           acc[r * BT + c] = __builtin_fmaf(t, xdr[c][j], acc[r * BT + c]);
           if (WRITE_I) {

@@ -89,6 +89,38 @@ hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
 }
 
 // ---------------------------------------------------------------------------
+// fp32 weights -> Q8_0 blocks (32 int8 codes, fp16 scale), one thread per
+// block.  The codes follow the Q8 block rule with the fp32 scale; the stored
+// scale is that scale rounded to fp16 (the Q8_0 type of "GGML：Backend 抽象与
+// 硬件加速", sections "Metal 与 Vulkan：默认路径和生成路径" and "对照本栈",
+// read as 32-element blocks with an fp16 scale).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void q8w_quantize_kernel(const float* __restrict__ w, int64_t M, int64_t K,
+                                                           int8_t* __restrict__ qw, uint16_t* __restrict__ d) {
+  const int64_t nb = K / kQK;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * nb) return;
+  const int64_t row = idx / nb, b = idx - row * nb;
+  float v[kQK];
+  load_block32(w + row * K + b * kQK, v);
+  uint32_t packed[8];
+  float dd;
+  int sum;
+  q8_pack_block(v, packed, dd, sum);
+  uint4* dst = reinterpret_cast<uint4*>(qw + row * K + b * kQK);
+  dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  d[row * nb + b] = f32_to_f16_bits_rne(dd);
+}
+
+hipError_t launch_q8w_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, hipStream_t s) {
+  const int64_t n = M * (K / kQK);
+  const int64_t grid = (n + 255) / 256;
+  hipLaunchKernelGGL(q8w_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, w, M, K, qw, d);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Fused RMSNorm * g -> Q8 (standalone prologue).  One workgroup per activation
 // row; the steps and their order are those of prologue_dev.h.  Rows of up to
 // 16384 elements take the register form (one pass over x), longer rows the

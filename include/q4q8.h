@@ -62,8 +62,11 @@ extern "C" {
 #define Q4Q8_E_LAUNCH (-4)      /* the HIP runtime reported a launch error */
 #define Q4Q8_E_UNSUPPORTED (-5) /* valid request outside what is built */
 
-/* Flags of q8_quantize_rmsnorm. */
+/* Flags of q8_quantize_rmsnorm (and of a q4q8_gemv_desc). */
 #define Q8_NO_NORM 1u /* quantise x as it is: no normalisation, g ignored */
+/* Flag of a q4q8_gemv_desc: the product's weights are Q8_0 planes (qs points
+ * to int8 codes [M][K], 16-byte aligned; d as for Q4), see mul_mat_q8_0_q8. */
+#define Q4Q8_WEIGHTS_Q8_0 2u
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* q4q8_last_error(void);
@@ -151,6 +154,34 @@ int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, con
                  const float* xd, int64_t B, float* y, void* stream);
 
 /*
+ * Q8_0 weights -- the second weight type.  The GGML backend page (sections
+ * "Metal 与 Vulkan：默认路径和生成路径" and "对照本栈") names Q8_0 beside Q4 as a
+ * type the conversion bridge emits and every backend kernel set must learn.
+ * A Q8_0 block is 32 signed int8 codes and one fp16 scale; its product with a
+ * Q8 activation block is I = sum_j q_j x_j (exact in int32) times d_w d_x.
+ *
+ * q8_0_quantize -- fp32 weights to Q8_0 planes.  Rule per 32-block: the Q8
+ * block rule of q8_quantize_rmsnorm (d = fl(amax / 127), id = fl(1 / d) or 0,
+ * q = roundf(fl(w * id)) clamped to [-127, 127]) with codes from the fp32 d
+ * and the stored scale fp16(d), nearest even.
+ *   w  [M][K] f32, 16-byte aligned      qw [M][K] i8, 16-byte aligned
+ *   d  [M][K/32] u16, 2-byte aligned
+ */
+int q8_0_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, void* stream);
+
+/*
+ * mul_mat_q8_0_q8 -- y = W x for M x K Q8_0 weights and B Q8 activation
+ * columns: mul_mat_q4q8 with the weight planes qw [M][K] i8 (16-byte aligned)
+ * and d [M][K/32] u16.  Same routes (streaming kernel for B <= 8 within its
+ * register classes, int8-MFMA tiled kernel otherwise), same exact block sums,
+ * same rounding contract and errors.  Grouped launches take Q8_0 products
+ * through the Q4Q8_WEIGHTS_Q8_0 descriptor flag; no folded-prologue or MoE
+ * variant takes Q8_0 weights.
+ */
+int mul_mat_q8_0_q8(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                    const float* xd, int64_t B, float* y, void* stream);
+
+/*
  * mul_mat_q4q8_rmsnorm -- mul_mat_q4q8 with the activation prologue folded in:
  * the B fp32 activation rows x [B][K] go through exactly the steps of
  * q8_quantize_rmsnorm (same codes and scales, bit for bit) inside the product
@@ -176,13 +207,16 @@ int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_
  * caller copies the image unchanged to device memory (16-byte aligned) once;
  * mul_mat_q4q8_group then launches from the device table, any number of times
  * (it is safe to capture in a HIP graph).  Products with M == 0 are dropped.
- * Every product uses B activation columns (1 <= B <= 4).  Products must not
- * write overlapping outputs.
+ * Every product uses B activation columns, 1 <= B <= 65535: B <= 8 takes the
+ * streaming kernel (every K must fit its register classes), larger B the
+ * tiled int8-MFMA kernel.  Products must not write overlapping outputs.  Each
+ * product's weights are Q4 planes, or Q8_0 planes with flags &
+ * Q4Q8_WEIGHTS_Q8_0; one group may mix both.
  *
  * A product's activations are either Q8 planes (xq, xd; x == NULL) or fp32
  * rows x (xq == NULL) that go through the prologue of q8_quantize_rmsnorm
- * (g and eps, or flags = Q8_NO_NORM).  Each distinct fp32 input (same x, g,
- * K, eps and flags) is quantised once per call, by a prologue pass that runs
+ * (g and eps, or flags & Q8_NO_NORM).  Each distinct fp32 input (same x, g,
+ * K, eps and Q8_NO_NORM) is quantised once per call, by a prologue pass that runs
  * before the streaming pass, into the caller's device workspace
  * (plan->workspace_bytes, 16-byte aligned, passed to q4q8_group_build because
  * the table records point into it).  The workspace belongs to the group:
@@ -192,7 +226,7 @@ int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64_t M, int64_
  * takes fp32 rows.
  */
 typedef struct q4q8_gemv_desc {
-  const uint8_t* qs;  /* [M][K/2], 16-byte aligned */
+  const uint8_t* qs;  /* [M][K/2] Q4 (or [M][K] Q8_0 codes, see flags), 16-byte aligned */
   const uint16_t* d;  /* [M][K/32] */
   int64_t M;
   int64_t K;
@@ -201,7 +235,7 @@ typedef struct q4q8_gemv_desc {
   const float* x;     /* [B][K] fp32 activations (when xq == NULL), 16-byte aligned */
   const float* g;     /* [K] norm weight, 16-byte aligned (with x, unless Q8_NO_NORM) */
   float eps;
-  uint32_t flags;     /* Q8_NO_NORM or 0 */
+  uint32_t flags;     /* Q8_NO_NORM (fp32 rows quantised as they are), Q4Q8_WEIGHTS_Q8_0 */
   float* y;           /* [B][M] */
 } q4q8_gemv_desc;
 
@@ -288,8 +322,8 @@ int moe_expert_sum_f32(const float* y, const float* w, int64_t T, int64_t top_k,
 #define Q4Q8_PATH_GEMV 1
 #define Q4Q8_PATH_GEMM 2
 
-/* Force the route taken by mul_mat_q4q8 (process-wide).  Forcing GEMV for a
- * shape it cannot hold returns Q4Q8_E_UNSUPPORTED from mul_mat_q4q8. */
+/* Force the route taken by mul_mat_q4q8 and mul_mat_q8_0_q8 (process-wide).
+ * Forcing GEMV for a shape it cannot hold returns Q4Q8_E_UNSUPPORTED. */
 int q4q8_set_path(int path);
 
 /* Like mul_mat_q4q8, and also writes the exact per-block integer sums
@@ -298,6 +332,11 @@ int q4q8_set_path(int path);
 int mul_mat_q4q8_blocksums(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K,
                            const int8_t* xq, const float* xd, int64_t B, float* y, int32_t* I,
                            void* stream);
+
+/* mul_mat_q8_0_q8 that also writes the exact block sums I [B][M][K/32]
+ * (int32, 4-byte aligned), as mul_mat_q4q8_blocksums. */
+int mul_mat_q8_0_q8_blocksums(const int8_t* qw, const uint16_t* d, int64_t M, int64_t K, const int8_t* xq,
+                              const float* xd, int64_t B, float* y, int32_t* I, void* stream);
 
 /* Per-route dispatch counters since load or the last reset:
  * out[0] GEMV launches, out[1] GEMM launches, out[2] routed (MUL_MAT_ID)

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_id_q4q8", "moe_expert_sum_f32",
-              "q8_quantize_rmsnorm_add", "q8_quantize_swiglu",
+              "q8_quantize_rmsnorm_add", "q8_quantize_swiglu", "q8_0_quantize", "mul_mat_q8_0_q8",
+              "mul_mat_q8_0_q8_blocksums",
               "mul_mat_id_q4q8_workspace", "q4q8_last_error", "q4q8_set_path",
               "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_version"):
         assert n in names, n
@@ -298,6 +299,24 @@ def test_group_build_tiled_layout():
     assert plan.n_prologue == 1 and plan.workspace_bytes == 300 * 8192 + 300 * 256 * 4
 
 
+def test_group_build_q8_0_records():
+    """A Q8_0 product (descriptor flag) carries its weight format in its
+    record (int32 offset 20) and, with two loads per block, half the rows per
+    window: 32 rows at K = 2048, B = 1, against 64 for Q4."""
+    a = _desc(M=64, K=2048)
+    b = _desc(M=64, K=2048, flags=q.WEIGHTS_Q8_0, y=4096)
+    c = _desc(M=64, K=2048, flags=q.WEIGHTS_Q8_0 | q.Q8_NO_NORM, xq=None, xd=None, x=512, g=None, y=8192)
+    image, plan = _build([a, b, c], 1, 1 << 20, 4096)
+    recs = image[:plan.map_offset].view(np.int32).reshape(3, 24)
+    assert recs[:, 20].tolist() == [0, 1, 1]
+    assert recs[:, 19].tolist() == [1, 2, 2] and plan.n_windows == 5
+    assert plan.n_prologue == 1
+    # the tiled route keeps the format too
+    image, plan = _build([a, b], 300)
+    recs = image[:plan.map_offset].view(np.int32).reshape(2, 24)
+    assert recs[:, 20].tolist() == [0, 1]
+
+
 def test_group_build_validation_is_host_only():
     bad = [
         ([_desc(K=100)], 1, q.Q4Q8_E_ARG),
@@ -347,3 +366,39 @@ def test_fused_single_validation():
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, ctypes.c_void_p(260), p, f, 0, 1, p, None) == q.Q4Q8_E_ALIGN
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 16384, p, p, f, 0, 4, p, None) == q.Q4Q8_E_UNSUPPORTED
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, p, f, 2, 1, p, None) == q.Q4Q8_E_ARG
+
+
+def test_q8_0_entry_points_validate():
+    L = q.lib()
+    # K not a multiple of 32, negative sizes
+    assert L.q8_0_quantize(_v(256), 4, 48, _v(256), _v(256), None) == q.Q4Q8_E_ARG
+    assert L.q8_0_quantize(_v(256), -1, 64, _v(256), _v(256), None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q8_0_q8(_v(256), _v(256), 4, 33, _v(256), _v(256), 1, _v(256), None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q8_0_q8(_v(256), _v(256), 4, 64, _v(256), _v(256), -2, _v(256), None) == q.Q4Q8_E_ARG
+    # null pointers
+    assert L.q8_0_quantize(None, 4, 64, _v(256), _v(256), None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q8_0_q8(None, _v(256), 4, 64, _v(256), _v(256), 1, _v(256), None) == q.Q4Q8_E_ARG
+    assert L.mul_mat_q8_0_q8_blocksums(_v(256), _v(256), 4, 64, _v(256), _v(256), 1, _v(256), None,
+                                       None) == q.Q4Q8_E_ARG
+    # misaligned weight codes (16-byte rule) and scales (2-byte rule)
+    assert L.q8_0_quantize(_v(256), 4, 64, _v(264), _v(256), None) == q.Q4Q8_E_ALIGN
+    assert L.q8_0_quantize(_v(256), 4, 64, _v(256), _v(257), None) == q.Q4Q8_E_ALIGN
+    assert L.mul_mat_q8_0_q8(_v(264), _v(256), 4, 64, _v(256), _v(256), 1, _v(256), None) == q.Q4Q8_E_ALIGN
+    assert L.mul_mat_q8_0_q8_blocksums(_v(256), _v(256), 4, 64, _v(256), _v(256), 1, _v(256), _v(258),
+                                       None) == q.Q4Q8_E_ALIGN
+    # empty products are no-ops
+    assert L.mul_mat_q8_0_q8(None, None, 0, 64, None, None, 3, None, None) == q.Q4Q8_OK
+    assert L.mul_mat_q8_0_q8_blocksums(None, None, 5, 64, None, None, 0, None, None, None) == q.Q4Q8_OK
+    assert L.q8_0_quantize(None, 0, 64, None, None, None) == q.Q4Q8_OK
+
+
+def test_q8_0_binding_checks_shapes():
+    import torch
+    qw = torch.zeros((4, 64), dtype=torch.int8)
+    d = torch.zeros((4, 2), dtype=torch.int16)
+    xq = torch.zeros((2, 96), dtype=torch.int8)
+    xd = torch.zeros((2, 3), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        q.mul_mat_q8_0_q8(qw, d, xq, xd)
+    with pytest.raises((TypeError, ValueError)):
+        q.mul_mat_q8_0_q8(qw.to(torch.uint8), d, xq[:, :64].contiguous(), xd[:, :2].contiguous())
