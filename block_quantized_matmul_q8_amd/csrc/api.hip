@@ -473,6 +473,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   plan->prologue_offset = (plan->map_offset + tiles * (int64_t)sizeof(int32_t) + 15) / 16 * 16;
   plan->table_bytes = plan->prologue_offset + (int64_t)(inputs.size() * sizeof(q4q8::PrologueJob));
   plan->workspace_bytes = ws_total;
+  plan->weight_formats = 0;
+  for (const q4q8::GemvProblem& r : recs) plan->weight_formats |= 1 << r.wf;
   plan->magic = kGroupMagic;
   if (!table_host) return ok();
   const char* why = nullptr;
@@ -531,8 +533,13 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
       (!tiled && !q4q8::gemv_supported(1, plan->max_k, plan->B)) ||
       plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
       plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
-      plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob))
+      plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob) ||
+      plan->weight_formats < 1 || plan->weight_formats > 3)
     return fail(Q4Q8_E_ARG, "corrupt plan");
+  // the kernel instance: single-format groups take the leaner ones
+  const int wf = plan->weight_formats == 1   ? q4q8::kWeightQ4
+                 : plan->weight_formats == 2 ? q4q8::kWeightQ8
+                                             : q4q8::kWeightMixed;
   int st;
   if ((st = check_device())) return st;
   const char* base = static_cast<const char*>(table_dev);
@@ -551,13 +558,13 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
     g_counts[1].fetch_add(1, std::memory_order_relaxed);
     return launched(q4q8::launch_gemm(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                       reinterpret_cast<const int32_t*>(base + plan->map_offset), plan->n_windows,
-                                      plan->B, nullptr, s),
+                                      plan->B, nullptr, s, wf),
                     "mul_mat_q4q8_group (tiled)");
   }
   g_counts[0].fetch_add(1, std::memory_order_relaxed);
   return launched(q4q8::launch_gemv_table(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                           reinterpret_cast<const int32_t*>(base + plan->map_offset),
-                                          plan->n_windows, plan->max_k, plan->B, false, nullptr, s),
+                                          plan->n_windows, plan->max_k, plan->B, false, nullptr, s, wf),
                   "mul_mat_q4q8_group");
 }
 

@@ -137,6 +137,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 enum WeightFormat : int {
   kWeightQ4 = 0,
   kWeightQ8 = 1,
+  kWeightMixed = 2,  // grouped launches only: each record's wf decides
 };
 
 // One product of a (grouped) GEMV launch, as the kernel reads it.
@@ -184,12 +185,13 @@ static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
 // Rows per window (the unit a workgroup streams) for a product with K and B;
-// wf: weight format (WeightFormat).
+// wf: weight format (kWeightQ4 or kWeightQ8).
 Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B, int wf = kWeightQ4);
 // Persistent launch over the products of a device `table`, window w of the
 // launch belonging to record map[w]; or, when table == nullptr, over the
 // single record `p`.  `n_windows` = total windows; `max_k` = largest K among
-// the products (selects the kernel instance and the LDS size).
+// the products (selects the kernel instance and the LDS size).  wf: the weight
+// format of `p`, or of every table record (kWeightMixed: read per record).
 Q4Q8_HIDDEN hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table,
                                          const int32_t* map, int64_t n_windows, int64_t max_k,
                                          int64_t B, bool any_fused, int32_t* I, hipStream_t s,
@@ -213,7 +215,8 @@ Q4Q8_HIDDEN hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_
 Q4Q8_HIDDEN int64_t gemm_tiles(int64_t M, int64_t B);
 // Tiled route over the single record `p` (table == nullptr, n_tiles =
 // gemm_tiles(p.M, B)) or over the products of a device `table`, tile t of the
-// launch belonging to record tile_map[t] (its first tile is win_begin).
+// launch belonging to record tile_map[t] (its first tile is win_begin); wf as
+// for launch_gemv_table.
 Q4Q8_HIDDEN hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
                                    int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s,
                                    int wf = kWeightQ4);

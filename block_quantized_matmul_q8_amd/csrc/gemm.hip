@@ -274,8 +274,10 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
 }
 
 
-// Q8_0 and Q4 tiles share the LDS stage layout; a grouped launch takes each
-// product's weight format from its record (uniform over a workgroup).
+// Q8_0 and Q4 tiles share the LDS stage layout.  WF = kWeightMixed (grouped
+// only): each record's format decides, uniformly over a workgroup; that
+// instance holds both tile bodies, so uniform groups take the single-format
+// ones.
 template <bool WRITE_I, bool GROUPED, int WF = kWeightQ4>
 __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
@@ -294,12 +296,14 @@ __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     const int x = bid % kXcds, pos = bid / kXcds;
     L = ((pos / n_nt) * kXcds + x) * n_nt + pos % n_nt;
   }
-  if constexpr (GROUPED) {
+  if constexpr (GROUPED && WF == kWeightMixed) {
     const GemvProblem P = table[tile_map[L]];
     if (P.wf == kWeightQ8)
       gemm_tile<WRITE_I, kWeightQ8>(P, L, n_nt, B, st, Iout);
     else
       gemm_tile<WRITE_I, kWeightQ4>(P, L, n_nt, B, st, Iout);
+  } else if constexpr (GROUPED) {
+    gemm_tile<WRITE_I, WF>(table[tile_map[L]], L, n_nt, B, st, Iout);
   } else {
     gemm_tile<WRITE_I, WF>(p0, L, n_nt, B, st, Iout);
   }
@@ -310,26 +314,35 @@ int64_t gemm_tiles(int64_t M, int64_t B) { return ((M + kTM - 1) / kTM) * ((B + 
 hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
                        int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s, int wf) {
   const dim3 grid((unsigned)n_tiles), block(kGemmThreads);
-  if (wf == kWeightQ8 && !table) {
+  if (table) {
+    if (I) return hipErrorInvalidValue;
+    if (wf == kWeightQ4)
+      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    else if (wf == kWeightQ8)
+      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    else if (wf == kWeightMixed)
+      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightMixed>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    else
+      return hipErrorInvalidValue;
+  } else if (wf == kWeightQ4) {
+    if (I)
+      hipLaunchKernelGGL((gemm_kernel<true, false, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+    else
+      hipLaunchKernelGGL((gemm_kernel<false, false, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
+                         (int)n_tiles, (int)B, I);
+  } else if (wf == kWeightQ8) {
     if (I)
       hipLaunchKernelGGL((gemm_kernel<true, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
                          (int)n_tiles, (int)B, I);
     else
       hipLaunchKernelGGL((gemm_kernel<false, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
                          (int)n_tiles, (int)B, I);
-    return hipGetLastError();
-  }
-  if (wf != kWeightQ4 && !table) return hipErrorInvalidValue;
-  if (table) {  // weight format per record
-    if (I) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
-                       (int)B, I);
-  } else if (I) {
-    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
-                       (int)B, I);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, s, p, table, tile_map, (int)n_tiles,
-                       (int)B, I);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

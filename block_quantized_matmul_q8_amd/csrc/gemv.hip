@@ -36,10 +36,11 @@ enum GemvKind : int {
   kKindBlockSums = 3,  // one product, Q8 planes, per-block sums written out
 };
 
-// WF: weight format of the single-product kinds (a grouped launch takes each
-// product's format from its record; the folded prologue serves Q4 weights); a
-// Q8_0 block is two loads, so it keeps half the rows in flight for the same
-// bytes in flight.
+// WF: weight format of the products (kWeightMixed, grouped only: each
+// record's format decides; the folded prologue serves Q4 weights).  A Q8_0
+// block is two loads, so it keeps half the rows in flight for the same bytes
+// in flight.  A mixed instance holds both segments (the larger register
+// footprint of the two), so uniform groups take the single-format ones.
 template <int BT, int J, int S, int KIND, int WF = kWeightQ4>
 __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ win_map,
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
       const int wl0 = w - P.win_begin, wl1 = seg_end - P.win_begin;
       const GemvClass cls = gemv_class_of(P.K, BT);
       dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
-        if (P.wf == kWeightQ8)
+        if (WF == kWeightQ8 || (WF == kWeightMixed && P.wf == kWeightQ8))
           gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif_of(kWeightQ8), kWeightQ8>(
               P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
         else
@@ -145,7 +146,12 @@ template <int BT>
 static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
                             int64_t n_windows, int64_t max_k, int B, bool fold, int32_t* I, hipStream_t s,
                             int wf) {
-  if (table) return launch_kind<BT, 1, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+  if (table) {
+    if (wf == kWeightQ8) return launch_kind<BT, 1, 1, kKindGroup, kWeightQ8>(p, table, map, n_windows, B, 0, I, s);
+    if (wf == kWeightMixed)
+      return launch_kind<BT, 1, 1, kKindGroup, kWeightMixed>(p, table, map, n_windows, B, 0, I, s);
+    return launch_kind<BT, 1, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+  }
   if (wf == kWeightQ8) {
     if (fold) return hipErrorInvalidValue;
     const GemvClass c = gemv_class_of(max_k, B);
@@ -180,7 +186,8 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
 hipError_t launch_gemv_table(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
                              int64_t n_windows, int64_t max_k, int64_t B, bool any_fused, int32_t* I,
                              hipStream_t s, int wf) {
-  if (table && (any_fused || I)) return hipErrorInvalidValue;  // grouped: Q8 planes, format per record
+  if (table && (any_fused || I)) return hipErrorInvalidValue;  // grouped launches read Q8 planes
+  if (wf != kWeightQ4 && wf != kWeightQ8 && !(table && wf == kWeightMixed)) return hipErrorInvalidValue;
   if (gemv_class_of(max_k, B).J == 0) return hipErrorInvalidValue;
   switch (gemv_bt((int)B)) {
     case 1: return launch_bt<1>(p, table, map, n_windows, max_k, (int)B, any_fused, I, s, wf);

@@ -250,6 +250,8 @@ typedef struct q4q8_group_plan {
   int64_t prologue_offset; /* byte offset of the prologue records in the image */
   int64_t table_bytes;     /* size of the table image */
   int64_t workspace_bytes; /* device workspace the prologue pass writes (0 if none) */
+  int32_t weight_formats;  /* 1: all products Q4, 2: all Q8_0, 3: both (selects the kernel instance) */
+  int32_t reserved;
 } q4q8_group_plan;
 
 /* Validate n descriptors and fill the plan.  With table_host == NULL only the

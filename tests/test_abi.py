@@ -199,8 +199,9 @@ def test_struct_layouts_match_the_header(tmp_path):
     import subprocess
     src = tmp_path / "sz.c"
     src.write_text('#include "q4q8.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(q4q8_gemv_desc), sizeof(q4q8_group_plan),'
-                   ' offsetof(q4q8_gemv_desc, y), offsetof(q4q8_group_plan, workspace_bytes));return 0;}\n')
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(q4q8_gemv_desc), sizeof(q4q8_group_plan),'
+                   ' offsetof(q4q8_gemv_desc, y), offsetof(q4q8_group_plan, workspace_bytes),'
+                   ' offsetof(q4q8_group_plan, weight_formats));return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
@@ -208,6 +209,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     assert int(out[1]) == ctypes.sizeof(q.GroupPlan)
     assert int(out[2]) == q.GemvDesc.y.offset
     assert int(out[3]) == q.GroupPlan.workspace_bytes.offset
+    assert int(out[4]) == q.GroupPlan.weight_formats.offset
 
 
 def _desc(M=64, K=2048, qs=256, d=256, xq=256, xd=256, x=None, g=None, y=256, flags=0, eps=1e-5):
@@ -310,11 +312,14 @@ def test_group_build_q8_0_records():
     recs = image[:plan.map_offset].view(np.int32).reshape(3, 24)
     assert recs[:, 20].tolist() == [0, 1, 1]
     assert recs[:, 19].tolist() == [1, 2, 2] and plan.n_windows == 5
-    assert plan.n_prologue == 1
+    assert plan.n_prologue == 1 and plan.weight_formats == 3
     # the tiled route keeps the format too
     image, plan = _build([a, b], 300)
     recs = image[:plan.map_offset].view(np.int32).reshape(2, 24)
-    assert recs[:, 20].tolist() == [0, 1]
+    assert recs[:, 20].tolist() == [0, 1] and plan.weight_formats == 3
+    # uniform groups select the single-format instances
+    assert _build([a], 1)[1].weight_formats == 1
+    assert _build([b, _desc(M=0, flags=q.WEIGHTS_Q8_0)], 1)[1].weight_formats == 2
 
 
 def test_group_build_validation_is_host_only():
