@@ -371,6 +371,48 @@ def gemm_only(n, dev):
     print(f"[gemm-only] {n} grouped prefill launches, T={T}, {ops} int8 ops each", flush=True)
 
 
+def q8_0_only(n, dev):
+    """Launch sequence for profiler runs of the Q8_0 weight type: the
+    Llama-3-8B layer shapes as Q8_0, 4 layers; n grouped streaming launches at
+    B = 1 over the 28 products, then n grouped tiled launches at T = 2048 over
+    one layer's seven products (all on Q8 planes)."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    layer = wl.LLAMA_3_8B
+    mats = []
+    for l in range(4):
+        for mi, m in enumerate(layer):
+            w = wl.weight_device(3, l, mi, m.M, m.K, dev)
+            qw, d = q.q8_0_quantize(w)
+            del w
+            mats.append((m, qw, d))
+    for B in (1, 2048):
+        planes = {}
+        for slot, K in wl.slot_k(layer).items():
+            x = wl.activation_device(3, 0, slot, B, K, dev)
+            g = wl.norm_weight_device(3, 0, slot, K, dev)
+            planes[slot] = q.q8_quantize_rmsnorm(x, g, 1e-5)[:2]
+        use = mats if B == 1 else mats[:7]
+        ys = [torch.empty((B, m.M), dtype=torch.float32, device=dev) for m, _, _ in use]
+        grp = q.Group([{"qw": qw, "d": d, "y": y, "xq": planes[m.slot][0], "xd": planes[m.slot][1]}
+                       for (m, qw, d), y in zip(use, ys)], B=B)
+        torch.cuda.synchronize()
+        for _ in range(n):
+            grp()
+        torch.cuda.synchronize()
+        if B == 1:
+            nbytes = sum(q8_0_bytes(m.M, m.K) + m.K * 9 // 8 + m.M * 4 for m, _, _ in use)
+            print(f"[q8_0-only] {n} grouped decode launches, B=1, {len(use)} products, {nbytes} bytes each",
+                  flush=True)
+        else:
+            ops = 2 * B * sum(m.M * m.K for m in layer)
+            print(f"[q8_0-only] {n} grouped prefill launches, T={B}, {ops} int8 ops each", flush=True)
+        del grp, ys, planes
+
+
 def moe_only(n, dev):
     """Launch sequence for profiler runs of the routed MoE step (stacked
     gate/up and down routed calls on the 64-expert, 16-token, top-8 shape),
@@ -727,6 +769,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--gemm-only", type=int, default=0, metavar="N",
                     help="launch N grouped prefill GEMMs (T=2048, Llama-3-8B layer) and exit")
+    ap.add_argument("--q8-0-only", type=int, default=0, metavar="N",
+                    help="launch N grouped Q8_0 decode launches (B=1) and N grouped Q8_0 prefill launches, and exit")
     ap.add_argument("--moe-only", type=int, default=0, metavar="N",
                     help="launch N routed MoE steps and exit")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
@@ -761,6 +805,9 @@ def main():
         return
     if args.moe_only:
         moe_only(args.moe_only, dev)
+        return
+    if args.q8_0_only:
+        q8_0_only(args.q8_0_only, dev)
         return
     report = {}
     model = bench_decode_1b(args, dev, report)
