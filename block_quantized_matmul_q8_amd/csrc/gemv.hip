@@ -65,10 +65,11 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
       const GemvClass cls = gemv_class_of(P.K, BT);
       dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
         if (WF == kWeightQ8 || (WF == kWeightMixed && P.wf == kWeightQ8))
-          gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif_of(kWeightQ8), kWeightQ8>(
+          gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif(BT, kWeightQ8), kWeightQ8>(
               P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
         else
-          gemv_segment<BT, JJ, SS, false, false>(P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
+          gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif(BT, kWeightQ4)>(
+              P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
       });
       w = seg_end;
       P = Pn;
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
     }
   } else {
     if (w_begin < w_end)
-      gemv_segment<BT, J, S, FOLD, WRITE_I, DenseCols, gemv_rif_of(WF), WF>(p0, DenseCols(p0), B, w_begin, w_end, smem,
-                                                                            &split, parity, Iout);
+      gemv_segment<BT, J, S, FOLD, WRITE_I, DenseCols, gemv_rif(BT, WF), WF>(p0, DenseCols(p0), B, w_begin, w_end,
+                                                                             smem, &split, parity, Iout);
   }
 }
 
@@ -97,12 +98,12 @@ bool gemv_supported(int64_t M, int64_t K, int64_t B) {
 
 bool gemv_fused_supported(int64_t K, int64_t B) {
   const GemvClass c = gemv_class_of(K, B);
-  return c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;
+  return B <= 4 && c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;
 }
 
 int gemv_window_rows(int64_t K, int64_t B, int wf) {
   if (B < 1 || B > 8) return 0;
-  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif_of(wf));
+  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif(gemv_bt((int)B), wf));
 }
 
 // Workgroups that can be resident at once for one kernel instance and LDS

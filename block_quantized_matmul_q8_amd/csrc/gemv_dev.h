@@ -83,9 +83,12 @@ __device__ __forceinline__ int code_sum8(const i32x4 a, const i32x4 b) {
 #define Q4Q8_GEMV_ROWS_IN_FLIGHT 16  // 16-byte loads per lane in flight per row group
 #endif
 
-// Rows in flight of a weight format: a Q8_0 block takes two 16-byte loads
-// per lane, so half the rows keep the same bytes in flight.
-__host__ __device__ constexpr int gemv_rif_of(int wf) {
+// 16-byte loads per lane in flight per row group for column width BT and
+// weight format wf: a Q8_0 block takes two loads per lane, so half the rows
+// keep the same bytes in flight.  (Raising it for 3..8 columns costs the
+// second workgroup per CU and measured slower at every width.)
+__host__ __device__ constexpr int gemv_rif(int BT, int wf) {
+  (void)BT;
   return wf == kWeightQ8 ? Q4Q8_GEMV_ROWS_IN_FLIGHT / 2 : Q4Q8_GEMV_ROWS_IN_FLIGHT;
 }
 
@@ -95,9 +98,11 @@ __host__ __device__ constexpr int gemv_bt(int B) { return B <= 1 ? 1 : B <= 2 ? 
 // Activation blocks (columns x blocks per lane) a lane may hold.
 __host__ __device__ constexpr int gemv_act_budget(int BT) { return BT <= 4 ? 8 : 16; }
 
-// Rows a wave keeps in flight per group for BT columns and J blocks per lane.
+// Rows a wave keeps in flight per group for BT columns and J blocks per lane
+// (at least 1; at most 64 / BT, so a group's outputs fit one value per lane).
 __host__ __device__ constexpr int gemv_rows_per_wave(int BT, int J, int rif = Q4Q8_GEMV_ROWS_IN_FLIGHT) {
-  return rif / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) > 0 ? rif / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4) : 1;
+  const int r = rif / J / (BT <= 2 ? 1 : BT <= 4 ? 2 : 4);
+  return r < 1 ? 1 : r > 64 / BT ? 64 / BT : r;
 }
 
 // Register blocking class of a product: J blocks per lane, K split over S

@@ -370,6 +370,7 @@ def test_fused_single_validation():
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, None, f, 0, 1, p, None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, ctypes.c_void_p(260), p, f, 0, 1, p, None) == q.Q4Q8_E_ALIGN
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 16384, p, p, f, 0, 4, p, None) == q.Q4Q8_E_UNSUPPORTED
+    assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, p, f, 0, 5, p, None) == q.Q4Q8_E_UNSUPPORTED  # B <= 4
     assert L.mul_mat_q4q8_rmsnorm(p, p, 8, 64, p, p, f, 2, 1, p, None) == q.Q4Q8_E_ARG
 
 
