@@ -413,6 +413,27 @@ def q8_0_only(n, dev):
         del grp, ys, planes
 
 
+def moe_weight_copies(dev, n_copies=4):
+    """n_copies independent sets of the MoE expert weights (stacked gate/up
+    [E][2 x 1408][2048] and down [E][2048][1408], 311 MB per set): steps
+    rotate over them, so the 256 MB last-level cache cannot serve a step from
+    the previous one."""
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    cfg = wl.MOE
+    copies = []
+    for c in range(n_copies):
+        qsd = []
+        for i, (M, K) in enumerate(((2 * cfg.ffn, cfg.hidden), (cfg.hidden, cfg.ffn))):
+            w = wl.weight_device(3 + 16 * c, 0, i, cfg.E * M, K, dev)
+            qs, d = q.q4_quantize(w)
+            del w
+            qsd.append((qs.view(cfg.E, M, K // 2), d.view(cfg.E, M, K // 32)))
+        copies.append(qsd)
+    return copies
+
+
 def moe_only(n, dev):
     """Launch sequence for profiler runs of the routed MoE step (stacked
     gate/up and down routed calls on the 64-expert, 16-token, top-8 shape),
@@ -424,24 +445,21 @@ def moe_only(n, dev):
 
     cfg = wl.MOE
     ids = torch.from_numpy(wl.expert_ids(0, cfg.T, cfg.E, cfg.top_k)).to(dev)
+    copies = moe_weight_copies(dev)
     calls = []
     for i, (M, K, S) in enumerate(((2 * cfg.ffn, cfg.hidden, 1), (cfg.hidden, cfg.ffn, cfg.top_k))):
-        w = wl.weight_device(3, 0, i, cfg.E * M, K, dev)
-        qs, d = q.q4_quantize(w)
-        del w
         x = wl.activation_device(3, 0, i, cfg.T * S, K, dev)
         g = wl.norm_weight_device(3, 0, i, K, dev)
         xq, xd, _ = q.q8_quantize_rmsnorm(x, g, 1e-5)
         y = torch.empty((cfg.T, cfg.top_k, M), dtype=torch.float32, device=dev)
         ws = torch.empty(q.mul_mat_id_q4q8_workspace(cfg.E, cfg.T, cfg.top_k), dtype=torch.uint8, device=dev)
-        calls.append((qs.view(cfg.E, M, K // 2), d.view(cfg.E, M, K // 32), xq.view(cfg.T, S, K),
-                      xd.view(cfg.T, S, K // 32), y, ws))
+        calls.append((xq.view(cfg.T, S, K), xd.view(cfg.T, S, K // 32), y, ws))
     torch.cuda.synchronize()
-    for _ in range(n):
-        for qs, d, xq, xd, y, ws in calls:
+    for step in range(n):
+        for (qs, d), (xq, xd, y, ws) in zip(copies[step % len(copies)], calls):
             q.mul_mat_id_q4q8(qs, d, xq, xd, ids, y=y, ws=ws)
     torch.cuda.synchronize()
-    print(f"[moe-only] {n} MoE steps (2 routed calls each)", flush=True)
+    print(f"[moe-only] {n} MoE steps (2 routed calls each, rotating {len(copies)} weight copies)", flush=True)
 
 
 def pmc_summary(fetch_dir, write_dir):
@@ -690,30 +708,30 @@ def bench_moe(args, dev):
 
     cfg = wl.MOE
     ids = torch.from_numpy(wl.expert_ids(0, cfg.T, cfg.E, cfg.top_k)).to(dev)
+    copies = moe_weight_copies(dev)
     mats = []
-    for name, M, K, S in (("gate_up", 2 * cfg.ffn, cfg.hidden, 1), ("down", cfg.hidden, cfg.ffn, cfg.top_k)):
-        w = wl.weight_device(3, 0, len(mats), cfg.E * M, K, dev)
-        qs, d = q.q4_quantize(w)
-        del w
-        x = wl.activation_device(3, 0, len(mats), cfg.T * S, K, dev)
-        gw = wl.norm_weight_device(3, 0, len(mats), K, dev)
+    for i, (M, K, S) in enumerate(((2 * cfg.ffn, cfg.hidden, 1), (cfg.hidden, cfg.ffn, cfg.top_k))):
+        x = wl.activation_device(3, 0, i, cfg.T * S, K, dev)
+        gw = wl.norm_weight_device(3, 0, i, K, dev)
         xq, xd, _ = q.q8_quantize_rmsnorm(x, gw, 1e-5)
         y = torch.empty((cfg.T, cfg.top_k, M), dtype=torch.float32, device=dev)
         ws = torch.empty(q.mul_mat_id_q4q8_workspace(cfg.E, cfg.T, cfg.top_k), dtype=torch.uint8, device=dev)
-        mats.append((qs.view(cfg.E, M, K // 2), d.view(cfg.E, M, K // 32), xq.view(cfg.T, S, K),
-                     xd.view(cfg.T, S, K // 32), y, ws, M, K, S))
+        mats.append((xq.view(cfg.T, S, K), xd.view(cfg.T, S, K // 32), y, ws, M, K, S))
+    step = [0]
 
     def fn():
-        for qs, d, xq, xd, y, ws, M, K, S in mats:
+        qsd = copies[step[0] % len(copies)]
+        step[0] += 1
+        for (qs, d), (xq, xd, y, ws, M, K, S) in zip(qsd, mats):
             q.mul_mat_id_q4q8(qs, d, xq, xd, ids, y=y, ws=ws)
-    ms, _ = time_direct(fn, max(5, args.steps // 2), 2)
+    ms, _ = time_direct(fn, max(8, args.steps // 2), 4)
     distinct = len(set(ids.cpu().numpy().ravel().tolist()))
     nbytes = 0
-    for qs, d, xq, xd, y, ws, M, K, S in mats:
+    for xq, xd, y, ws, M, K, S in mats:
         nbytes += distinct * q4_bytes(M, K) + cfg.T * S * K * 9 // 8 + cfg.T * cfg.top_k * M * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     # the weighted expert-plane sum of the down projection's planes
-    y_down = mats[1][4]
+    y_down = mats[1][2]
     w = torch.from_numpy(wl.expert_weights(0, cfg.T, cfg.top_k)).to(dev)
     out = torch.empty((cfg.T, cfg.hidden), dtype=torch.float32, device=dev)
     ms_sum = per_launch_ms(lambda: q.moe_expert_sum_f32(y_down, w, out=out), 20)
@@ -721,6 +739,7 @@ def bench_moe(args, dev):
     return {"GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
             "distinct_experts": distinct, "bytes": nbytes,
             "launches": "2 routed calls (stacked gate/up, down), each a routing kernel + a streaming kernel",
+            "weight_copies": len(copies),
             "expert_sum": {"us": round(ms_sum * 1e3, 2), "GB/s": round(sum_bytes / (ms_sum * 1e-3) / 1e9, 1),
                            "bytes": sum_bytes,
                            "what": "weighted in-order sum of the down projection's 8 expert planes, "

@@ -56,7 +56,7 @@ SHAPES = [
     (64, 14336, 2), (40, 16384, 4), (70, 8224, 3), (50, 14336, 8),   # GEMV route, K split over waves
     (3, 32768, 1), (5, 65536, 1), (40, 32768, 2),
     (130, 1408, 9), (1000, 2048, 33), (257, 4096, 130), (64, 14336, 16),
-    (128, 64, 128), (1, 32, 200),                                    # GEMM route
+    (128, 64, 128), (1, 32, 200), (77, 8224, 20),                    # GEMM route (K = 8224: a 1-block last stage)
 ]
 
 

@@ -72,7 +72,7 @@ SHAPES = [
     (64, 14336, 2), (40, 16384, 4), (70, 8224, 3), (50, 14336, 8),   # streaming route, K split over waves
     (3, 32768, 1), (5, 65536, 1), (40, 32768, 2),
     (130, 1408, 9), (1000, 2048, 33), (257, 4096, 130), (64, 14336, 16),
-    (128, 64, 128), (1, 32, 200),                                    # tiled route
+    (128, 64, 128), (1, 32, 200), (77, 8224, 20),                    # tiled route (K = 8224: a 1-block last stage)
 ]
 
 
@@ -231,3 +231,55 @@ def test_group_mixes_weight_formats(B):
             y1 = q.mul_mat_q4q8(p["qs"], p["d"], xq_d, xd_d)
         torch.cuda.synchronize()
         assert np.array_equal(y1.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32)), i
+
+
+@pytest.mark.parametrize("B", [2, 8])
+def test_mixed_group_in_a_graph(B):
+    """A group mixing Q4 and Q8_0 products, some on fp32 rows (prologue pass),
+    captured in a HIP graph; every replay, with eager launches of the same
+    group in between, equals the eager result bit for bit, which matches the
+    oracle."""
+    dev = torch.device("cuda:0")
+    shapes = [(1024, 4096), (512, 14336), (2048, 2048), (300, 4096)]
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        w = workloads.weight(61, 0, i, M, K)
+        x = workloads.activation(61, 0, i % 2, B, K)
+        g = workloads.norm_weight(61, 0, i % 2, K)
+        xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+        p = {"y": torch.zeros((B, M), dtype=torch.float32, device=dev)}
+        if i % 2 == 0:
+            qw, d = oracle.q8w_quantize(w)
+            p["qw"] = to_dev(qw)
+            refs.append(oracle.mul_mat_q8w(qw, d, xq_o, xd_o, nthreads=NTHREADS, want_y64=False)[0])
+        else:
+            qs, d = oracle.q4_quantize(w)
+            p["qs"] = to_dev(qs)
+            refs.append(oracle.mul_mat(qs, d, xq_o, xd_o, nthreads=NTHREADS, want_y64=False)[0])
+        p["d"] = to_dev(d.view(np.int16))
+        p.update(x=to_dev(x), g=to_dev(g), eps=workloads.RMS_EPS)
+        probs.append(p)
+    grp = q.Group(probs, B=B)
+    assert grp.plan.weight_formats == 3
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        grp()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [p["y"].cpu().numpy().copy() for p in probs]
+    for i, (y, ref) in enumerate(zip(eager, refs)):
+        assert_close(y, ref, f"eager product {i}")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp()
+    for rep in range(3):
+        for p in probs:
+            p["y"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (p, y) in enumerate(zip(probs, eager)):
+            assert np.array_equal(p["y"].cpu().numpy().view(np.uint32), y.view(np.uint32)), (rep, i)
+        grp()                      # eager work between replays
+        torch.cuda.synchronize()
