@@ -153,9 +153,15 @@ Q4Q8_EXPORT const char* q4q8_last_error(void) { return g_err; }
 
 Q4Q8_EXPORT int q4q8_version(void) { return 100; }
 
+// One thread per 32-block: the launch grid must stay within 2^31 workgroups.
+static int check_blocks(int64_t M, int64_t K) {
+  if (M * (K / q4q8::kQK) > ((int64_t)1 << 38)) return fail(Q4Q8_E_ARG, "matrix too large (M * K / 32 > 2^38)");
+  return Q4Q8_OK;
+}
+
 Q4Q8_EXPORT int q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs, uint16_t* d, void* stream) {
   int st;
-  if ((st = check_k(K)) || (st = check_dims(M, 1))) return st;
+  if ((st = check_k(K)) || (st = check_dims(M, 1)) || (st = check_blocks(M, K))) return st;
   if (M == 0) return ok();
   if (!w || !qs || !d) return fail(Q4Q8_E_ARG, "null pointer argument");
   if (!aligned(w, 16) || !aligned(qs, 16) || !aligned(d, 2)) return fail(Q4Q8_E_ALIGN, "w/qs must be 16-byte aligned, d 2-byte");
@@ -233,7 +239,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_blocksums(const uint8_t* qs, const uint16_t* d, int
 
 Q4Q8_EXPORT int q8_0_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, void* stream) {
   int st;
-  if ((st = check_k(K)) || (st = check_dims(M, 1))) return st;
+  if ((st = check_k(K)) || (st = check_dims(M, 1)) || (st = check_blocks(M, K))) return st;
   if (M == 0) return ok();
   if (!w || !qw || !d) return fail(Q4Q8_E_ARG, "null pointer argument");
   if (!aligned(w, 16) || !aligned(qw, 16) || !aligned(d, 2))

@@ -83,7 +83,7 @@ int q4q8_version(void);
  * section "构建开关如何变成运行时能力", places weight re-layout at load time;
  * this call is where the kernel-friendly SoA planes are produced.)
  *   w  [M][K] f32, 16-byte aligned      qs [M][K/2] u8, 16-byte aligned
- *   d  [M][K/32] u16, 2-byte aligned
+ *   d  [M][K/32] u16, 2-byte aligned     M * K / 32 <= 2^38 (else Q4Q8_E_ARG)
  */
 int q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs, uint16_t* d, void* stream);
 
@@ -165,7 +165,7 @@ int mul_mat_q4q8(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, con
  * q = roundf(fl(w * id)) clamped to [-127, 127]) with codes from the fp32 d
  * and the stored scale fp16(d), nearest even.
  *   w  [M][K] f32, 16-byte aligned      qw [M][K] i8, 16-byte aligned
- *   d  [M][K/32] u16, 2-byte aligned
+ *   d  [M][K/32] u16, 2-byte aligned     M * K / 32 <= 2^38 (else Q4Q8_E_ARG)
  */
 int q8_0_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, void* stream);
 

@@ -381,6 +381,10 @@ def test_q8_0_entry_points_validate():
     assert L.q8_0_quantize(_v(256), -1, 64, _v(256), _v(256), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q8_0_q8(_v(256), _v(256), 4, 33, _v(256), _v(256), 1, _v(256), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q8_0_q8(_v(256), _v(256), 4, 64, _v(256), _v(256), -2, _v(256), None) == q.Q4Q8_E_ARG
+    # a grid past 2^31 workgroups is refused on the host
+    assert L.q8_0_quantize(_v(256), 1 << 30, 1 << 14, _v(256), _v(256), None) == q.Q4Q8_E_ARG
+    assert L.q4_quantize(_v(256), 1 << 30, 1 << 14, _v(256), _v(256), None) == q.Q4Q8_E_ARG
+    assert "too large" in q.q4q8_last_error()
     # null pointers
     assert L.q8_0_quantize(None, 4, 64, _v(256), _v(256), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q8_0_q8(None, _v(256), 4, 64, _v(256), _v(256), 1, _v(256), None) == q.Q4Q8_E_ARG
