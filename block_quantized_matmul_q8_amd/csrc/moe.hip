@@ -14,6 +14,8 @@
 //   sel lists the selected experts in expert order, costp the prefix of their
 //   streaming costs (costp[i] = cost of sel[0..i)); ctl[0] is their number.
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "gemv_dev.h"
 
@@ -41,11 +43,12 @@ __host__ __device__ inline int moe_window_cost(int c) {
   return cost;
 }
 
-// In-place exclusive scan of v[0..count) by all kRouteThreads threads, total
-// into v[count]: a contiguous chunk per thread, a shuffle scan within each
-// wave, one thread over the wave totals (wave_tot: kRouteThreads / 64 ints).
+// In-place exclusive scan of v[0..count) by all NT threads, total into
+// v[count]: a contiguous chunk per thread, a shuffle scan within each wave,
+// one thread over the wave totals (wave_tot: NT / 64 ints).
+template <int NT>
 __device__ void block_exclusive_scan(int* v, int count, int* wave_tot, int tid) {
-  const int per = (count + kRouteThreads - 1) / kRouteThreads;
+  const int per = (count + NT - 1) / NT;
   const int lo = min(count, tid * per), hi = min(count, lo + per);
   int sum = 0;
   for (int e = lo; e < hi; ++e) sum += v[e];
@@ -60,7 +63,7 @@ __device__ void block_exclusive_scan(int* v, int count, int* wave_tot, int tid) 
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int w = 0; w < kRouteThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
       const int c = wave_tot[w];
       wave_tot[w] = run;
       run += c;
@@ -77,48 +80,44 @@ __device__ void block_exclusive_scan(int* v, int count, int* wave_tot, int tid) 
   __syncthreads();
 }
 
-// Routing: one workgroup.  Pass 1 reads every id once: a valid pair takes
-// its rank within its expert (LDS atomics), an invalid one is written to the
-// tail of `list` (valid pairs fill it from the front, so the two never
-// meet).  Block scans give the per-expert offsets, the selected experts'
-// indices and the prefix of their streaming costs; the pairs are scattered
-// into the
-// grouped list, and the rows of invalid pairs are filled with quiet NaNs.
-// LDS: counts, selected indices, cost prefix (E + 1 each) | wave totals.
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int n_win, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ list, int32_t* __restrict__ rank, int32_t* __restrict__ sel,
-    int32_t* __restrict__ costp, int32_t* __restrict__ ctl, int M, float* __restrict__ y) {
-  extern __shared__ int lds[];
-  int* cnt = lds;                                // E + 1: counts, then offsets
-  int* sidx = cnt + E + 1;                       // E + 1: selected index
-  int* cpre = sidx + E + 1;                      // E + 1: cost prefix
-  int* wave_tot = cpre + E + 1;                  // kRouteThreads / 64
-  __shared__ int n_bad;
+// Routing by one workgroup of NT threads.  Pass 1 reads every id once: a
+// valid pair takes its rank within its expert (LDS atomics), an invalid one
+// is written to the tail of `list` (valid pairs fill it from the front, so
+// the two never meet).  Block scans give the per-expert offsets, the selected
+// experts' indices and the prefix of their streaming costs; the pairs are
+// scattered into the grouped list, and (when nan_rows) the rows of invalid
+// pairs are filled with quiet NaNs.  cnt, sidx, cpre: E + 1 ints of LDS each,
+// wave_tot NT / 64, n_bad one; the outputs (offsets .. ctl, the workspace
+// layout above) may live in LDS or global memory.
+template <int NT>
+__device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n, int E, int n_win, int* cnt,
+                                          int* sidx, int* cpre, int* wave_tot, int* n_bad, int32_t* offsets,
+                                          int32_t* list, int32_t* rank, int32_t* sel, int32_t* costp,
+                                          int32_t* ctl, bool nan_rows, int M, float* __restrict__ y) {
   const int tid = threadIdx.x;
-  for (int e = tid; e <= E; e += kRouteThreads) cnt[e] = 0;
-  if (tid == 0) n_bad = 0;
+  for (int e = tid; e <= E; e += NT) cnt[e] = 0;
+  if (tid == 0) *n_bad = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kRouteThreads) {
+  for (int i = tid; i < n; i += NT) {
     const int e = ids[i];
     if (e >= 0 && e < E)
       rank[i] = atomicAdd(&cnt[e], 1);
     else
-      list[n - 1 - atomicAdd(&n_bad, 1)] = i;
+      list[n - 1 - atomicAdd(n_bad, 1)] = i;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) {
+  for (int e = tid; e < E; e += NT) {
     const int c = cnt[e];
     sidx[e] = c > 0 ? 1 : 0;
     cpre[e] = c > 0 ? n_win * moe_window_cost(c) : 0;
   }
   __syncthreads();
-  block_exclusive_scan(cnt, E, wave_tot, tid);
-  block_exclusive_scan(sidx, E, wave_tot, tid);
-  block_exclusive_scan(cpre, E, wave_tot, tid);
-  for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = cnt[e];
+  block_exclusive_scan<NT>(cnt, E, wave_tot, tid);
+  block_exclusive_scan<NT>(sidx, E, wave_tot, tid);
+  block_exclusive_scan<NT>(cpre, E, wave_tot, tid);
+  for (int e = tid; e <= E; e += NT) offsets[e] = cnt[e];
   // Selected experts in expert order with the prefix of their costs.
-  for (int e = tid; e < E; e += kRouteThreads) {
+  for (int e = tid; e < E; e += NT) {
     if (cnt[e + 1] > cnt[e]) {
       sel[sidx[e]] = e;
       costp[sidx[e]] = cpre[e];
@@ -128,17 +127,40 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     costp[sidx[E]] = cpre[E];
     ctl[0] = sidx[E];
   }
-  for (int i = tid; i < n; i += kRouteThreads) {
+  for (int i = tid; i < n; i += NT) {
     const int e = ids[i];
     if (e >= 0 && e < E) list[cnt[e] + rank[i]] = i;
   }
-  // Pairs with an id outside [0, E) get a row of quiet NaNs.
-  const float qnan = __builtin_bit_cast(float, 0x7FC00000u);
-  const int nb_bad = n_bad;
-  for (int k = 0; k < nb_bad; ++k) {
-    const int64_t row = (int64_t)list[n - 1 - k] * M;
-    for (int m = tid; m < M; m += kRouteThreads) y[row + m] = qnan;
+  if (nan_rows) {
+    // Pairs with an id outside [0, E) get a row of quiet NaNs.
+    const float qnan = __builtin_bit_cast(float, 0x7FC00000u);
+    const int nb_bad = *n_bad;
+    for (int k = 0; k < nb_bad; ++k) {
+      const int64_t row = (int64_t)list[n - 1 - k] * M;
+      for (int m = tid; m < M; m += NT) y[row + m] = qnan;
+    }
   }
+}
+
+// The routing as its own launch (one workgroup), results in the workspace.
+// LDS: counts, selected indices, cost prefix (E + 1 each) | wave totals.
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int n_win, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ list, int32_t* __restrict__ rank, int32_t* __restrict__ sel,
+    int32_t* __restrict__ costp, int32_t* __restrict__ ctl, int M, float* __restrict__ y) {
+  extern __shared__ int lds[];
+  __shared__ int n_bad;
+  moe_route<kRouteThreads>(ids, n, E, n_win, lds, lds + E + 1, lds + 2 * (E + 1), lds + 3 * (E + 1), &n_bad,
+                           offsets, list, rank, sel, costp, ctl, true, M, y);
+}
+
+// Small routings (few experts and pairs) run inside every workgroup of the
+// streaming launch instead, in LDS: one launch per call instead of two.
+// LDS ints: cnt, sidx, cpre, offsets, costp (E + 1 each), sel (E), list,
+// rank (n each), wave totals (kGemvThreads / 64), n_bad, ctl.
+constexpr int kFusedRouteMaxInts = 4096;
+__host__ __device__ constexpr int64_t moe_fused_route_ints(int64_t E, int64_t n) {
+  return 5 * (E + 1) + E + 2 * n + kGemvThreads / 64 + 2;
 }
 
 // 16-byte weight loads each lane keeps in flight per row group, per column
@@ -181,14 +203,44 @@ static int moe_window_rows(int64_t K) {
 // time, each pass with the narrowest column width that holds it.
 // KMAX: the band of K (moe_band), so each instance compiles four segment
 // variants only.
-template <int KMAX>
+// FUSED: the workgroup first routes the ids itself (moe_route in LDS;
+// workgroup 0 also fills the NaN rows), else the routing comes from the
+// workspace written by moe_route_kernel.
+template <int KMAX, bool FUSED>
 __global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
     const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int M, int K,
     const int8_t* __restrict__ xq, const float* __restrict__ xd, int per_slot, int top_k,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ list, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ costp, const int32_t* __restrict__ ctl, float* __restrict__ y, int n_win,
-    int unit) {
+    const int32_t* __restrict__ g_offsets, const int32_t* __restrict__ g_list, const int32_t* __restrict__ g_sel,
+    const int32_t* __restrict__ g_costp, const int32_t* __restrict__ g_ctl, float* __restrict__ y, int n_win,
+    int unit, const int32_t* __restrict__ ids, int n, int E) {
   __shared__ SplitScratch split;
+  extern __shared__ int rl[];
+  const int32_t* offsets = g_offsets;
+  const int32_t* list = g_list;
+  const int32_t* sel = g_sel;
+  const int32_t* costp = g_costp;
+  const int32_t* ctl = g_ctl;
+  if constexpr (FUSED) {
+    int* cnt = rl;
+    int* sidx = cnt + E + 1;
+    int* cpre = sidx + E + 1;
+    int* l_off = cpre + E + 1;
+    int* l_costp = l_off + E + 1;
+    int* l_sel = l_costp + E + 1;
+    int* l_list = l_sel + E;
+    int* l_rank = l_list + n;
+    int* wave_tot = l_rank + n;
+    int* n_bad = wave_tot + kGemvThreads / 64;
+    int* l_ctl = n_bad + 1;
+    moe_route<kGemvThreads>(ids, n, E, n_win, cnt, sidx, cpre, wave_tot, n_bad, l_off, l_list, l_rank, l_sel,
+                            l_costp, l_ctl, blockIdx.x == 0, M, y);
+    __syncthreads();
+    offsets = l_off;
+    list = l_list;
+    sel = l_sel;
+    costp = l_costp;
+    ctl = l_ctl;
+  }
   const int lane = threadIdx.x & 63;
   const int nb = K >> 5;
   const int n_sel = ctl[0];
@@ -261,6 +313,27 @@ __global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
   }
 }
 
+// Workgroups of a streaming instance resident at once (per CU times CUs),
+// queried once per instance and device with the largest fused-routing LDS.
+static int64_t moe_resident_workgroups(const void* kernel) {
+  static std::mutex mu;
+  static std::vector<std::pair<std::pair<const void*, int>, int64_t>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& e : cache)
+    if (e.first.first == kernel && e.first.second == dev) return e.second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemvThreads,
+                                                   (size_t)kFusedRouteMaxInts * sizeof(int)) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int64_t n = (int64_t)per_cu * cus;
+  cache.push_back({{kernel, dev}, n});
+  return n;
+}
+
 int64_t moe_schedule_cost_bound(int64_t E, int64_t M, int64_t K, int64_t n) {
   const int unit = moe_window_rows(K);
   const int64_t n_win = (M + unit - 1) / unit;
@@ -279,37 +352,35 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
   int32_t* ctl = costp + E + 1;
   const int unit = moe_window_rows(K);
   const int64_t n_win = (M + unit - 1) / unit;
-  const size_t route_lds = (3 * ((size_t)E + 1) + kRouteThreads / 64) * sizeof(int);
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)n_win,
-                     offsets, list, rank, sel, costp, ctl, (int)M, y);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // (the widest band keeps the separate routing launch: its instance has no
+  // registers to spare for the fused routing)
+  const bool fused = moe_fused_route_ints(E, n) <= kFusedRouteMaxInts && moe_band(K) <= 8192;
+  const size_t fused_lds = fused ? (size_t)moe_fused_route_ints(E, n) * sizeof(int) : 0;
+  if (!fused) {
+    const size_t route_lds = (3 * ((size_t)E + 1) + kRouteThreads / 64) * sizeof(int);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)n_win,
+                       offsets, list, rank, sel, costp, ctl, (int)M, y);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   auto go = [&](auto kernel) {
-    static std::mutex mu;
-    static int resident = 0;
-    {
-      std::lock_guard<std::mutex> lk(mu);
-      if (resident == 0) {
-        int per_cu = 0, cus = 0, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, kGemvThreads, 0) !=
-                hipSuccess || per_cu < 1)
-          per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-          cus = 256;
-        resident = per_cu * cus;
-      }
-    }
-    int64_t grid = resident;
+    int64_t grid = moe_resident_workgroups((const void*)kernel);
     if (grid > E * n_win) grid = E * n_win;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kGemvThreads), 0, s, qs, d, (int)M, (int)K, xq, xd,
-                       n_x_slots == 1 ? 0 : 1, (int)top_k, offsets, list, sel, costp, ctl, y, (int)n_win, unit);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kGemvThreads), fused_lds, s, qs, d, (int)M, (int)K, xq,
+                       xd, n_x_slots == 1 ? 0 : 1, (int)top_k, offsets, list, sel, costp, ctl, y, (int)n_win, unit,
+                       ids, n, (int)E);
+  };
+  auto band = [&](auto k_fused, auto k_ws) {
+    if (fused)
+      go(k_fused);
+    else
+      go(k_ws);
   };
   switch (moe_band(K)) {
-    case 2048: go(moe_stream_kernel<2048>); break;
-    case 4096: go(moe_stream_kernel<4096>); break;
-    case 8192: go(moe_stream_kernel<8192>); break;
-    case 16384: go(moe_stream_kernel<16384>); break;
+    case 2048: band(moe_stream_kernel<2048, true>, moe_stream_kernel<2048, false>); break;
+    case 4096: band(moe_stream_kernel<4096, true>, moe_stream_kernel<4096, false>); break;
+    case 8192: band(moe_stream_kernel<8192, true>, moe_stream_kernel<8192, false>); break;
+    case 16384: go(moe_stream_kernel<16384, false>); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

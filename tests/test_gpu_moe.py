@@ -65,6 +65,26 @@ def test_bad_ids_give_nan_rows():
     _check_rows(y, y_o, ids, E)
 
 
+@pytest.mark.parametrize("E", [40, 900])
+def test_routing_in_launch_and_separate(E):
+    """Small routings run inside every workgroup of the streaming launch;
+    larger ones (here 900 experts) take the separate routing launch.  Both,
+    on ids that select the same experts (plus invalid ids), against the
+    oracle."""
+    M, K, T, top_k = 70, 512, 9, 4
+    _, qs40, d40 = _experts(37, 40, M, K)
+    qs = np.zeros((E, M, K // 2), np.uint8)
+    d = np.zeros((E, M, K // 32), np.uint16)
+    qs[:40], d[:40] = qs40, d40
+    xq, xd = _acts(37, T, top_k, K)
+    ids = workloads.expert_ids(37, T, 40, top_k)
+    ids[2, 1] = E
+    ids[6, 3] = -1
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(y, y_o, ids, E)
+
+
 def test_single_expert_reduces_to_mul_mat():
     E, M, K, T = 1, 96, 1408, 7
     _, qs, d = _experts(33, E, M, K)
