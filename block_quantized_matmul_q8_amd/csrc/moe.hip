@@ -166,13 +166,19 @@ __host__ __device__ constexpr int64_t moe_fused_route_ints(int64_t E, int64_t n)
 // 16-byte weight loads each lane keeps in flight per row group, per column
 // width (1, 2, 4, 8 routed pairs per pass) and K band.  One kernel instance
 // holds the segments of all four widths, so its register allocation is the
-// largest of theirs: 8 / 8 / 16 / 16 measured fastest for the 2048 band (the
-// wider passes need more bytes in flight, the narrow ones are held back by the
-// wide ones' registers), and the 16384 band keeps width 4 at 8 so that its
-// instance stays free of scratch spills.
+// largest of theirs.  The 2048 band takes 8 / 8 / 16 / 8, which fits two
+// workgroups per CU (245 VGPRs) and measured fastest: 4.1 TB/s for the MoE
+// step against 3.6 with 16 at width 8 and one workgroup per CU, 3.0 with 8 at
+// width 4 (one per CU) and 3.3 with 4 at width 8.  The larger bands take
+// 8 / 8 / 16 / 16 at one workgroup per CU, and the 16384 band keeps width 4
+// at 8 so that its instance stays free of scratch spills.
 __host__ __device__ constexpr int moe_rif(int BT, int band) {
+  if (band <= 2048) return BT <= 2 ? 8 : BT <= 4 ? 16 : 8;
   return BT <= 2 ? 8 : BT <= 4 ? (band >= 16384 ? 8 : 16) : 16;
 }
+
+// Workgroups per CU the streaming instance of a K band is built for.
+__host__ __device__ constexpr int moe_waves_per_simd(int band) { return band <= 2048 ? 2 : 1; }
 
 // The power-of-two band of K whose blocking classes an instance compiles:
 // 2048, 4096, 8192 or 16384 (0: K too large).  Within a band every column
@@ -207,7 +213,7 @@ static int moe_window_rows(int64_t K) {
 // workgroup 0 also fills the NaN rows), else the routing comes from the
 // workspace written by moe_route_kernel.
 template <int KMAX, bool FUSED>
-__global__ __launch_bounds__(kGemvThreads, 1) void moe_stream_kernel(
+__global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_stream_kernel(
     const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d, int M, int K,
     const int8_t* __restrict__ xq, const float* __restrict__ xd, int per_slot, int top_k,
     const int32_t* __restrict__ g_offsets, const int32_t* __restrict__ g_list, const int32_t* __restrict__ g_sel,
