@@ -255,7 +255,7 @@ def bench_decode_1b(args, dev, report):
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "q4q8::gemv_kernel<1, 1, 1, 0> (grouped streaming instance, B = 1; "
+                     "kernel": "q4q8::gemv_kernel<1, 4, 1, 0> (grouped streaming instance, B = 1, K <= 8192; "
                                "one launch over the 112 products)",
                      "bytes_per_launch": model.step_bytes, "avg_launch_ms": round(dom_ms, 5)},
     })

@@ -36,13 +36,26 @@ enum GemvKind : int {
   kKindBlockSums = 3,  // one product, Q8 planes, per-block sums written out
 };
 
+// Workgroups per CU an instance is built for.  A grouped instance holds the
+// segments of every blocking class up to J, so its registers are the largest
+// of theirs; the single-column Q4 instance without the 8-block class (every
+// product with K <= 8192) fits two workgroups per CU at the full rows in
+// flight, which measured 2.5% faster on the Llama-3.2-1B decode step.  With
+// the 8-block class it needs more than 256 registers; holding it to 256
+// spills, and halving that class's rows instead cost 3% on K = 14336.
+__host__ __device__ constexpr int gemv_min_wg_per_cu(int BT, int J, int KIND, int WF) {
+  return KIND == kKindGroup && WF == kWeightQ4 && BT == 1 && J <= 4 ? 2 : Q4Q8_GEMV_MIN_WG_PER_CU;
+}
+
 // WF: weight format of the products (kWeightMixed, grouped only: each
 // record's format decides; the folded prologue serves Q4 weights).  A Q8_0
 // block is two loads, so it keeps half the rows in flight for the same bytes
 // in flight.  A mixed instance holds both segments (the larger register
 // footprint of the two), so uniform groups take the single-format ones.
+// Grouped instances (KIND == kKindGroup): J is the largest blocking class
+// served (every product's class must be at most J with S == 1, or J == 8).
 template <int BT, int J, int S, int KIND, int WF = kWeightQ4>
-__global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_kernel(
+__global__ __launch_bounds__(kGemvThreads, gemv_min_wg_per_cu(BT, J, KIND, WF)) void gemv_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ win_map,
     int n_windows, int B, int32_t* __restrict__ Iout) {
   constexpr bool GROUPED = KIND == kKindGroup;
@@ -64,6 +77,7 @@ __global__ __launch_bounds__(kGemvThreads, Q4Q8_GEMV_MIN_WG_PER_CU) void gemv_ke
       const int wl0 = w - P.win_begin, wl1 = seg_end - P.win_begin;
       const GemvClass cls = gemv_class_of(P.K, BT);
       dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
+        if constexpr (JJ > J) return;
         if (WF == kWeightQ8 || (WF == kWeightMixed && P.wf == kWeightQ8))
           gemv_segment<BT, JJ, SS, false, false, DenseCols, gemv_rif(BT, kWeightQ8), kWeightQ8>(
               P, DenseCols(P), B, wl0, wl1, smem, &split, parity, Iout);
@@ -148,10 +162,15 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
                             int64_t n_windows, int64_t max_k, int B, bool fold, int32_t* I, hipStream_t s,
                             int wf) {
   if (table) {
-    if (wf == kWeightQ8) return launch_kind<BT, 1, 1, kKindGroup, kWeightQ8>(p, table, map, n_windows, B, 0, I, s);
+    // max_k is the group's largest K: every product's class is at most its class
+    if (wf == kWeightQ8) return launch_kind<BT, 8, 1, kKindGroup, kWeightQ8>(p, table, map, n_windows, B, 0, I, s);
     if (wf == kWeightMixed)
-      return launch_kind<BT, 1, 1, kKindGroup, kWeightMixed>(p, table, map, n_windows, B, 0, I, s);
-    return launch_kind<BT, 1, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+      return launch_kind<BT, 8, 1, kKindGroup, kWeightMixed>(p, table, map, n_windows, B, 0, I, s);
+    if constexpr (BT == 1) {
+      const GemvClass c = gemv_class_of(max_k, BT);
+      if (c.S == 1 && c.J <= 4) return launch_kind<BT, 4, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+    }
+    return launch_kind<BT, 8, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
   }
   if (wf == kWeightQ8) {
     if (fold) return hipErrorInvalidValue;

@@ -245,7 +245,7 @@ typedef struct q4q8_group_plan {
   int32_t n_records;       /* product records in the table image */
   int32_t n_prologue;      /* distinct fp32 inputs the prologue pass quantises */
   int64_t n_windows;       /* work windows of the streaming pass (rows of ~32 KiB of weights) */
-  int64_t max_k;           /* largest K of a product */
+  int64_t max_k;           /* largest K of a product (also selects the kernel instance) */
   int64_t map_offset;      /* byte offset of the window -> record map in the image */
   int64_t prologue_offset; /* byte offset of the prologue records in the image */
   int64_t table_bytes;     /* size of the table image */
@@ -253,6 +253,8 @@ typedef struct q4q8_group_plan {
   int32_t weight_formats;  /* 1: all products Q4, 2: all Q8_0, 3: both (selects the kernel instance) */
   int32_t reserved;
 } q4q8_group_plan;
+/* Every field is written by q4q8_group_build and read as it left them: a
+ * launch checks their consistency but cannot detect every edited value. */
 
 /* Validate n descriptors and fill the plan.  With table_host == NULL only the
  * plan is computed (table_bytes and workspace_bytes tell the sizes; workspace
