@@ -132,6 +132,35 @@ def test_group_mixed(B):
         assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("k_max", [8192, 8224])
+def test_one_column_group_at_the_instance_boundary(k_max):
+    """One-column groups whose largest K is 8192 take the instance built
+    without the 8-block class; one more block takes the full instance.  Both
+    mix every smaller class and must match the oracle, and each product must
+    equal its single-product call bit for bit."""
+    dev = torch.device("cuda:0")
+    specs = [(257, 32), (96, 1024), (130, 2048), (75, 4096), (300, 6144), (64, k_max), (33, 8192)]
+    problems, refs = [], []
+    for i, (M, K) in enumerate(specs):
+        qs, d = _weights(46, 0, i, M, K)
+        x = workloads.activation(46, 0, i, 1, K)
+        g = workloads.norm_weight(46, 0, i, K)
+        xq, xd, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+        y = torch.full((1, M), float("nan"), dtype=torch.float32, device=dev)
+        problems.append({"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "xq": to_dev(xq), "xd": to_dev(xd),
+                         "y": y})
+        refs.append(oracle.mul_mat(qs, d, xq, xd, nthreads=16, want_y64=False)[0])
+    grp = q.Group(problems, B=1)
+    assert grp.plan.max_k == k_max
+    grp()
+    torch.cuda.synchronize()
+    for p, ref in zip(problems, refs):
+        assert_close(p["y"].cpu().numpy(), ref, f"k_max={k_max} M={p['qs'].shape[0]}")
+        single = q.mul_mat_q4q8(p["qs"], p["d"], p["xq"], p["xd"])
+        torch.cuda.synchronize()
+        assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
+
+
 def test_group_full_llama_1b_layer_in_a_graph():
     """One Llama-3.2-1B layer (seven matrices, four activation rows with their
     own norm weights) as one group with the prologue folded in, captured in a
