@@ -19,10 +19,10 @@ namespace q4q8 {
 // workgroup carries the same load from start to end and the launch has no
 // rounds of short-lived workgroups.  A share spans few products; the next
 // product's record is requested when a segment starts, so it is at hand when
-// the segment ends.  The grouped instance serves every blocking class of its
-// column width (the workgroup dispatches uniformly on each product's class)
-// and reads Q8 planes only; single-product instances compile their own class
-// only.  The grouped and single-product forms are separate instances because
+// the segment ends.  A grouped instance serves every blocking class of its
+// column width up to its template J (the workgroup dispatches uniformly on
+// each product's class) and reads Q8 planes only; single-product instances
+// compile their own class only.  The grouped and single-product forms are separate instances because
 // selecting between the kernel argument and the table at run time would make
 // every access a generic flat access.
 #ifndef Q4Q8_GEMV_MIN_WG_PER_CU
