@@ -337,7 +337,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_rmsnorm(const uint8_t* qs, const uint16_t* d, int64
   p.g = no_norm ? nullptr : g;
   p.eps = eps;
   p.mode = no_norm ? q4q8::kModeRaw : q4q8::kModeNorm;
-  const int win = q4q8::gemv_window_rows(K, B);
+  const int win = q4q8::gemv_window_rows(K, B, q4q8::kWeightQ4, true);
   p.n_win = (int32_t)((M + win - 1) / win);
   g_counts[0].fetch_add(1, std::memory_order_relaxed);
   g_counts[3].fetch_add(1, std::memory_order_relaxed);

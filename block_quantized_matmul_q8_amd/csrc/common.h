@@ -185,8 +185,8 @@ static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
 // Rows per window (the unit a workgroup streams) for a product with K and B;
-// wf: weight format (kWeightQ4 or kWeightQ8).
-Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B, int wf = kWeightQ4);
+// wf: weight format (kWeightQ4 or kWeightQ8); fold: the folded-prologue form.
+Q4Q8_HIDDEN int gemv_window_rows(int64_t K, int64_t B, int wf = kWeightQ4, bool fold = false);
 // Persistent launch over the products of a device `table`, window w of the
 // launch belonging to record map[w]; or, when table == nullptr, over the
 // single record `p`.  `n_windows` = total windows; `max_k` = largest K among

@@ -38,10 +38,10 @@ enum GemvKind : int {
 
 // Workgroups per CU an instance is built for.  A grouped instance holds the
 // segments of every blocking class up to J, so its registers are the largest
-// of theirs; the single-column Q4 instance without the 8-block class (every
-// product with K <= 8192) fits two workgroups per CU at the full rows in
-// flight, which measured 2.5% faster on the Llama-3.2-1B decode step.  With
-// the 8-block class it needs more than 256 registers; holding it to 256
+// of theirs; the single-column Q4 instance without the 8-block classes (every
+// product with K <= 32768) fits two workgroups per CU at the full rows in
+// flight, which measured 1.3-2.5% faster on the Llama-3.2-1B decode step.
+// With an 8-block class it needs more than 256 registers; holding it to 256
 // spills, and halving that class's rows instead cost 3% on K = 14336.
 __host__ __device__ constexpr int gemv_min_wg_per_cu(int BT, int J, int KIND, int WF) {
   return KIND == kKindGroup && WF == kWeightQ4 && BT == 1 && J <= 4 ? 2 : Q4Q8_GEMV_MIN_WG_PER_CU;
@@ -53,7 +53,7 @@ __host__ __device__ constexpr int gemv_min_wg_per_cu(int BT, int J, int KIND, in
 // in flight.  A mixed instance holds both segments (the larger register
 // footprint of the two), so uniform groups take the single-format ones.
 // Grouped instances (KIND == kKindGroup): J is the largest blocking class
-// served (every product's class must be at most J with S == 1, or J == 8).
+// served (every product's class must have at most J blocks per lane).
 template <int BT, int J, int S, int KIND, int WF = kWeightQ4>
 __global__ __launch_bounds__(kGemvThreads, gemv_min_wg_per_cu(BT, J, KIND, WF)) void gemv_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ win_map,
@@ -111,13 +111,13 @@ bool gemv_supported(int64_t M, int64_t K, int64_t B) {
 }
 
 bool gemv_fused_supported(int64_t K, int64_t B) {
-  const GemvClass c = gemv_class_of(K, B);
+  const GemvClass c = gemv_class_unsplit(K, B);
   return B <= 4 && c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;
 }
 
-int gemv_window_rows(int64_t K, int64_t B, int wf) {
+int gemv_window_rows(int64_t K, int64_t B, int wf, bool fold) {
   if (B < 1 || B > 8) return 0;
-  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif(gemv_bt((int)B), wf));
+  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif(gemv_bt((int)B), wf), fold);
 }
 
 // Workgroups that can be resident at once for one kernel instance and LDS
@@ -168,7 +168,7 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
       return launch_kind<BT, 8, 1, kKindGroup, kWeightMixed>(p, table, map, n_windows, B, 0, I, s);
     if constexpr (BT == 1) {
       const GemvClass c = gemv_class_of(max_k, BT);
-      if (c.S == 1 && c.J <= 4) return launch_kind<BT, 4, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+      if (c.J <= 4) return launch_kind<BT, 4, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
     }
     return launch_kind<BT, 8, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
   }
@@ -184,7 +184,7 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
     });
     return err;
   }
-  const GemvClass c = gemv_class_of(max_k, B);
+  const GemvClass c = fold ? gemv_class_unsplit(max_k, B) : gemv_class_of(max_k, B);
   const size_t lds = fold ? fused_lds_bytes(max_k, B) : 0;
   hipError_t err = hipErrorInvalidValue;
   dispatch_class<BT>(c.J, c.S, [&]<int JJ, int SS>() {

@@ -43,7 +43,10 @@ def test_fused_single(M, K, B):
 def test_fused_codes_equal_standalone_prologue(M, K, B, raw):
     """The folded-in prologue produces the codes of the standalone prologue
     bit for bit: with identical codes the product kernel does identical
-    arithmetic in both modes, so the outputs must agree bit for bit."""
+    arithmetic in both modes, so the outputs must agree bit for bit.  The
+    exception is one column with K > 8192: there the plain product splits K
+    over waves while the folded form keeps K in one wave, so the two fp32
+    sums differ in rounding order and both are held to the oracle instead."""
     qs, d = _weights(44, 0, M % 5, M, K)
     x = workloads.activation(44, 0, 1, B, K) * np.float32(2.5)
     g = workloads.norm_weight(44, 0, 1, K)
@@ -54,7 +57,12 @@ def test_fused_codes_equal_standalone_prologue(M, K, B, raw):
     xq, xd, _ = q.q8_quantize_rmsnorm(x_d, g_d, workloads.RMS_EPS, flags=flags)
     y_u = q.mul_mat_q4q8(qs_d, d_d, xq, xd)
     torch.cuda.synchronize()
-    assert np.array_equal(y_f.cpu().numpy().view(np.uint32), y_u.cpu().numpy().view(np.uint32))
+    if B == 1 and K > 8192:
+        ref = _ref(qs, d, x, None if raw else g, no_norm=raw)
+        assert_close(y_f.cpu().numpy(), ref, f"folded M={M} K={K}")
+        assert_close(y_u.cpu().numpy(), ref, f"plain M={M} K={K}")
+    else:
+        assert np.array_equal(y_f.cpu().numpy().view(np.uint32), y_u.cpu().numpy().view(np.uint32))
     xq_o, _, _ = oracle.q8_quantize_rmsnorm(x, None if raw else g, workloads.RMS_EPS, no_norm=raw)
     assert np.array_equal(xq.cpu().numpy(), xq_o)
 
@@ -132,14 +140,16 @@ def test_group_mixed(B):
         assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("k_max", [8192, 8224])
+@pytest.mark.parametrize("k_max", [32768, 32800])
 def test_one_column_group_at_the_instance_boundary(k_max):
-    """One-column groups whose largest K is 8192 take the instance built
-    without the 8-block class; one more block takes the full instance.  Both
-    mix every smaller class and must match the oracle, and each product must
-    equal its single-product call bit for bit."""
+    """One-column groups whose largest K is 32768 take the instance built
+    without the 8-block classes (K split over 2 or 4 waves above 8192); one
+    more block takes the full instance.  Both mix every smaller class and must
+    match the oracle, and each product must equal its single-product call bit
+    for bit."""
     dev = torch.device("cuda:0")
-    specs = [(257, 32), (96, 1024), (130, 2048), (75, 4096), (300, 6144), (64, k_max), (33, 8192)]
+    specs = [(257, 32), (96, 1024), (130, 2048), (75, 4096), (300, 6144), (64, 8192), (40, 8224),
+             (33, 14336), (21, 16416), (17, k_max)]
     problems, refs = [], []
     for i, (M, K) in enumerate(specs):
         qs, d = _weights(46, 0, i, M, K)
