@@ -39,12 +39,15 @@ enum GemvKind : int {
 // Workgroups per CU an instance is built for.  A grouped instance holds the
 // segments of every blocking class up to J, so its registers are the largest
 // of theirs; the single-column Q4 instance without the 8-block classes (every
-// product with K <= 32768) fits two workgroups per CU at the full rows in
-// flight, which measured 1.3-2.5% faster on the Llama-3.2-1B decode step.
+// product with K <= 32768) and the two-column one without the 4-block
+// classes (K <= 16384) fit two workgroups per CU at the full rows in flight,
+// which measured 1.3-2.5% faster on the Llama-3.2-1B decode step.
 // With an 8-block class it needs more than 256 registers; holding it to 256
 // spills, and halving that class's rows instead cost 3% on K = 14336.
 __host__ __device__ constexpr int gemv_min_wg_per_cu(int BT, int J, int KIND, int WF) {
-  return KIND == kKindGroup && WF == kWeightQ4 && BT == 1 && J <= 4 ? 2 : Q4Q8_GEMV_MIN_WG_PER_CU;
+  return KIND == kKindGroup && WF == kWeightQ4 && ((BT == 1 && J <= 4) || (BT == 2 && J <= 2))
+             ? 2
+             : Q4Q8_GEMV_MIN_WG_PER_CU;
 }
 
 // WF: weight format of the products (kWeightMixed, grouped only: each
@@ -169,6 +172,10 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
     if constexpr (BT == 1) {
       const GemvClass c = gemv_class_of(max_k, BT);
       if (c.J <= 4) return launch_kind<BT, 4, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
+    }
+    if constexpr (BT == 2) {
+      const GemvClass c = gemv_class_of(max_k, BT);
+      if (c.J <= 2) return launch_kind<BT, 2, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
     }
     return launch_kind<BT, 8, 1, kKindGroup>(p, table, map, n_windows, B, 0, I, s);
   }

@@ -126,10 +126,10 @@ __host__ __device__ constexpr GemvClass gemv_class_unsplit(int64_t K, int64_t B)
 }
 
 // The class of every other streaming launch.  One column prefers at most 4
-// blocks per lane, splitting K over 2 or 4 waves before it takes 8: a grouped
-// instance without the 8-block classes fits two workgroups per CU (Llama-3-8B
-// at B = 1, K = 14336: 1.5-2% faster than 8 blocks per lane at one workgroup
-// per CU).
+// blocks per lane and two columns at most 2, splitting K over 2 or 4 waves
+// before they take more: a grouped instance without the larger classes fits
+// two workgroups per CU (Llama-3-8B, K = 14336: 1.5-2% faster at B = 1 and
+// at B = 2 than the larger classes at one workgroup per CU).
 __host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
   if (B < 1 || B > 8 || K < kQK) return {0, 0};
   const int64_t nb = K / kQK;
@@ -137,6 +137,11 @@ __host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
     for (int S = 1; S <= 4; S *= 2) {
       const int64_t per = (nb + 64 * S - 1) / (64 * S);
       if (per <= 4) return {per <= 1 ? 1 : per <= 2 ? 2 : 4, S};
+    }
+  if (gemv_bt((int)B) == 2)
+    for (int S = 1; S <= 4; S *= 2) {
+      const int64_t per = (nb + 64 * S - 1) / (64 * S);
+      if (per <= 2) return {per <= 1 ? 1 : 2, S};
     }
   return gemv_class_unsplit(K, B);
 }
@@ -424,6 +429,8 @@ __host__ __device__ __forceinline__ void dispatch_class(int J, int S, F&& f) {
     if (S == 1 && J == 4) f.template operator()<4, 1>();
     if (S == 2 && J == 4) f.template operator()<4, 2>();
     if (S == 4 && J == 4) f.template operator()<4, 4>();
+    if (S == 2 && J == 2) f.template operator()<2, 2>();
+    if (S == 4 && J == 2) f.template operator()<2, 4>();
   } else {
     if (S == 1 && J == 1) f.template operator()<1, 1>();
     if (S == 1 && J == 2) f.template operator()<2, 1>();
