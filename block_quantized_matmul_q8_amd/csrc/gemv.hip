@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kGemvThreads, gemv_min_wg_per_cu(BT, J, KIND, WF)) 
       const int seg_end = min(w_end, P.win_begin + P.n_win);
       const GemvProblem Pn = table[min(rec + 1, rec_last)];
       const int wl0 = w - P.win_begin, wl1 = seg_end - P.win_begin;
-      const GemvClass cls = gemv_class_of(P.K, BT);
+      const GemvClass cls = gemv_class_of(P.K, BT, WF == kWeightMixed ? P.wf : WF);
       dispatch_class<BT>(cls.J, cls.S, [&]<int JJ, int SS>() {
         if constexpr (JJ > J) return;
         if (WF == kWeightQ8 || (WF == kWeightMixed && P.wf == kWeightQ8))
@@ -120,7 +120,7 @@ bool gemv_fused_supported(int64_t K, int64_t B) {
 
 int gemv_window_rows(int64_t K, int64_t B, int wf, bool fold) {
   if (B < 1 || B > 8) return 0;
-  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif(gemv_bt((int)B), wf), fold);
+  return gemv_window_rows_bt(K, gemv_bt((int)B), gemv_rif(gemv_bt((int)B), wf), fold || wf == kWeightQ8);
 }
 
 // Workgroups that can be resident at once for one kernel instance and LDS
@@ -181,7 +181,7 @@ static hipError_t launch_bt(const GemvProblem& p, const GemvProblem* table, cons
   }
   if (wf == kWeightQ8) {
     if (fold) return hipErrorInvalidValue;
-    const GemvClass c = gemv_class_of(max_k, B);
+    const GemvClass c = gemv_class_of(max_k, B, kWeightQ8);
     hipError_t err = hipErrorInvalidValue;
     dispatch_class<BT>(c.J, c.S, [&]<int JJ, int SS>() {
       if (I)

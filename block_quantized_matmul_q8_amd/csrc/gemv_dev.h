@@ -125,13 +125,16 @@ __host__ __device__ constexpr GemvClass gemv_class_unsplit(int64_t K, int64_t B)
   return {0, 0};
 }
 
-// The class of every other streaming launch.  One column prefers at most 4
-// blocks per lane and two columns at most 2, splitting K over 2 or 4 waves
-// before they take more: a grouped instance without the larger classes fits
-// two workgroups per CU (Llama-3-8B, K = 14336: 1.5-2% faster at B = 1 and
-// at B = 2 than the larger classes at one workgroup per CU).
-__host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
+// The class of every other streaming launch.  With Q4 weights one column
+// prefers at most 4 blocks per lane and two columns at most 2, splitting K
+// over 2 or 4 waves before they take more: a grouped instance without the
+// larger classes fits two workgroups per CU (Llama-3-8B, K = 14336: 1.5-2%
+// faster at B = 1 and at B = 2 than the larger classes at one workgroup per
+// CU).  Q8_0 weights keep the unsplit class: the split measured 3-5% slower
+// for them at B = 1.
+__host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B, int wf = kWeightQ4) {
   if (B < 1 || B > 8 || K < kQK) return {0, 0};
+  if (wf == kWeightQ8) return gemv_class_unsplit(K, B);
   const int64_t nb = K / kQK;
   if (gemv_bt((int)B) == 1)
     for (int S = 1; S <= 4; S *= 2) {
@@ -147,7 +150,7 @@ __host__ __device__ constexpr GemvClass gemv_class_of(int64_t K, int64_t B) {
 }
 
 // Rows per window of the class serving K with column width BT (0: none);
-// unsplit: the folded prologue's class.
+// unsplit: the folded prologue's class, and the class of Q8_0 weights.
 __host__ __device__ inline int gemv_window_rows_bt(int64_t K, int BT, int rif = Q4Q8_GEMV_ROWS_IN_FLIGHT,
                                                    bool unsplit = false) {
   const GemvClass c = unsplit ? gemv_class_unsplit(K, BT) : gemv_class_of(K, BT);
