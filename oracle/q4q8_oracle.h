@@ -24,9 +24,16 @@
  * restores).  Readings of every point the pages leave open are listed in the
  * function comments below.
  *
- * Parity status: every function here is pinned by tests against closed
- * forms, hand-derived examples, library routines or brute force; none is
- * "parity unpinned".
+ * Parity status: every reading taken below is pinned by a test that the
+ * plausible alternative reading fails: closed forms, hand-derived examples
+ * re-derived on exact rationals, library routines or brute force.  The block
+ * rules' reciprocal-multiply (id = 1/d, then w * id rather than w / d) and
+ * their codes from the fp32 scale (not the stored fp16 one) are pinned by
+ * blocks that sit on a rounding boundary between the two readings; the
+ * within-block order of the sum of squares by a block whose sequential and
+ * pairwise sums differ.  The fp32 summation order of the products is not a
+ * reading: every order is correct there, and outputs are compared within a
+ * tolerance.
  *
  * Plane layouts (all row-major, no padding):
  *   qs  u8  [M][K/2]  block b of row m occupies bytes m*K/2 + 16b .. +15;

@@ -283,8 +283,10 @@ def test_group_tiled_mixed(B):
 def test_group_tiled_prefill_layer_sampled(T):
     """A Llama-3-8B-shaped prefill layer (T tokens, all seven matrices, fp32
     rows through the prologue pass) as one grouped tiled launch, the launch
-    the benchmark times; the oracle recomputes 40 sampled rows x 40 sampled
-    tokens of each matrix, including the last row and token."""
+    the benchmark times.  Every output must be written (y starts as NaN); the
+    oracle recomputes 40 sampled rows x 40 sampled tokens of each matrix,
+    including the last row and token, and at T = 512 every output of the down
+    projection (4096 x 14336)."""
     dev = torch.device("cuda:0")
     layer = workloads.LLAMA_3_8B
     rng = np.random.default_rng(T + 1)
@@ -303,6 +305,8 @@ def test_group_tiled_prefill_layer_sampled(T):
     grp = q.Group(problems, B=T)
     grp()
     torch.cuda.synchronize()
+    for p, m in zip(problems, layer):
+        assert bool(torch.isfinite(p["y"]).all()), f"T={T} {m.name}: unwritten or non-finite outputs"
     for p, w, m in zip(problems, ws, layer):
         rows = np.sort(rng.choice(m.M, 40, replace=False))
         toks = np.sort(rng.choice(T, 40, replace=False))
@@ -312,14 +316,20 @@ def test_group_tiled_prefill_layer_sampled(T):
         y_o, _ = oracle.mul_mat(qs_o, d_o, xq_o, xd_o, nthreads=16, want_y64=False)
         y_s = p["y"].cpu().numpy()[np.ix_(toks, rows)]
         assert_close(y_s, y_o, f"T={T} {m.name}")
+        if T == 512 and m.name == "down":
+            qs_f, d_f = oracle.q4_quantize(w)
+            xq_f, xd_f, _ = oracle.q8_quantize_rmsnorm(xs[m.slot], gs[m.slot], workloads.RMS_EPS)
+            y_f, _ = oracle.mul_mat(qs_f, d_f, xq_f, xd_f, nthreads=16, want_y64=False)
+            assert_close(p["y"].cpu().numpy(), y_f, f"T={T} down, every output")
 
 
 def test_full_decode_step_sampled():
     """The benchmark's headline launch as it is timed: all 16 Llama-3.2-1B
     layers (112 products, 64 fp32 activation rows with their norm weights) as
-    one grouped call, weights drawn on the device as in the benchmark.  The
-    oracle recomputes 12 sampled rows of every product (the last row
-    included) from the same weights and rows."""
+    one grouped call, weights drawn on the device as in the benchmark.  Every
+    output must be written (y starts as NaN); the oracle recomputes 12 sampled
+    rows of every product (the last row included) from the same weights and
+    rows."""
     import bench
     dev = torch.device("cuda:0")
     model = bench.DecodeModel(workloads.LLAMA_3_2_1B, 16, 1, 0, dev)
@@ -328,6 +338,8 @@ def test_full_decode_step_sampled():
         m["y"].fill_(float("nan"))
     step()
     torch.cuda.synchronize()
+    for m in (mm for layer in model.mats for mm in layer):
+        assert bool(torch.isfinite(m["y"]).all()), f"{m['name']}: unwritten or non-finite outputs"
     rng = np.random.default_rng(7)
     for l in range(model.n_layers):
         acts = {s: (x.cpu().numpy(), g.cpu().numpy()) for s, (x, g) in model.acts[l].items()}

@@ -159,8 +159,10 @@ def test_full_decode_layer(model):
 @pytest.mark.parametrize("T", [512, 2048])
 def test_full_prefill_layer_sampled(T):
     """Prefill at full shape (T tokens, all seven Llama-3-8B matrices): the GPU
-    computes every output; the oracle recomputes 48 sampled rows x 48 sampled
-    tokens of each matrix one by one."""
+    computes every output (all of y must be written: it starts as NaN); its
+    activation codes and scales equal the oracle prologue's bit for bit on
+    sampled tokens, and the oracle recomputes 48 sampled rows x 48 sampled
+    tokens of each matrix one by one from its own codes and scales."""
     dev = torch.device("cuda:0")
     layer = workloads.LLAMA_3_8B
     rng = np.random.default_rng(T)
@@ -169,25 +171,55 @@ def test_full_prefill_layer_sampled(T):
         x = workloads.activation(1, 0, slot, T, K)
         g = workloads.norm_weight(1, 0, slot, K)
         xq, xd, _ = q.q8_quantize_rmsnorm(to_dev(x), to_dev(g), workloads.RMS_EPS)
-        acts[slot] = (xq, xd)
+        acts[slot] = (xq, xd, x, g)
     for mi, mat in enumerate(layer):
         w = workloads.weight(1, 0, mi, mat.M, mat.K)
         qs, d = q.q4_quantize(to_dev(w))
-        xq, xd = acts[mat.slot]
-        y = q.mul_mat_q4q8(qs, d, xq, xd)
+        xq, xd, x, g = acts[mat.slot]
+        y = torch.full((T, mat.M), float("nan"), dtype=torch.float32, device=dev)
+        q.mul_mat_q4q8(qs, d, xq, xd, y=y)
         torch.cuda.synchronize(dev)
+        assert bool(torch.isfinite(y).all()), f"prefill T={T} {mat.name}: unwritten or non-finite outputs"
         rows = np.sort(rng.choice(mat.M, 48, replace=False))
         toks = np.sort(rng.choice(T, 48, replace=False))
         rows[-1] = mat.M - 1
         toks[-1] = T - 1
         qs_o, d_o = oracle.q4_quantize(w[rows])
-        xq_s = xq.cpu().numpy()[toks]
-        xd_s = xd.cpu().numpy()[toks]
-        y_o, _ = oracle.mul_mat(qs_o, d_o, xq_s, xd_s, nthreads=NTHREADS, want_y64=False)
+        xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x[toks], g, workloads.RMS_EPS)
+        assert np.array_equal(xq.cpu().numpy()[toks], xq_o)
+        assert np.array_equal(xd.cpu().numpy()[toks].view(np.uint32), xd_o.view(np.uint32))
+        y_o, _ = oracle.mul_mat(qs_o, d_o, xq_o, xd_o, nthreads=NTHREADS, want_y64=False)
         y_s = y.cpu().numpy()[np.ix_(toks, rows)]
         assert_close(y_s, y_o, f"prefill T={T} {mat.name}")
-        # the activation codes fed to the GEMM match the oracle prologue on the sampled tokens
-        x = workloads.activation(1, 0, mat.slot, T, mat.K)[toks]
-        g = workloads.norm_weight(1, 0, mat.slot, mat.K)
-        xq_o, _, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
-        assert np.array_equal(xq_s, xq_o)
+
+
+def test_prefill_down_projection_t512_full():
+    """The Llama-3-8B down projection (4096 x 14336) at T = 512, on the tiled
+    route: every one of the 2M outputs against the oracle (from the oracle's
+    own weight codes and activation codes, which the GPU's equal bit for bit),
+    and the int32 block sums of one 128-row tile column (all 512 tokens x 448
+    blocks) bit for bit."""
+    dev = torch.device("cuda:0")
+    T, M, K = 512, 4096, 14336
+    w = workloads.weight(8, 0, 6, M, K)
+    x = workloads.activation(8, 0, 3, T, K)
+    g = workloads.norm_weight(8, 0, 3, K)
+    qs, d = q.q4_quantize(to_dev(w))
+    xq, xd, _ = q.q8_quantize_rmsnorm(to_dev(x), to_dev(g), workloads.RMS_EPS)
+    qs_o, d_o = oracle.q4_quantize(w)
+    xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+    assert np.array_equal(qs.cpu().numpy(), qs_o) and np.array_equal(d.cpu().numpy().view(np.uint16), d_o)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), xd_o.view(np.uint32))
+    y = torch.full((T, M), float("nan"), dtype=torch.float32, device=dev)
+    q.mul_mat_q4q8(qs, d, xq, xd, y=y)
+    torch.cuda.synchronize(dev)
+    y = y.cpu().numpy()
+    assert np.isfinite(y).all()
+    y_o, _ = oracle.mul_mat(qs_o, d_o, xq_o, xd_o, nthreads=NTHREADS, want_y64=False)
+    assert_close(y, y_o, "down projection T=512, every output")
+    col = slice(1920, 2048)   # one tile column of 128 weight rows
+    yb, I = q.mul_mat_q4q8_blocksums(qs[col], d[col], xq, xd)
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(I.cpu().numpy(), oracle.block_dots(qs_o[col], K, xq_o))
+    assert_close(yb.cpu().numpy(), y_o[:, col], "tile column through the block-sum instance")

@@ -40,6 +40,53 @@ def test_q4_quantize_hand_examples(hand_examples):
     assert np.all(qs[3] == hand_examples["E3"]["q4_qs_byte"]) and d[3, 0] == 0
 
 
+def test_e7_reciprocal_multiply_on_gpu(hand_examples):
+    """E7: the GPU quantisers take id = fl(1 / d) and then fl(w * id), as the
+    oracle does; a dividing kernel would give code 1 (Q4) and -127 (Q8, Q8_0)
+    at j = 1.  The block sits among random blocks so that it is one block of a
+    longer row (and of several rows) as well."""
+    e7 = hand_examples["E7"]
+    w = workloads.weight(14, 0, 0, 3, 96)
+    w[0, 32:64] = e7["q4_w"]
+    w[2, :32] = e7["q4_w"]
+    qs, d = q.q4_quantize(to_dev(w))
+    qs, d = qs.cpu().numpy(), f16_bits(d)
+    assert qs[0, 16:32].tolist() == e7["q4_qs"] and qs[2, :16].tolist() == e7["q4_qs"]
+    assert d[0, 1] == int(e7["q4_d_bits"], 16) and d[2, 0] == int(e7["q4_d_bits"], 16)
+    qs_o, d_o = oracle.q4_quantize(w)
+    assert np.array_equal(qs, qs_o) and np.array_equal(d, d_o)
+
+    v = workloads.activation(14, 1, 0, 2, 96)
+    v[1, 64:] = e7["q8_v"]
+    xq, xd, xs = q.q8_quantize_rmsnorm(to_dev(v), None, 0.0, flags=q.Q8_NO_NORM, want_xs=True)
+    xq, xd, xs = xq.cpu().numpy(), xd.cpu().numpy(), xs.cpu().numpy()
+    assert xq[1, 64:].tolist() == e7["q8_codes"] and float(xd[1, 2]) == e7["q8_d"] and int(xs[1, 2]) == e7["q8_sum"]
+    o = oracle.q8_quantize_rmsnorm(v, None, 0.0, no_norm=True)
+    assert np.array_equal(xq, o[0]) and np.array_equal(xd.view(np.uint32), o[1].view(np.uint32))
+
+    qw, dw = q.q8_0_quantize(to_dev(v))
+    qw, dw = qw.cpu().numpy(), f16_bits(dw)
+    assert qw[1, 64:].tolist() == e7["q8_codes"] and dw[1, 2] == int(e7["q8_0_d_bits"], 16)
+    qw_o, dw_o = oracle.q8w_quantize(v)
+    assert np.array_equal(qw, qw_o) and np.array_equal(dw, dw_o)
+
+
+def test_e8_codes_from_fp32_scale_on_gpu(hand_examples):
+    """E8: the Q4 and Q8_0 weight quantisers take their codes from the fp32
+    scale and store fp16(d); codes from the fp16 scale would be 12 (Q4) and
+    4 (Q8_0) at j = 1."""
+    e8 = hand_examples["E8"]
+    w = workloads.weight(15, 0, 0, 2, 64)
+    w[1, 32:] = e8["q4_w"]
+    qs, d = q.q4_quantize(to_dev(w))
+    qs, d = qs.cpu().numpy(), f16_bits(d)
+    assert qs[1, 16:].tolist() == e8["q4_qs"] and d[1, 1] == int(e8["q4_d_bits"], 16)
+    w[1, 32:] = e8["q8_0_w"]
+    qw, dw = q.q8_0_quantize(to_dev(w))
+    qw, dw = qw.cpu().numpy(), f16_bits(dw)
+    assert qw[1, 32:].tolist() == e8["q8_0_codes"] and dw[1, 1] == int(e8["q8_0_d_bits"], 16)
+
+
 def test_q4_quantize_wide_range_and_subnormal_scales():
     """Scales that round to fp16 subnormals and to large fp16 values."""
     g = np.random.default_rng(5)

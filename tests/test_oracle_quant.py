@@ -1,7 +1,7 @@
 """Pins of the oracle's Q4 / Q8 quantisers and the RMSNorm prologue.
 
 Pinned against: the hand-derived examples in tests/golden/hand_examples.json
-(E1-E6), closed-form round-trip error bounds derived from the block rule,
+(E1-E8), closed-form round-trip error bounds derived from the block rule,
 closed forms for constant rows, and an fp64 RMS normalisation within the
 fp32 error bound of the fixed reduction order.
 """
@@ -218,6 +218,85 @@ def test_golden_rmsnorm_examples_rederived_exactly(hand_examples):
         assert mod.bits(r["d"]) == hand_examples[name]["xd_bits"]
         assert r["v_times_id"] == hand_examples[name]["code"]
     assert mod.bits(mod.e5_y(mod.constant_row(1)["d"], hand_examples["E5"]["I"])) == hand_examples["E5"]["y_bits"]
+
+
+def _derive_module():
+    import importlib.util
+    path = os.path.join(os.path.dirname(__file__), "golden", "derive_hand_examples.py")
+    spec = importlib.util.spec_from_file_location("derive_hand_examples", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_golden_e7_rederived_exactly(hand_examples):
+    """E7's stored codes follow from the reciprocal-multiply rule on exact
+    rationals, and a plain division gives the other stored codes: the block
+    really separates the two readings."""
+    mod = _derive_module()
+    e7 = hand_examples["E7"]
+    r = mod.e7_blocks()
+    assert float(r["q4"]["d"]) == 7.0 and float(r["q8"]["d"]) == e7["q8_d"]
+    assert r["q4"]["codes"] == e7["q4_codes"] and r["q4"]["codes_if_divided"] == e7["q4_codes_if_divided"]
+    assert r["q8"]["codes"] == e7["q8_codes"] and r["q8"]["codes_if_divided"] == e7["q8_codes_if_divided"]
+    assert e7["q4_codes"] != e7["q4_codes_if_divided"] and e7["q8_codes"] != e7["q8_codes_if_divided"]
+
+
+def test_e7_reciprocal_multiply_not_divide(hand_examples):
+    """The block rules take id = fl(1 / d) and then fl(w * id), not fl(w / d):
+    Q4, Q8 (through the no-norm flag) and Q8_0 codes of E7 equal the
+    reciprocal-multiply codes (a dividing oracle fails here)."""
+    e7 = hand_examples["E7"]
+    qs, d = oracle.q4_quantize(np.array([e7["q4_w"]], dtype=np.float32))
+    assert int(d[0, 0]) == _h(e7["q4_d_bits"])
+    assert qs[0].tolist() == e7["q4_qs"]
+    assert oracle.q4_unpack_codes(qs, 32)[0].tolist() == e7["q4_codes"]
+    v = np.array([e7["q8_v"]], dtype=np.float32)
+    for xq, xd, xs in (oracle.q8_quantize(v), oracle.q8_quantize_rmsnorm(v, None, 1e-5, no_norm=True)):
+        assert xq[0].tolist() == e7["q8_codes"] and float(xd[0, 0]) == e7["q8_d"] and int(xs[0, 0]) == e7["q8_sum"]
+    qw, dw = oracle.q8w_quantize(v)
+    assert qw[0].tolist() == e7["q8_codes"] and int(dw[0, 0]) == _h(e7["q8_0_d_bits"])
+
+
+def test_golden_e8_rederived_exactly(hand_examples):
+    """E8's stored codes follow from the fp32 scale on exact rationals, and
+    codes from the stored fp16 scale would be the other stored codes."""
+    mod = _derive_module()
+    e8 = hand_examples["E8"]
+    r = mod.e8_blocks()
+    for name, key_w in (("q4", "q4"), ("q8_0", "q8_0")):
+        assert r[name]["codes"] == e8[f"{key_w}_codes"], name
+        assert r[name]["codes_if_from_f16"] == e8[f"{key_w}_codes_if_from_f16"], name
+        assert e8[f"{key_w}_codes"] != e8[f"{key_w}_codes_if_from_f16"], name
+        assert mod.bits(r[name]["d"]) == "0x3dcccccd"
+        assert float(r[name]["d16"]) == float(np.uint16(int(e8[f"{key_w}_d_bits"], 16)).view(np.float16))
+
+
+def test_e8_codes_from_fp32_scale(hand_examples):
+    """The Q4 and Q8_0 weight rules take their codes from the fp32 scale and
+    store fp16(d) beside them (an oracle that quantised with the stored fp16
+    scale fails here)."""
+    e8 = hand_examples["E8"]
+    qs, d = oracle.q4_quantize(np.array([e8["q4_w"]], dtype=np.float32))
+    assert int(d[0, 0]) == _h(e8["q4_d_bits"]) and qs[0].tolist() == e8["q4_qs"]
+    assert oracle.q4_unpack_codes(qs, 32)[0].tolist() == e8["q4_codes"]
+    qw, dw = oracle.q8w_quantize(np.array([e8["q8_0_w"]], dtype=np.float32))
+    assert qw[0].tolist() == e8["q8_0_codes"] and int(dw[0, 0]) == _h(e8["q8_0_d_bits"])
+
+
+def test_block_partial_sums_are_sequential():
+    """Within a block the squares are summed left to right in fp32: for
+    x = [4096, 1, 1, 1, 0 x 28] the sequential sum is 2^24 (each + 1 ties to
+    even), where a pairwise order would give 2^24 + 2; s follows in closed
+    form from ssq = 2^24 with numpy's correctly rounded fp32 ops."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :4] = [4096.0, 1.0, 1.0, 1.0]
+    _, s = oracle.rmsnorm(x, 0.0)
+    mean = np.float32(np.float32(2.0 ** 24) / np.float32(32.0))
+    expect = np.float32(1.0) / np.sqrt(mean)
+    other = np.float32(1.0) / np.sqrt(np.float32(np.float32(2.0 ** 24 + 2.0) / np.float32(32.0)))
+    assert expect != other
+    assert s[0] == expect
 
 
 # --- RMS_NORM + MUL + ADD -> Q8 ---------------------------------------------
