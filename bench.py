@@ -7,8 +7,9 @@ activation rows x ~ N(0,1) (attention input, O input, FFN input, down input)
 with their own norm weights g ~ N(1, 0.1); every row goes through the fused
 RMSNorm * g -> Q8 prologue once and the products that share it read the same
 codes.  The step is one grouped call: a prologue pass over the 64 rows, then
-one streaming launch over the 112 products, captured in a HIP graph.
-value = algorithmic bytes per step / time per step, where the bytes are the
+one streaming launch over the 112 products, captured in a HIP graph and
+replayed: value = algorithmic bytes per step / median per-replay time (HIP
+events around each replay), where the bytes are the
 Q4 weights (18 B per 32), each matrix's Q8 activation (36 B per 32) and its
 fp32 output.
 
@@ -73,8 +74,8 @@ def capture(fn):
 
 
 def time_graph(g, steps, warmup):
-    """Median-free plain average over `steps` replays after `warmup`, bracketed
-    by synchronisation on both sides (one process, so no barrier is needed)."""
+    """Plain average over `steps` replays after `warmup`, bracketed by
+    synchronisation on both sides (one process, so no barrier is needed)."""
     import torch
     for _ in range(warmup):
         g.replay()
@@ -89,6 +90,30 @@ def time_graph(g, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_graph_replays(g, steps, warmup):
+    """Per-replay times of a captured step: `warmup` replays, a synchronisation,
+    then `steps` replays back to back on the current stream with a HIP event
+    recorded before the first and after each one (so replay i is timed by
+    events i and i + 1), and a synchronisation.  Returns (median ms, mean ms,
+    min ms, max ms, wall seconds of the timed region)."""
+    import statistics
+
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return statistics.median(per), ev[0].elapsed_time(ev[steps]) / steps, min(per), max(per), wall
 
 
 def time_direct(fn, steps, warmup):
@@ -109,6 +134,53 @@ def time_direct(fn, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks of the GPU, as rocm-smi
+    reports them (read-only query), else from the sysfs DPM tables (the active
+    level is marked with '*'); None where neither is readable."""
+    import glob
+    import subprocess
+
+    out = {"sclk": None, "mclk": None, "source": None}
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(res.stdout)
+        card = data[sorted(data)[0]]
+        for k, v in card.items():
+            kl = k.lower()
+            if kl.startswith("sclk"):
+                out["sclk"] = v
+            elif kl.startswith("mclk"):
+                out["mclk"] = v
+        out["source"] = "rocm-smi --showclocks"
+    except Exception:
+        pass
+    if out["sclk"] is None:
+        for key in ("sclk", "mclk"):
+            for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{key}")):
+                try:
+                    with open(f) as fh:
+                        act = [l.strip() for l in fh if "*" in l]
+                    if act:
+                        out[key] = act[0]
+                        out["source"] = "sysfs pp_dpm_*"
+                        break
+                except OSError:
+                    continue
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def per_launch_ms(fn, reps):
@@ -220,19 +292,24 @@ def committed_traffic():
 
 
 def bench_decode_1b(args, dev, report):
+    import block_quantized_matmul_q8_amd as q
     import workloads as wl
 
     model = DecodeModel(wl.LLAMA_3_2_1B, 16, 1, 0, dev)
     step, stream_only = decode_1b_groups(model)
-    ms, wall = time_direct(lambda: step(), args.steps, args.warmup)
-    value = model.step_bytes / (ms * 1e-3) / 1e9
+    # headline: the step captured in a HIP graph, median of per-replay times
     g_step = capture(lambda: step())
-    ms_graph, _ = time_graph(g_step, args.steps, args.warmup)
+    ms, ms_mean, ms_min, ms_max, wall = time_graph_replays(g_step, args.steps, args.warmup)
     del g_step
+    clocks = gpu_clocks()
+    value = model.step_bytes / (ms * 1e-3) / 1e9
+    # the same step launched directly, back to back (no graph)
+    ms_direct, _ = time_direct(lambda: step(), args.steps, args.warmup)
 
     # dominant kernel: the streaming pass, the same launch as the step's second
     # kernel (same products, Q8 planes of the same values)
     dom_ms = per_launch_ms(lambda: stream_only(), max(args.steps, 10))
+    dom_kernel = q.q4q8_last_kernel()
     dom_gbs = model.step_bytes / (dom_ms * 1e-3) / 1e9
     traffic, traffic_src = committed_traffic()
 
@@ -249,15 +326,22 @@ def bench_decode_1b(args, dev, report):
         "step_bytes": model.step_bytes,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "launches_per_step": 2,
-        "timing": "steps launched back to back on one stream, HIP events around the timed steps",
-        "graph_replay": {"GB/s": round(model.step_bytes / (ms_graph * 1e-3) / 1e9, 1),
-                         "ms_per_step": round(ms_graph, 5)},
+        "timing": (f"the step captured in a HIP graph; {args.warmup} warm-up replays, then {args.steps} "
+                   "replays back to back with a HIP event before the first and after each; value and "
+                   "ms_per_step from the median per-replay time"),
+        "graph_replay_stats": {"median_ms": round(ms, 5), "mean_ms": round(ms_mean, 5), "min_ms": round(ms_min, 5),
+                               "max_ms": round(ms_max, 5)},
+        "direct_launches": {"GB/s": round(model.step_bytes / (ms_direct * 1e-3) / 1e9, 1),
+                            "ms_per_step": round(ms_direct, 5),
+                            "timing": "the same step launched directly, back to back, mean over the timed steps"},
+        "gpu_clocks": clocks,
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "q4q8::gemv_kernel<1, 4, 1, 0> (grouped streaming instance, B = 1, K <= 8192; "
-                               "one launch over the 112 products)",
-                     "bytes_per_launch": model.step_bytes, "avg_launch_ms": round(dom_ms, 5)},
+                     "kernel": dom_kernel,
+                     "launch": "the grouped streaming pass over the 112 products, on Q8 planes",
+                     "bytes_per_launch": model.step_bytes, "avg_launch_ms": round(dom_ms, 5),
+                     "timing": "back-to-back launches between two HIP events on the launch stream"},
     })
     report.update(extras)
     return model
@@ -572,11 +656,12 @@ def bench_prefill(args, dev):
         step = q.Group([{"qs": qs, "d": d, "y": y, "x": acts[m.slot][0], "g": acts[m.slot][1], "eps": 1e-5}
                         for (m, qs, d), y in zip(mats, ys)], B=T)
         ms = per_launch_ms(lambda: gemm(), max(5, args.steps // 2))
+        kernel = q.q4q8_last_kernel()
         ms_step, _ = time_direct(lambda: step(), max(5, args.steps // 2), 2)
         ops = 2 * T * sum(m.M * m.K for m in layer)
         tops = ops / (ms * 1e-3) / 1e12
         out[f"T={T}"] = {"TOPS": round(tops, 1), "frac_i8_peak": round(tops / I8_PEAK_TOPS, 4),
-                         "ms_per_layer": round(ms, 4),
+                         "ms_per_layer": round(ms, 4), "kernel": kernel,
                          "step_with_prologue": {"TOPS": round(ops / (ms_step * 1e-3) / 1e12, 1),
                                                 "ms": round(ms_step, 4)},
                          "launch": "one grouped tiled launch over the 7 products"}
@@ -754,7 +839,10 @@ def cpu_baseline(model, seconds=10.0):
 
     import oracle
 
-    nthreads = min(os.cpu_count() or 1, 16)
+    # every CPU this process may run on, up to the 16 that one GPU's jobs are
+    # allotted on the GPU machines
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    nthreads = max(1, min(avail, 16))
     host = []
     for l in range(model.n_layers):
         acts = {s: (x.cpu().numpy(), g.cpu().numpy()) for s, (x, g) in model.acts[l].items()}
@@ -775,7 +863,9 @@ def cpu_baseline(model, seconds=10.0):
     gbs = model.step_bytes * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{reps} full decode step(s) of the Llama-3.2-1B-shaped workload (16 layers, B=1), "
-                      f"{el:.1f} s, {nthreads} threads"}
+                      f"{el:.1f} s, {nthreads} threads (output rows split over threads)",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "cpus_available": avail,
+            "build": "gcc -O2 -ffp-contract=off -fno-fast-math, plain C, no intrinsics"}
 
 
 def main():
@@ -835,6 +925,18 @@ def main():
         report["decode_8b"] = bench_decode_8b(args, dev)
         print("[bench] 8B decode done", file=sys.stderr, flush=True)
         report["prefill"] = bench_prefill(args, dev)
+        p = report["prefill"]["T=2048"]
+        report["roofline_gemm"] = {
+            "bound": "mfma", "dtype": "i8", "achieved": p["TOPS"], "peak": I8_PEAK_TOPS, "unit": "TOPS",
+            "frac": round(p["TOPS"] / I8_PEAK_TOPS, 4), "kernel": p["kernel"],
+            "launch": "Llama-3-8B-shaped prefill layer, T = 2048: one grouped tiled launch over the 7 products "
+                      "on Q8 planes",
+            "ops_per_launch": 2 * 2048 * sum(m.M * m.K for m in __import__("workloads").LLAMA_3_8B),
+            "avg_launch_ms": p["ms_per_layer"],
+            "timing": "back-to-back launches between two HIP events on the launch stream",
+            "profile": "profiles/gemm_prefill_llama8b_t2048.txt",
+            "T=512": {"achieved": report["prefill"]["T=512"]["TOPS"],
+                      "frac": report["prefill"]["T=512"]["frac_i8_peak"]}}
         print("[bench] prefill done", file=sys.stderr, flush=True)
         report["moe"] = bench_moe(args, dev)
         print("[bench] moe done", file=sys.stderr, flush=True)
@@ -861,9 +963,11 @@ def main():
         "dtype": "i8",
         "data": "synthetic (seeded, device-drawn N(0,0.02) weights, N(0,1) activations, N(1,0.1) norm weights)",
         "config": {"workload": "llama-3.2-1b-shaped decode, B=1, 16 layers x 7 Q4 matrices; RMSNorm*g->Q8 "
-                               "prologue pass over the 64 activation rows + one streaming launch, in a HIP graph",
+                               "prologue pass over the 64 activation rows + one streaming launch, captured in a "
+                               "HIP graph (median per-replay time)",
                    "hidden": 2048, "ffn": 8192, "kv_rows": 512, "layers": 16, "B": 1},
         "roofline": report.pop("roofline"),
+        "roofline_gemm": report.pop("roofline_gemm", None),
         "cpu_baseline": report.pop("cpu_baseline"),
     }
     line.update(report)

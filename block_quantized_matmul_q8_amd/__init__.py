@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.q4q8_last_error.argtypes = []
     L.q4q8_version.restype = i32
     L.q4q8_version.argtypes = []
+    L.q4q8_last_kernel.restype = ctypes.c_char_p
+    L.q4q8_last_kernel.argtypes = []
     L.q4_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
     L.q8_quantize_rmsnorm.argtypes = [vp, i64, i64, vp, f32, u32, vp, vp, vp, vp]
     L.mul_mat_q4q8.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
@@ -538,6 +540,11 @@ def q4q8_dispatch_counts(reset: bool = False):
 
 def q4q8_last_error() -> str:
     return lib().q4q8_last_error().decode()
+
+
+def q4q8_last_kernel() -> str:
+    """Kernel instance that this thread's last library call launched last."""
+    return lib().q4q8_last_kernel().decode()
 
 
 def q4q8_version() -> int:

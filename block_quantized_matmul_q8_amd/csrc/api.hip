@@ -5,8 +5,11 @@
 // idea of "GGML：Backend 抽象与硬件加速" (section "注册顺序决定默认优先级"):
 // a request the library cannot serve is rejected explicitly, never computed
 // wrongly.
+#include <cxxabi.h>
+
 #include <atomic>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -21,6 +24,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local const void* g_last_kernel = nullptr;
+thread_local char g_last_kernel_name[512] = "";
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -149,7 +154,23 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
 
 }  // namespace
 
+namespace q4q8 {
+void note_launch(const void* kernel) { g_last_kernel = kernel; }
+}  // namespace q4q8
+
 Q4Q8_EXPORT const char* q4q8_last_error(void) { return g_err; }
+
+Q4Q8_EXPORT const char* q4q8_last_kernel(void) {
+  g_last_kernel_name[0] = '\0';
+  if (!g_last_kernel) return g_last_kernel_name;
+  const char* raw = hipKernelNameRefByPtr(g_last_kernel, nullptr);
+  if (!raw) return g_last_kernel_name;
+  int st = -1;
+  char* dem = abi::__cxa_demangle(raw, nullptr, nullptr, &st);
+  snprintf(g_last_kernel_name, sizeof g_last_kernel_name, "%s", (st == 0 && dem) ? dem : raw);
+  free(dem);
+  return g_last_kernel_name;
+}
 
 Q4Q8_EXPORT int q4q8_version(void) { return 100; }
 

@@ -181,6 +181,10 @@ struct alignas(16) PrologueJob {
 static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
 
 
+// Records the kernel instance a launch site is about to launch (host pointer
+// of the __global__ function), per calling thread, for q4q8_last_kernel().
+Q4Q8_HIDDEN void note_launch(const void* kernel);
+
 // Route selection helpers (host).
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);

@@ -314,37 +314,21 @@ int64_t gemm_tiles(int64_t M, int64_t B) { return ((M + kTM - 1) / kTM) * ((B + 
 hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* table, const int32_t* tile_map,
                        int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s, int wf) {
   const dim3 grid((unsigned)n_tiles), block(kGemmThreads);
+  auto go = [&](auto kernel) {
+    note_launch((const void*)kernel);
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, p, table, tile_map, (int)n_tiles, (int)B, I);
+    return hipGetLastError();
+  };
   if (table) {
     if (I) return hipErrorInvalidValue;
-    if (wf == kWeightQ4)
-      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-    else if (wf == kWeightQ8)
-      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-    else if (wf == kWeightMixed)
-      hipLaunchKernelGGL((gemm_kernel<false, true, kWeightMixed>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-    else
-      return hipErrorInvalidValue;
-  } else if (wf == kWeightQ4) {
-    if (I)
-      hipLaunchKernelGGL((gemm_kernel<true, false, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-    else
-      hipLaunchKernelGGL((gemm_kernel<false, false, kWeightQ4>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-  } else if (wf == kWeightQ8) {
-    if (I)
-      hipLaunchKernelGGL((gemm_kernel<true, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-    else
-      hipLaunchKernelGGL((gemm_kernel<false, false, kWeightQ8>), grid, block, 0, s, p, table, tile_map,
-                         (int)n_tiles, (int)B, I);
-  } else {
+    if (wf == kWeightQ4) return go(gemm_kernel<false, true, kWeightQ4>);
+    if (wf == kWeightQ8) return go(gemm_kernel<false, true, kWeightQ8>);
+    if (wf == kWeightMixed) return go(gemm_kernel<false, true, kWeightMixed>);
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  if (wf == kWeightQ4) return I ? go(gemm_kernel<true, false, kWeightQ4>) : go(gemm_kernel<false, false, kWeightQ4>);
+  if (wf == kWeightQ8) return I ? go(gemm_kernel<true, false, kWeightQ8>) : go(gemm_kernel<false, false, kWeightQ8>);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace q4q8

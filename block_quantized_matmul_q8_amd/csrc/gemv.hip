@@ -155,6 +155,7 @@ static hipError_t launch_kind(const GemvProblem& p, const GemvProblem* table, co
   const void* k = (const void*)gemv_kernel<BT, J, S, KIND, WF>;
   int64_t grid = resident_workgroups(k, lds);
   if (grid > n_windows) grid = n_windows;
+  note_launch(k);
   hipLaunchKernelGGL((gemv_kernel<BT, J, S, KIND, WF>), dim3((unsigned)grid), dim3(kGemvThreads), lds, s, p,
                      table, map, (int)n_windows, B, I);
   return hipGetLastError();

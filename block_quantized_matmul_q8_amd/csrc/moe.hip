@@ -364,6 +364,7 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
   const size_t fused_lds = fused ? (size_t)moe_fused_route_ints(E, n) * sizeof(int) : 0;
   if (!fused) {
     const size_t route_lds = (3 * ((size_t)E + 1) + kRouteThreads / 64) * sizeof(int);
+    note_launch((const void*)moe_route_kernel);
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)n_win,
                        offsets, list, rank, sel, costp, ctl, (int)M, y);
     hipError_t err = hipGetLastError();
@@ -372,6 +373,7 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
   auto go = [&](auto kernel) {
     int64_t grid = moe_resident_workgroups((const void*)kernel);
     if (grid > E * n_win) grid = E * n_win;
+    note_launch((const void*)kernel);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kGemvThreads), fused_lds, s, qs, d, (int)M, (int)K, xq,
                        xd, n_x_slots == 1 ? 0 : 1, (int)top_k, offsets, list, sel, costp, ctl, y, (int)n_win, unit,
                        ids, n, (int)E);
@@ -420,6 +422,7 @@ __global__ __launch_bounds__(kSumThreads) void moe_expert_sum_kernel(const float
 hipError_t launch_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M, float* out,
                                  hipStream_t s) {
   const dim3 grid((unsigned)((M + kSumThreads - 1) / kSumThreads), (unsigned)T);
+  note_launch((const void*)moe_expert_sum_kernel);
   hipLaunchKernelGGL(moe_expert_sum_kernel, grid, dim3(kSumThreads), 0, s, y, w, (int)top_k, M, out);
   return hipGetLastError();
 }

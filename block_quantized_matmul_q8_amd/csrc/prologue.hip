@@ -84,6 +84,7 @@ hipError_t launch_q4_quantize(const float* w, int64_t M, int64_t K, uint8_t* qs,
                               hipStream_t s) {
   const int64_t n = M * (K / kQK);
   const int64_t grid = (n + 255) / 256;
+  note_launch((const void*)q4_quantize_kernel);
   hipLaunchKernelGGL(q4_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, w, M, K, qs, d);
   return hipGetLastError();
 }
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(256) void q8w_quantize_kernel(const float* __restri
 hipError_t launch_q8w_quantize(const float* w, int64_t M, int64_t K, int8_t* qw, uint16_t* d, hipStream_t s) {
   const int64_t n = M * (K / kQK);
   const int64_t grid = (n + 255) / 256;
+  note_launch((const void*)q8w_quantize_kernel);
   hipLaunchKernelGGL(q8w_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, w, M, K, qw, d);
   return hipGetLastError();
 }
@@ -165,6 +167,7 @@ hipError_t launch_q8_rmsnorm(const float* x, int64_t B, int64_t K, const float* 
                              const float* a, int64_t a_row_stride) {
   const int P = next_pow2_int((int)(K / kQK));
   const size_t lds = (no_norm || K <= kFastPrologueK) ? 0 : 2 * (size_t)P * sizeof(float);
+  note_launch((const void*)rmsnorm_q8_kernel);
   hipLaunchKernelGGL(rmsnorm_q8_kernel, dim3((unsigned)B), dim3(kPrologueThreads), lds, s, x,
                      (int)K, g, eps, no_norm ? 1 : 0, P, xq, xd, xs, a, a_row_stride);
   return hipGetLastError();
@@ -201,6 +204,7 @@ __global__ __launch_bounds__(256) void swiglu_q8_kernel(const float* __restrict_
 hipError_t launch_swiglu_q8(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride,
                             int8_t* xq, float* xd, int32_t* xs, hipStream_t s) {
   const int64_t n = B * (F / kQK);
+  note_launch((const void*)swiglu_q8_kernel);
   hipLaunchKernelGGL(swiglu_q8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gate, up, B, F,
                      row_stride, xq, xd, xs);
   return hipGetLastError();
@@ -242,6 +246,7 @@ __global__ __launch_bounds__(kPrologueThreads) void group_prologue_kernel(
 hipError_t launch_group_prologue(const PrologueJob* jobs, int64_t n_jobs, int64_t B, int64_t max_k,
                                  hipStream_t s) {
   const size_t lds = max_k > kFastPrologueK ? 2 * (size_t)next_pow2_int((int)(max_k / kQK)) * sizeof(float) : 0;
+  note_launch((const void*)group_prologue_kernel);
   hipLaunchKernelGGL(group_prologue_kernel, dim3((unsigned)n_jobs, (unsigned)B), dim3(kPrologueThreads), lds,
                      s, jobs);
   return hipGetLastError();

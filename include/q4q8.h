@@ -68,7 +68,12 @@ extern "C" {
  * to int8 codes [M][K], 16-byte aligned; d as for Q4), see mul_mat_q8_0_q8. */
 #define Q4Q8_WEIGHTS_Q8_0 2u
 
-/* Message describing the last failed call on this thread ("" if none). */
+/* Message describing the last failed call on this thread ("" if none).  The
+ * error convention follows the supports_op idea of "GGML：Backend 抽象与硬件
+ * 加速" (section "注册顺序决定默认优先级"): a request the library cannot serve
+ * is rejected explicitly with a reason, never computed wrongly.  The string
+ * lives in thread-local storage owned by the library and stays valid until
+ * the thread's next library call; the call never fails. */
 const char* q4q8_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -344,8 +349,24 @@ int mul_mat_q8_0_q8_blocksums(const int8_t* qw, const uint16_t* d, int64_t M, in
 
 /* Per-route dispatch counters since load or the last reset:
  * out[0] GEMV launches, out[1] GEMM launches, out[2] routed (MUL_MAT_ID)
- * calls, out[3] prologue launches.  reset != 0 clears them after reading. */
+ * calls, out[3] prologue launches.  reset != 0 clears them after reading
+ * (atomically per counter; the counters are process-wide).  The analogue of
+ * the fusion statistics of "llama.cpp b10909：Metal后端融合表重构，修复约5%
+ * token生成性能回退" (section "融合统计与回归测试": counting which fused
+ * kernels ran, so that a silently lost fusion shows): here they show which
+ * route a call took.  out must hold 4 values; returns Q4Q8_E_ARG if null. */
 int q4q8_dispatch_counts(uint64_t out[4], int reset);
+
+/* Name of the kernel instance (demangled, with its template arguments) that
+ * the calling thread's last library call launched last -- for a grouped call
+ * the streaming or tiled pass, for a routed call its streaming pass -- or ""
+ * before any launch.  Like the dispatch counters above, the analogue of the
+ * fusion statistics of the Metal fusion page (section "融合统计与回归测试":
+ * which fused kernels actually ran), so that a measurement can name the
+ * instance it timed.  The string lives in thread-local storage owned by the
+ * library and stays valid until the thread's next call of this function;
+ * the call never fails. */
+const char* q4q8_last_kernel(void);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
               "q8_quantize_rmsnorm_add", "q8_quantize_swiglu", "q8_0_quantize", "mul_mat_q8_0_q8",
               "mul_mat_q8_0_q8_blocksums",
               "mul_mat_id_q4q8_workspace", "q4q8_last_error", "q4q8_set_path",
-              "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_version"):
+              "mul_mat_q4q8_blocksums", "q4q8_dispatch_counts", "q4q8_last_kernel", "q4q8_version"):
         assert n in names, n
 
 
@@ -45,6 +45,11 @@ def test_binding_has_same_names():
 
 def test_version():
     assert q.q4q8_version() == 100
+
+
+def test_last_kernel_before_any_launch():
+    """No launch on this thread yet (the CPU suite launches nothing)."""
+    assert q.q4q8_last_kernel() == ""
 
 
 def _v(addr):
