@@ -8,28 +8,47 @@
 // fp32 is F = 1.5 * 2^23 + I exactly (|I| < 2^22), and the per-block rescale
 // is two fp32 fmas per output element: t = fma(F, d_w, -1.5 * 2^23 * d_w) =
 // fl(I * d_w) (the product 1.5 * 2^23 * d_w is exact for an fp16 d_w), then
-// acc = fma(t, d_x, acc).  Those two fmas per output and block are the
-// kernel's bound: the vector ALU, not the matrix core.
+// acc = fma(t, d_x, acc).
+//
+// What bounds it on gfx950 (measured): a 32x32x32 i8 MFMA occupies its SIMD
+// for about 33.5 cycles, and an fp32 fma issues every ~2.35 cycles when two
+// or more waves feed the SIMD (one wave alone issues one every ~4.6 cycles,
+// and one that depends on the fma just before it waits) -- but the two do
+// not overlap once the vector ALU is saturated.  A 32 x 32 tile-block
+// therefore costs about 33.5 + 32 x 2.35 = 109 SIMD cycles (about 30% of the
+// int8 peak); every other vector instruction adds to it, and LDS reads
+// (about 5 cycles per contiguous 1 KiB wave read, 8 for strided ones and 4x
+// that for 4-way bank conflicts, per CU) must stay under it.  With two waves
+// per SIMD (the register budget of this tiling), the stage fetch, the stage
+// store and the barrier leave a SIMD with one ready wave about a third of the
+// time, and then its vector ALU runs at half rate.
 //
 // Operand roles: A = activations (MFMA rows = tokens), B = weights (MFMA
-// columns = weight rows).  Each lane then holds one weight row (one d_w per
-// lane) and 16 token rows, and the output y[token][row] is stored with
-// consecutive lanes on consecutive rows.
+// columns = weight rows).  Each lane then holds one weight row per 32-row
+// tile (one d_w per lane) and 16 token rows: 8 (r / 4) + 4 (lane / 32) +
+// (r % 4) for result register r.
 //
 // Tiling: a workgroup of 4 waves computes 128 tokens x 128 weight rows; each
-// wave a 64 x 64 quadrant (2 x 2 MFMA tiles).  A stage is 4 blocks of K (128
-// bytes of activation codes per token, 64 bytes of packed weight codes per
-// row), so every global load instruction covers whole cache lines.  Two LDS
+// wave 32 tokens x 128 rows (4 MFMA tiles side by side), so the 16 token
+// scales a lane needs per block are read once and serve 4 tiles.  A stage is
+// 4 blocks of K.  Stage layout in LDS, per block: activations and weight
+// codes as [32-row group][half][32 rows][16 bytes], so that the operand read
+// of a wave (lane = half * 32 + row) is one contiguous 1 KiB; the row slot is
+// XOR-ed with 8 * half, which keeps those reads contiguous per half and
+// with padded block planes spreads the stage writes over the banks.  Two LDS
 // stage buffers: while stage s is computed, stage s + 1 travels from global
-// memory into registers and then into the other buffer (weights unpacked to
+// memory into registers and then into the other buffer (Q4 codes unpacked to
 // signed int8 once, shared by all 128 tokens), so each stage costs one
-// barrier.  Loads are unconditional from clamped addresses; rows, tokens and
-// blocks past the end get zero scales, so they add exact zeros.
+// barrier.  Global loads are shaped for few cache lines per instruction
+// (whole 128-byte lines of a token or row; the 4 scales of a token or row of
+// a stage in one load) and take no vector instructions in a full stage (a
+// uniform base plus per-lane offsets fixed per tile).  Loads are
+// unconditional from clamped addresses; rows and tokens past the end are
+// computed but never stored, and blocks past the end are skipped.
 //
 // Q8_0 weights (32 signed int8 codes and one fp16 scale per block) take the
-// same path: a stage then holds 128 bytes of codes per weight row, fetched as
-// four 16-byte pieces per thread and stored to LDS as they are (no unpack);
-// everything after the LDS stage is shared with the Q4 route.
+// same path: their codes go to LDS as they are (no unpack); everything after
+// the LDS stage is shared with the Q4 route.
 //
 // One launch serves one product or a group of products (a device table of
 // records plus a tile -> record map; the map lists the long-K products
@@ -43,13 +62,13 @@ namespace q4q8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 128;  // weight rows per workgroup
-constexpr int kTN = 128;  // tokens per workgroup
-constexpr int kIT = kTN / 64;  // 32-token MFMA tiles per wave
-constexpr int kNA = kTN / 32;  // 16-byte activation chunks per thread per stage
-constexpr int kNBuf = 2;       // LDS stage buffers
-constexpr int kKB = 4;             // 32-blocks per stage
+constexpr int kTM = 128;            // weight rows per workgroup
+constexpr int kTN = 128;            // tokens per workgroup
+constexpr int kJT = kTM / 32;       // 32-row MFMA tiles per wave
+constexpr int kKB = 4;              // 32-blocks per stage
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
 
@@ -58,13 +77,26 @@ __device__ __forceinline__ uint32_t nib_to_s8(uint32_t n) {
   return (n + 0x78787878u) ^ 0x80808080u;
 }
 
+// Block planes are padded (activation codes by 32 bytes, weight codes by
+// 64), so that the stage writes of 16 consecutive lanes -- 2 tokens x 4
+// blocks x 2 halves of activation codes, 4 rows x 4 blocks of Q4 codes --
+// fall on 16 distinct 16-byte bank slots.
 struct GemmStage {
-  int8_t a[kKB][kTN][kQK];   // activation codes
-  int8_t w[kKB][kTM][kQK];   // weight codes as signed int8
-  float dx[kKB][kTN];        // activation scales (0 past the end)
-  float dw[kKB][kTM];        // weight scales (0 past the end)
-  float cw[kKB][kTM];        // -1.5 * 2^23 * dw
+  struct {
+    int8_t v[kTN / 32][2][32][16];     // activation codes [token group][half][token ^ 8 half][16 B]
+    int8_t pad[32];
+  } a[kKB];
+  struct {
+    int8_t v[kTM / 32][2][32][16];     // weight codes as signed int8, same layout over rows
+    int8_t pad[64];
+  } w[kKB];
+  float dx[kKB][kTN];                  // activation scales
+  f32x2 dwc[kKB][kTM];                 // (d_w, -1.5 * 2^23 * d_w)
 };
+
+// Byte offset of the 16-byte piece (half h, row r) inside a [32-row group]
+// region of the a / w arrays (one block).
+__device__ __forceinline__ int piece_off(int r, int h) { return h * 512 + ((r & 31) ^ (8 * h)) * 16; }
 
 // Tile L of product P (its tiles start at P.win_begin): n_nt token tiles per
 // weight tile; st: the workgroup's LDS stage buffers.
@@ -72,7 +104,6 @@ template <bool WRITE_I, int WF>
 __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt, int B, GemmStage* st,
                                           int32_t* __restrict__ Iout) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wt = wave >> 1, ww = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int M = P.M, K = P.K;
   const uint8_t* __restrict__ qs = P.qs;
@@ -81,24 +112,79 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
   const float* __restrict__ xd = P.xd;
   float* __restrict__ y = P.y;
   const int nb = K / kQK;
-  constexpr int kNW = WF == kWeightQ8 ? 4 : 2;  // 16-byte weight chunks per thread per stage
   const int64_t row_bytes = WF == kWeightQ8 ? K : K / 2;
   const int lt = L - P.win_begin;
   const int m0 = (lt / n_nt) * kTM, n0 = (lt % n_nt) * kTN;
 
-  // Thread -> data of a stage: activation chunk c = 256 i + tid is token
-  // c / 8, 16-byte piece c % 8 (two pieces per block); Q4 weight chunk
-  // c = 256 i + tid is row c / 4, block c % 4, Q8_0 weight chunk row c / 8,
-  // piece c % 8 like the activations; scales: row / token tid / 2,
-  // blocks 2 (tid % 2) and 2 (tid % 2) + 1 (read one value each: d rows are
-  // only 2-byte aligned).
-  auto fetch = [&](int kb0, i32x4 (&a)[kNA], u32x4 (&w)[kNW], uint32_t (&dw)[2], float (&dx)[2]) {
+  // Per stage and thread, through registers:
+  //   - activation chunks c = 256 i + tid: token c / 8, 16-byte piece c % 8
+  //     (block (c % 8) / 2, half c % 2), so 8 lanes read one token's 128
+  //     contiguous bytes;
+  //   - Q4 weight chunks c = 256 i + tid: row c / 4, block c % 4 (16 bytes
+  //     holding codes j and j + 16 per byte); Q8_0: row c / 8, piece c % 8
+  //     like the activations;
+  //   - scales of the stage's 4 blocks: the activation scales of token
+  //     tid % 128 (16 bytes) and the weight scales of row tid % 128 (8
+  //     bytes); threads below 128 store the former, the others the latter.
+  // A full stage whose scale rows keep that alignment (K a multiple of 128;
+  // the usual case) addresses each of them as a uniform base -- the tile's
+  // first row, advanced by the stage -- plus a 32-bit per-lane offset
+  // computed once per tile (rows past the end clamped to the last one): no
+  // vector instructions and no branches, so that nothing makes the wave wait
+  // for the loads before the stage store that consumes them.  Any other stage
+  // clamps every row and block index and reads the scales one at a time.
+  constexpr int kNA = kTN / 32;
+  constexpr int kNW = WF == kWeightQ8 ? 4 : 2;
+  constexpr int kWB = WF == kWeightQ8 ? kQK : kQK / 2;  // weight bytes per row and block
+  const int sr = tid & 127;
+  const int8_t* __restrict__ xtile = xq + (int64_t)n0 * K;
+  const uint8_t* __restrict__ wtile = qs + (int64_t)m0 * row_bytes;
+  const float* __restrict__ xdtile = xd + (int64_t)n0 * nb;
+  const uint16_t* __restrict__ dtile = d + (int64_t)m0 * nb;
+  uint32_t aoff[kNA], woff[kNW];
+#pragma unroll
+  for (int i = 0; i < kNA; ++i) {
+    const int c = 256 * i + tid;
+    aoff[i] = (uint32_t)min(c / 8, B - 1 - n0) * (uint32_t)K + 32u * ((c % 8) / 2) + 16u * (c % 2);
+  }
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) {
+    const int c = 256 * i + tid;
+    if constexpr (WF == kWeightQ8)
+      woff[i] = (uint32_t)min(c / 8, M - 1 - m0) * (uint32_t)row_bytes + 32u * ((c % 8) / 2) + 16u * (c % 2);
+    else
+      woff[i] = (uint32_t)min(c / 4, M - 1 - m0) * (uint32_t)row_bytes + 16u * (c % 4);
+  }
+  const uint32_t xsoff = (uint32_t)min(sr, B - 1 - n0) * (uint32_t)nb;
+  const uint32_t wsoff = (uint32_t)min(sr, M - 1 - m0) * (uint32_t)nb;
+  const bool fast_ok = (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(xd) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(d) & 7) == 0;
+
+  // Staged data of one stage: packed weight scales in sw, activation scales
+  // (or, from the general fetch, the weight scales one per word) in sx.
+  struct Staged {
+    i32x4 a[kNA];
+    u32x4 w[kNW];
+    u32x4 sx;
+    u32x2 sw;
+  };
+  auto fetch_fast = [&](int kb0, Staged& f) {
+    const int8_t* xs = xtile + (int64_t)kb0 * kQK;
+    const uint8_t* ws = wtile + (int64_t)kb0 * kWB;
+#pragma unroll
+    for (int i = 0; i < kNA; ++i) f.a[i] = *gptr(reinterpret_cast<const i32x4*>(xs + aoff[i]));
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) f.w[i] = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4*>(ws + woff[i])));
+    f.sx = *gptr(reinterpret_cast<const u32x4*>(xdtile + kb0 + xsoff));
+    f.sw = *gptr(reinterpret_cast<const u32x2*>(dtile + kb0 + wsoff));
+  };
+  auto fetch_any = [&](int kb0, Staged& f) {
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
       const int n = min(n0 + c / 8, B - 1);
       const int blk = min(kb0 + (c % 8) / 2, nb - 1);
-      a[i] = *gptr(reinterpret_cast<const i32x4*>(xq + (int64_t)n * K + (int64_t)blk * kQK + 16 * (c % 2)));
+      f.a[i] = *gptr(reinterpret_cast<const i32x4*>(xq + (int64_t)n * K + (int64_t)blk * kQK + 16 * (c % 2)));
     }
 #pragma unroll
     for (int i = 0; i < kNW; ++i) {
@@ -106,171 +192,181 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
       if constexpr (WF == kWeightQ8) {
         const int m = min(m0 + c / 8, M - 1);
         const int blk = min(kb0 + (c % 8) / 2, nb - 1);
-        w[i] = __builtin_nontemporal_load(gptr(
+        f.w[i] = __builtin_nontemporal_load(gptr(
             reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * kQK + 16 * (c % 2))));
       } else {
         const int m = min(m0 + c / 4, M - 1);
         const int blk = min(kb0 + c % 4, nb - 1);
-        w[i] = __builtin_nontemporal_load(
+        f.w[i] = __builtin_nontemporal_load(
             gptr(reinterpret_cast<const u32x4*>(qs + (int64_t)m * row_bytes + (int64_t)blk * 16)));
       }
     }
-    const int m = min(m0 + tid / 2, M - 1);
-    const int n = min(n0 + tid / 2, B - 1);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int blk = min(kb0 + 2 * (tid % 2) + e, nb - 1);
-      dw[e] = gptr(d)[(int64_t)m * nb + blk];
-      if (tid / 2 < kTN) dx[e] = gptr(xd)[(int64_t)n * nb + blk];
+    if (tid < 128) {
+      const Q4Q8_GLOBAL uint32_t* p = gptr(reinterpret_cast<const uint32_t*>(xdtile + xsoff));
+      f.sx = u32x4{p[min(kb0, nb - 1)], p[min(kb0 + 1, nb - 1)], p[min(kb0 + 2, nb - 1)], p[min(kb0 + 3, nb - 1)]};
+    } else {
+      const Q4Q8_GLOBAL uint16_t* p = gptr(dtile + wsoff);
+      f.sx = u32x4{p[min(kb0, nb - 1)], p[min(kb0 + 1, nb - 1)], p[min(kb0 + 2, nb - 1)], p[min(kb0 + 3, nb - 1)]};
     }
+    f.sw = u32x2{0u, 0u};  // every field written on both paths: nothing to merge
   };
 
-  auto store_stage = [&](GemmStage& sg, int kb0, const i32x4 (&a)[kNA], const u32x4 (&w)[kNW],
-                         const uint32_t (&dwb)[2], const float (&dxv)[2]) {
+  // packed: the weight scales are in sw (fetch_fast), else one per word of sx.
+  auto store_stage = [&](GemmStage& sg, bool packed, const Staged& f) {
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int c = 256 * i + tid;
-      *reinterpret_cast<i32x4*>(&sg.a[(c % 8) / 2][c / 8][16 * (c % 2)]) = a[i];
+      const int t = c / 8, blk = (c % 8) / 2, hh = c % 2;
+      *reinterpret_cast<i32x4*>(&sg.a[blk].v[t / 32][0][0][0] + piece_off(t, hh)) = f.a[i];
     }
     if constexpr (WF == kWeightQ8) {
 #pragma unroll
       for (int i = 0; i < kNW; ++i) {
         const int c = 256 * i + tid;
-        *reinterpret_cast<u32x4*>(&sg.w[(c % 8) / 2][c / 8][16 * (c % 2)]) = w[i];
+        const int r = c / 8, blk = (c % 8) / 2, hh = c % 2;
+        *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, hh)) = f.w[i];
       }
     } else {
       const uint32_t m4 = 0x0F0F0F0Fu;
 #pragma unroll
       for (int i = 0; i < kNW; ++i) {
         const int c = 256 * i + tid;
-        const u32x4 qv = w[i];
+        const int r = c / 4, blk = c % 4;
+        const u32x4 qv = f.w[i];
         const u32x4 lo = {nib_to_s8(qv.x & m4), nib_to_s8(qv.y & m4), nib_to_s8(qv.z & m4), nib_to_s8(qv.w & m4)};
         const u32x4 hi = {nib_to_s8((qv.x >> 4) & m4), nib_to_s8((qv.y >> 4) & m4), nib_to_s8((qv.z >> 4) & m4),
                           nib_to_s8((qv.w >> 4) & m4)};
-        *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][0]) = lo;
-        *reinterpret_cast<u32x4*>(&sg.w[c % 4][c / 4][16]) = hi;
+        *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, 0)) = lo;
+        *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, 1)) = hi;
       }
     }
-    const int r = tid / 2;
-    const bool row_ok = m0 + r < M, tok_ok = n0 + r < B;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int blk = 2 * (tid % 2) + e;
-      const bool blk_ok = kb0 + blk < nb;
-      const float dwf = (row_ok && blk_ok) ? f16_bits_to_f32((uint16_t)dwb[e]) : 0.0f;
-      sg.dw[blk][r] = dwf;
-      sg.cw[blk][r] = -kMagic * dwf;
-      if (r < kTN) sg.dx[blk][r] = (tok_ok && blk_ok) ? dxv[e] : 0.0f;
+    if (tid < 128) {
+      // reinterpret the whole vector (hipcc miscompiles a bit cast of one
+      // element of a vector value: it reads element 0)
+      const f32x4 v = __builtin_bit_cast(f32x4, f.sx);
+      sg.dx[0][sr] = v.x;
+      sg.dx[1][sr] = v.y;
+      sg.dx[2][sr] = v.z;
+      sg.dx[3][sr] = v.w;
+    } else {
+      const uint32_t b0 = packed ? f.sw.x & 0xFFFFu : f.sx.x, b1 = packed ? f.sw.x >> 16 : f.sx.y;
+      const uint32_t b2 = packed ? f.sw.y & 0xFFFFu : f.sx.z, b3 = packed ? f.sw.y >> 16 : f.sx.w;
+      const float w0 = f16_bits_to_f32((uint16_t)b0), w1 = f16_bits_to_f32((uint16_t)b1);
+      const float w2 = f16_bits_to_f32((uint16_t)b2), w3 = f16_bits_to_f32((uint16_t)b3);
+      sg.dwc[0][sr] = f32x2{w0, -kMagic * w0};
+      sg.dwc[1][sr] = f32x2{w1, -kMagic * w1};
+      sg.dwc[2][sr] = f32x2{w2, -kMagic * w2};
+      sg.dwc[3][sr] = f32x2{w3, -kMagic * w3};
     }
   };
 
-  float acc[kIT][2][16];
+  float acc[kJT][16];
 #pragma unroll
-  for (int i = 0; i < kIT; ++i)
+  for (int j = 0; j < kJT; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+  // The seed lives in vector registers for the whole tile (the MFMA reads it
+  // as its accumulator input); materialised through asm so that the compiler
+  // does not keep it in scalar registers and copy it over before every MFMA.
   v16i seed;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) seed[r] = kMagicBits;
-
-  i32x4 fa[kNA];
-  u32x4 fw[kNW];
-  uint32_t fdw[2];
-  float fdx[2];
-  fetch(0, fa, fw, fdw, fdx);
-  if constexpr (kNBuf == 2) {
-    store_stage(st[0], 0, fa, fw, fdw, fdx);
-    __syncthreads();
+  for (int r = 0; r < 16; ++r) {
+    int v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(kMagicBits));
+    seed[r] = v;
   }
+  const int loff = piece_off(l32, h);  // this lane's 16-byte piece in a row-group region
 
+  // Stage pipeline: stage s + 1 is fetched (the fast form when it is full
+  // and the scale rows are aligned) while stage s is computed, and stored to
+  // the other LDS buffer after it; one barrier per stage.
+  Staged f;
+  fetch_any(0, f);
+  store_stage(st[0], false, f);
+  __syncthreads();
   int buf = 0;
   for (int kb0 = 0; kb0 < nb; kb0 += kKB) {
     const bool more = kb0 + kKB < nb;
-    if constexpr (kNBuf == 1) {
-      __syncthreads();  // the previous stage has been read
-      store_stage(st[0], kb0, fa, fw, fdw, fdx);
-      __syncthreads();
+    const bool fast = fast_ok && kb0 + 2 * kKB <= nb;
+    if (more) {  // in flight during this stage's compute
+      if (fast)
+        fetch_fast(kb0 + kKB, f);
+      else
+        fetch_any(kb0 + kKB, f);
     }
-    if (more) fetch(kb0 + kKB, fa, fw, fdw, fdx);  // in flight during this stage's compute
-    const GemmStage& sg = st[kNBuf == 2 ? buf : 0];
-
+    const GemmStage& sg = st[buf];
 #pragma unroll
     for (int blk = 0; blk < kKB; ++blk) {
       if (kb0 + blk < nb) {
-        v4i a[kIT], b[2];
-        float dw[2], cw[2];
+        const v4i a = *reinterpret_cast<const v4i*>(&sg.a[blk].v[wave][0][0][0] + loff);
+        float dx[16];
 #pragma unroll
-        for (int it = 0; it < kIT; ++it)
-          a[it] = *reinterpret_cast<const v4i*>(&sg.a[blk][wt * (kTN / 2) + it * 32 + l32][16 * h]);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const int wrow = ww * 64 + jt * 32 + l32;
-          b[jt] = *reinterpret_cast<const v4i*>(&sg.w[blk][wrow][16 * h]);
-          dw[jt] = sg.dw[blk][wrow];
-          cw[jt] = sg.cw[blk][wrow];
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wave * 32 + 8 * g + 4 * h]);
+          dx[4 * g + 0] = v.x;
+          dx[4 * g + 1] = v.y;
+          dx[4 * g + 2] = v.z;
+          dx[4 * g + 3] = v.w;
         }
-        // The four block products go to the matrix core first, into
-        // separate registers, so it works while the vector ALU rescales.
-        v16i Di[kIT][2];
-        v16f Fv[kIT][2];
+        // The 4 tiles of the block in a pipeline: tile jt + 1's operands are
+        // read and its MFMA issued before tile jt is rescaled, so at most two
+        // results and two weight fragments are live (the register budget of
+        // two workgroups per CU).  Scheduling barriers keep that order.
+        v4i b = *reinterpret_cast<const v4i*>(&sg.w[blk].v[0][0][0][0] + loff);
+        f32x2 dwc = sg.dwc[blk][l32];
+        // Whole result vectors are reinterpreted: hipcc (ROCm 7.2)
+        // miscompiles a per-element int <-> float bit cast of an MFMA
+        // result, propagating element 0 to every element.
+        v16i Di = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, seed, 0, 0, 0);
 #pragma unroll
-        for (int it = 0; it < kIT; ++it)
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            // Reinterpret the whole result vector at once: hipcc (ROCm 7.2)
-            // miscompiles a per-element int <-> float bit cast of an MFMA
-            // result, propagating element 0 to every element.
-            Di[it][jt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[it], b[jt], seed, 0, 0, 0);
-            Fv[it][jt] = __builtin_bit_cast(v16f, Di[it][jt]);
+        for (int jt = 0; jt < kJT; ++jt) {
+          v16i Dn;
+          f32x2 dwn;
+          if (jt + 1 < kJT) {
+            const v4i bn = *reinterpret_cast<const v4i*>(&sg.w[blk].v[jt + 1][0][0][0] + loff);
+            dwn = sg.dwc[blk][(jt + 1) * 32 + l32];
+            Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bn, seed, 0, 0, 0);
           }
-#pragma unroll
-        for (int it = 0; it < kIT; ++it) {
-          float dx[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wt * (kTN / 2) + it * 32 + 8 * g + 4 * h]);
-            dx[4 * g + 0] = v.x;
-            dx[4 * g + 1] = v.y;
-            dx[4 * g + 2] = v.z;
-            dx[4 * g + 3] = v.w;
-          }
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (WRITE_I) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float t = __builtin_fmaf(Fv[it][jt][r], dw[jt], cw[jt]);
-              acc[it][jt][r] = __builtin_fmaf(t, dx[r], acc[it][jt][r]);
-              if (WRITE_I) {
-                const int n = n0 + wt * (kTN / 2) + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int m = m0 + ww * 64 + jt * 32 + l32;
-                if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = Di[it][jt][r] - kMagicBits;
-              }
+              const int n = n0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              const int m = m0 + jt * 32 + l32;
+              if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = Di[r] - kMagicBits;
             }
+          }
+          // Two passes, so that no fma waits on the one just before it
+          // (back-to-back dependent vector instructions stall on gfx950):
+          // t = fl(I * d_w) in place of F for all 16 elements, then the sums.
+          v16f Fv = __builtin_bit_cast(v16f, Di);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Fv[r] = __builtin_fmaf(Fv[r], dwc.x, dwc.y);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[jt][r] = __builtin_fmaf(Fv[r], dx[r], acc[jt][r]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (jt + 1 < kJT) {
+            Di = Dn;
+            dwc = dwn;
           }
         }
       }
     }
-    if constexpr (kNBuf == 2) {
-      // The other buffer was last read in the previous stage, which every
-      // wave finished before the barrier that ended it.
-      if (more) store_stage(st[buf ^ 1], kb0 + kKB, fa, fw, fdw, fdx);
-      __syncthreads();
-      buf ^= 1;
-    }
+    // The other buffer was last read in the previous stage, which every wave
+    // finished before the barrier that ended it.
+    if (more) store_stage(st[buf ^ 1], fast, f);
+    __syncthreads();
+    buf ^= 1;
   }
 
 #pragma unroll
-  for (int it = 0; it < kIT; ++it)
+  for (int jt = 0; jt < kJT; ++jt)
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wt * (kTN / 2) + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int m = m0 + ww * 64 + jt * 32 + l32;
-        if (n < B && m < M) y[(int64_t)n * M + m] = acc[it][jt][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int n = n0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int m = m0 + jt * 32 + l32;
+      if (n < B && m < M) y[(int64_t)n * M + m] = acc[jt][r];
+    }
 }
 
 
@@ -282,7 +378,7 @@ template <bool WRITE_I, bool GROUPED, int WF = kWeightQ4>
 __global__ __launch_bounds__(kGemmThreads, WRITE_I ? 1 : 2) void gemm_kernel(
     GemvProblem p0, const GemvProblem* __restrict__ table, const int32_t* __restrict__ tile_map,
     int n_tiles, int B, int32_t* __restrict__ Iout) {
-  __shared__ __align__(16) GemmStage st[kNBuf];
+  __shared__ __align__(16) GemmStage st[2];
 
   // Tile of this workgroup.  The tile list is dealt to the XCDs (workgroup
   // bid runs on XCD bid % 8) in chunks of n_nt consecutive tiles -- the token
