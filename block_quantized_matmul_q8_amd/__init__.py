@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.mul_mat_id_q4q8_workspace.argtypes = [i64, i64, i64]
     L.mul_mat_id_q4q8_workspace.restype = sz
     L.mul_mat_id_q4q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+    L.mul_mat_id_q4q8_noalloc.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp]
     L.mul_mat_q4q8_rmsnorm.argtypes = [vp, vp, i64, i64, vp, vp, f32, u32, i64, vp, vp]
     L.moe_expert_sum_f32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.q8_quantize_rmsnorm_add.argtypes = [vp, i64, i64, vp, vp, i64, f32, vp, vp, vp, vp]
@@ -100,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.q4q8_set_path.argtypes = [i32]
     L.q4q8_dispatch_counts.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     for name in ("q4_quantize", "q8_quantize_rmsnorm", "mul_mat_q4q8", "mul_mat_q4q8_blocksums",
-                 "mul_mat_id_q4q8", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
+                 "mul_mat_id_q4q8", "mul_mat_id_q4q8_noalloc", "q4q8_set_path", "q4q8_dispatch_counts", "mul_mat_q4q8_rmsnorm",
                  "q4q8_group_build", "mul_mat_q4q8_group", "moe_expert_sum_f32", "q8_quantize_rmsnorm_add",
                  "q8_quantize_swiglu", "q8_0_quantize", "mul_mat_q8_0_q8", "mul_mat_q8_0_q8_blocksums"):
         getattr(L, name).restype = i32
@@ -502,6 +503,33 @@ def mul_mat_id_q4q8(qs, d, xq, xd, ids, y=None, ws=None, stream=None):
     _check("mul_mat_id_q4q8",
            lib().mul_mat_id_q4q8(_ptr(qs), _ptr(d), E, M, K, _ptr(xq), _ptr(xd), S, _ptr(ids), T, top_k, _ptr(y),
                                  _ptr(ws), ws.numel(), _stream(stream, qs.device)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20  # Q4Q8_NOALLOC_SCRATCH_BYTES of q4q8.h
+
+
+def mul_mat_id_q4q8_noalloc(qs, d, xq, xd, ids, y, stream=None):
+    """mul_mat_id_q4q8 through the entry point that allocates nothing: the
+    routing workspace is the library's per-device scratch (so y must be given;
+    calls on one GPU must be ordered on one stream)."""
+    _need(qs, "qs", (torch.uint8,), 3)
+    _need(d, "d", _F16_BITS, 3)
+    _need(xq, "xq", (torch.int8,), 3)
+    _need(xd, "xd", (torch.float32,), 3)
+    _need(ids, "ids", (torch.int32,), 2)
+    _need(y, "y", (torch.float32,))
+    E, M, half = qs.shape
+    K = 2 * half
+    T, S, K2 = xq.shape
+    top_k = ids.shape[1]
+    if K2 != K or ids.shape[0] != T or d.shape != (E, M, K // QK) or xd.shape != (T, S, K // QK):
+        raise ValueError("shape mismatch")
+    if y.numel() != T * top_k * M:
+        raise ValueError("y shape does not match")
+    _check("mul_mat_id_q4q8_noalloc",
+           lib().mul_mat_id_q4q8_noalloc(_ptr(qs), _ptr(d), E, M, K, _ptr(xq), _ptr(xd), S, _ptr(ids), T, top_k,
+                                         _ptr(y), _stream(stream, qs.device)))
     return y
 
 

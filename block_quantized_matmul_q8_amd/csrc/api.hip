@@ -288,33 +288,65 @@ Q4Q8_EXPORT size_t mul_mat_id_q4q8_workspace(int64_t E, int64_t T, int64_t top_k
   return q4q8::moe_workspace_bytes(E, T, top_k);
 }
 
-Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
-                                const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
-                                int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
+// Checks shared by the two routed entry points (everything but the workspace).
+static int check_moe_args(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K, const int8_t* xq,
+                          const float* xd, int64_t n_x_slots, const int32_t* ids, int64_t T, int64_t top_k,
+                          const float* y) {
   int st;
   if ((st = check_k(K)) || (st = check_dims(M, T))) return st;
   if (E <= 0 || E > 4096) return fail(Q4Q8_E_ARG, "E = %lld must be in [1, 4096]", (long long)E);
   if (top_k <= 0 || top_k > 64) return fail(Q4Q8_E_ARG, "top_k = %lld must be in [1, 64]", (long long)top_k);
   if (n_x_slots != 1 && n_x_slots != top_k) return fail(Q4Q8_E_ARG, "n_x_slots must be 1 or top_k");
   if (T * top_k > 65536) return fail(Q4Q8_E_ARG, "T * top_k exceeds 65536");
-  if (M == 0 || T == 0) return ok();
-  if (!qs || !d || !xq || !xd || !ids || !y || !ws) return fail(Q4Q8_E_ARG, "null pointer argument");
-  if (!aligned(qs, 16) || !aligned(xq, 16) || !aligned(ws, 16) || !aligned(d, 2) || !aligned(xd, 4) ||
-      !aligned(ids, 4) || !aligned(y, 4))
+  if (M == 0 || T == 0) return Q4Q8_OK;
+  if (!qs || !d || !xq || !xd || !ids || !y) return fail(Q4Q8_E_ARG, "null pointer argument");
+  if (!aligned(qs, 16) || !aligned(xq, 16) || !aligned(d, 2) || !aligned(xd, 4) || !aligned(ids, 4) ||
+      !aligned(y, 4))
     return fail(Q4Q8_E_ALIGN, "misaligned pointer argument");
-  if (ws_bytes < q4q8::moe_workspace_bytes(E, T, top_k))
-    return fail(Q4Q8_E_ARG, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
-                q4q8::moe_workspace_bytes(E, T, top_k));
   if (!q4q8::gemv_supported(1, K, 8))
     return fail(Q4Q8_E_UNSUPPORTED, "K = %lld too large for the routed kernel", (long long)K);
   if (q4q8::moe_schedule_cost_bound(E, M, K, T * top_k) >= INT32_MAX)
     return fail(Q4Q8_E_UNSUPPORTED, "M = %lld with E = %lld is too large for the routed schedule", (long long)M,
                 (long long)E);
+  return Q4Q8_OK;
+}
+
+Q4Q8_EXPORT int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
+                                const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
+                                int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_moe_args(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y))) return st;
+  if (M == 0 || T == 0) return ok();
+  if (!ws) return fail(Q4Q8_E_ARG, "null pointer argument (ws)");
+  if (!aligned(ws, 16)) return fail(Q4Q8_E_ALIGN, "misaligned pointer argument (ws)");
+  if (ws_bytes < q4q8::moe_workspace_bytes(E, T, top_k))
+    return fail(Q4Q8_E_ARG, "workspace of %zu bytes is smaller than the %zu required", ws_bytes,
+                q4q8::moe_workspace_bytes(E, T, top_k));
   if ((st = check_device())) return st;
   g_counts[2].fetch_add(1, std::memory_order_relaxed);
   return launched(q4q8::launch_moe(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y, ws,
                                    static_cast<hipStream_t>(stream)),
                   "mul_mat_id_q4q8");
+}
+
+Q4Q8_EXPORT int mul_mat_id_q4q8_noalloc(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
+                                        const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
+                                        int64_t T, int64_t top_k, float* y, void* stream) {
+  int st;
+  if ((st = check_moe_args(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y))) return st;
+  if (M == 0 || T == 0) return ok();
+  const size_t need = q4q8::moe_workspace_bytes(E, T, top_k);
+  if (need > q4q8::moe_scratch_bytes())
+    return fail(Q4Q8_E_UNSUPPORTED, "routing of E = %lld, T * top_k = %lld needs %zu bytes, beyond the %zu-byte scratch",
+                (long long)E, (long long)(T * top_k), need, q4q8::moe_scratch_bytes());
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  hipError_t err = q4q8::moe_scratch(&ws);
+  if (err != hipSuccess) return fail(Q4Q8_E_LAUNCH, "scratch address: %s", hipGetErrorString(err));
+  g_counts[2].fetch_add(1, std::memory_order_relaxed);
+  return launched(q4q8::launch_moe(qs, d, E, M, K, xq, xd, n_x_slots, ids, T, top_k, y, ws,
+                                   static_cast<hipStream_t>(stream)),
+                  "mul_mat_id_q4q8_noalloc");
 }
 
 Q4Q8_EXPORT int moe_expert_sum_f32(const float* y, const float* w, int64_t T, int64_t top_k, int64_t M,

@@ -225,6 +225,10 @@ Q4Q8_HIDDEN hipError_t launch_gemm(const GemvProblem& p, const GemvProblem* tabl
                                    int64_t n_tiles, int64_t B, int32_t* I, hipStream_t s,
                                    int wf = kWeightQ4);
 Q4Q8_HIDDEN size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+// The library-owned routing scratch of the current device (device address)
+// and its size: the workspace of mul_mat_id_q4q8_noalloc.
+Q4Q8_HIDDEN size_t moe_scratch_bytes();
+Q4Q8_HIDDEN hipError_t moe_scratch(void** out);
 Q4Q8_HIDDEN hipError_t launch_moe_expert_sum(const float* y, const float* w, int64_t T, int64_t top_k,
                                              int64_t M, float* out, hipStream_t s);
 // Upper bound of the routed launch's total schedule cost (it must fit int32).

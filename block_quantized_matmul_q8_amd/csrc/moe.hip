@@ -17,6 +17,7 @@
 #include <utility>
 #include <vector>
 
+#include "../../include/q4q8.h"
 #include "gemv_dev.h"
 
 namespace q4q8 {
@@ -338,6 +339,38 @@ static int64_t moe_resident_workgroups(const void* kernel) {
   const int64_t n = (int64_t)per_cu * cus;
   cache.push_back({{kernel, dev}, n});
   return n;
+}
+
+// Built-in scratch of the allocation-free routed entry point: the routing
+// workspace (offsets, list, rank, selected experts, cost prefix, control
+// words) of a call that cannot bring one.  Every valid call fits (E <= 4096
+// and T * top_k <= 65536 need at most 573,464 bytes).  Each GPU holds its own
+// copy until the process ends; in host code `scratch` is only a host-side
+// stand-in, so kernels get the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kMoeScratchBytes = Q4Q8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+size_t moe_scratch_bytes() { return kMoeScratchBytes; }
+
+hipError_t moe_scratch(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDev] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 int64_t moe_schedule_cost_bound(int64_t E, int64_t M, int64_t K, int64_t n) {

@@ -304,6 +304,29 @@ int mul_mat_id_q4q8(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, 
                     int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mul_mat_id_q4q8_noalloc -- mul_mat_id_q4q8 without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layouts, results (bit for bit) and errors as mul_mat_id_q4q8; the routing
+ * workspace is instead a library-owned scratch array of
+ * Q4Q8_NOALLOC_SCRATCH_BYTES in each GPU's memory, held from the first call on
+ * that device until the process ends.  The call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).
+ *   - Every call on one device shares that device's scratch, which keeps the
+ *     last call's contents: calls that overlap on one GPU (on different
+ *     streams, or from different threads without ordering) race.  Order them
+ *     on one stream.  No content needs clearing between calls (the routing
+ *     writes every word it reads).
+ *   - A routing that needs more than the scratch returns Q4Q8_E_UNSUPPORTED
+ *     with a message; every call valid for mul_mat_id_q4q8 (E <= 4096,
+ *     T * top_k <= 65536) needs at most 573,464 bytes and fits.
+ */
+#define Q4Q8_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+int mul_mat_id_q4q8_noalloc(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M, int64_t K,
+                            const int8_t* xq, const float* xd, int64_t n_x_slots, const int32_t* ids,
+                            int64_t T, int64_t top_k, float* y, void* stream);
+
+/*
  * moe_expert_sum_f32 -- sum of the expert planes of a MUL_MAT_ID result.  The
  * OpenVINO page ("llama.cpp b10981发布：OpenVINO后端优化有状态解码与GPU MoE推理")
  * describes those planes being added by a chain of ADD ops after the routing
