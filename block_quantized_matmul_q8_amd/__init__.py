@@ -58,7 +58,7 @@ class GroupPlan(ctypes.Structure):
                 ("n_prologue", ctypes.c_int32), ("n_windows", ctypes.c_int64), ("max_k", ctypes.c_int64),
                 ("map_offset", ctypes.c_int64), ("prologue_offset", ctypes.c_int64),
                 ("table_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("weight_formats", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("weight_formats", ctypes.c_int32), ("max_prologue_k", ctypes.c_int32)]
 
 
 _lib = None

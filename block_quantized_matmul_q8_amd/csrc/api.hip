@@ -534,6 +534,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   plan->workspace_bytes = ws_total;
   plan->weight_formats = 0;
   for (const q4q8::GemvProblem& r : recs) plan->weight_formats |= 1 << r.wf;
+  plan->max_prologue_k = 0;
+  for (const Input& in : inputs) plan->max_prologue_k = std::max(plan->max_prologue_k, (int32_t)in.K);
   plan->magic = kGroupMagic;
   if (!table_host) return ok();
   const char* why = nullptr;
@@ -593,7 +595,9 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
       plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
       plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
       plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob) ||
-      plan->weight_formats < 1 || plan->weight_formats > 3)
+      plan->weight_formats < 1 || plan->weight_formats > 3 || plan->max_prologue_k < 0 ||
+      plan->max_prologue_k > plan->max_k || plan->max_prologue_k % q4q8::kQK != 0 ||
+      plan->max_prologue_k > q4q8::kMaxPrologueK || (plan->n_prologue > 0) != (plan->max_prologue_k > 0))
     return fail(Q4Q8_E_ARG, "corrupt plan");
   // the kernel instance: single-format groups take the leaner ones
   const int wf = plan->weight_formats == 1   ? q4q8::kWeightQ4
@@ -607,7 +611,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
     g_counts[3].fetch_add(1, std::memory_order_relaxed);
     st = launched(q4q8::launch_group_prologue(
                       reinterpret_cast<const q4q8::PrologueJob*>(base + plan->prologue_offset),
-                      plan->n_prologue, plan->B, plan->max_k, s),
+                      plan->n_prologue, plan->B, plan->max_prologue_k, s),
                   "mul_mat_q4q8_group (prologue pass)");
     if (st) return st;
   }

@@ -256,7 +256,8 @@ typedef struct q4q8_group_plan {
   int64_t table_bytes;     /* size of the table image */
   int64_t workspace_bytes; /* device workspace the prologue pass writes (0 if none) */
   int32_t weight_formats;  /* 1: all products Q4, 2: all Q8_0, 3: both (selects the kernel instance) */
-  int32_t reserved;
+  int32_t max_prologue_k;  /* largest K among the fp32 inputs of the prologue pass (0 if none);
+                              sizes that pass's LDS, which Q8-plane products never enter */
 } q4q8_group_plan;
 /* Every field is written by q4q8_group_build and read as it left them: a
  * launch checks their consistency but cannot detect every edited value. */

@@ -251,6 +251,7 @@ def test_group_build_layout_is_host_only():
     # per lane for each of the 4 waves: 64 rows at K = 2048 (one 32-block per
     # lane), 16 rows at K = 8192 (four per lane)
     assert plan.n_records == 5 and plan.B == 1 and plan.n_prologue == 3 and plan.max_k == 8192
+    assert plan.max_prologue_k == 8192
     assert plan.n_windows == 1 + 4 + 2 + 1 + 1
     # Q8 planes per job: 8192 codes then 256 fp32 scales, 16-byte aligned
     assert plan.workspace_bytes == 3 * (8192 + 1024)
@@ -354,6 +355,19 @@ def test_group_build_validation_is_host_only():
         assert ei.value.status == code
 
 
+def test_group_prologue_lds_sized_by_prologue_inputs_only():
+    """A tiled group mixing an fp32-row product (K = 4096) with a Q8-plane
+    product of very long K: the prologue pass quantises only the former, so
+    its LDS is sized by max_prologue_k = 4096, not by max_k (2^20 here would
+    ask for several hundred KiB of LDS and fail the whole call)."""
+    big = _desc(K=1 << 20, M=16)
+    rows = _desc(xq=None, xd=None, x=512, g=768, K=4096, M=128)
+    _, plan = _build([big, rows], 64, 1 << 20, 1 << 20)
+    assert plan.max_k == 1 << 20 and plan.max_prologue_k == 4096 and plan.n_prologue == 1
+    _, plan = _build([_desc(K=4096)], 64)
+    assert plan.max_prologue_k == 0 and plan.n_prologue == 0
+
+
 def test_group_launch_rejects_foreign_plans():
     L = q.lib()
     plan = q.GroupPlan()
@@ -361,7 +375,8 @@ def test_group_launch_rejects_foreign_plans():
     _, good = _build([_desc()], 1)
     assert L.mul_mat_q4q8_group(None, ctypes.byref(good), None) == q.Q4Q8_E_ARG
     assert L.mul_mat_q4q8_group(ctypes.c_void_p(264), ctypes.byref(good), None) == q.Q4Q8_E_ALIGN
-    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 70000)):
+    for field, value in (("n_windows", 0), ("max_k", 40), ("table_bytes", 12), ("n_prologue", 5), ("B", 70000),
+                         ("max_prologue_k", 64)):
         bad = q.GroupPlan.from_buffer_copy(good)
         setattr(bad, field, value)
         assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, field
