@@ -37,6 +37,44 @@ __host__ __device__ __forceinline__ int next_pow2_int(int n) {
   return p;
 }
 
+// Sum over the 64 lanes of a wave as a pairwise tree: level k adds lane
+// groups of 2^k that are neighbours (lane ^ 2^k), so every lane ends with the
+// tree sum of the wave (fp32 addition is commutative, so the operand order
+// within a pair does not matter).  Levels 1..8 are DPP lane permutations
+// folded into the add (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror: each maps a lane group onto its neighbour group), levels 16 and
+// 32 v_permlane16/32_swap, whose two results hold the pair's two values in
+// every lane -- no LDS round trip at any level.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+  v = __fadd_rn(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = __fadd_rn(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = __fadd_rn(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = __fadd_rn(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  // Elements of the swap pairs are copied into scalars before any bit cast
+  // (hipcc miscompiles a bit cast of one element of a vector value).
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                    false, false);
+  const unsigned a0 = p16[0], a1 = p16[1];
+  v = __fadd_rn(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                    false, false);
+  const unsigned b0 = p32[0], b1 = p32[1];
+  return __fadd_rn(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
+// Largest |v_j| of a block, as a tree (the maximum does not depend on the
+// order, and a tree is 5 dependent steps instead of 31).
+__device__ __forceinline__ float block_amax(const float (&v)[kQK]) {
+  float m[kQK / 2];
+#pragma unroll
+  for (int j = 0; j < kQK / 2; ++j) m[j] = fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1]));
+#pragma unroll
+  for (int w = kQK / 4; w >= 1; w /= 2)
+#pragma unroll
+    for (int j = 0; j < w; ++j) m[j] = fmaxf(m[2 * j], m[2 * j + 1]);
+  return m[0];
+}
+
 // RMS scale s of one row, computed cooperatively by all `nthreads` threads of
 // the workgroup (every thread must call it).  `red` is LDS scratch of 2 * P
 // floats; `s_slot` one LDS float.  Returns s to every thread.
@@ -76,9 +114,7 @@ __device__ __forceinline__ float wg_rms_scale(const float* __restrict__ xr, int 
 // all-zero block), q = roundf(v * id) clamped to [-127, 127].  packed[8]
 // holds the codes in index order (4 per dword, little-endian), sum their sum.
 __device__ __forceinline__ void q8_pack_block(const float (&v)[kQK], uint32_t (&packed)[8], float& d, int& sum) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kQK; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const float amax = block_amax(v);
   d = __fdiv_rn(amax, 127.0f);
   const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
   sum = 0;
@@ -196,9 +232,7 @@ __device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
 #pragma unroll
         for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(xv[h][j], xv[h][j]));
       }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) acc = __fadd_rn(acc, __shfl_xor(acc, off, 64));
-      gsum[h] = acc;
+      gsum[h] = wave_tree_sum(acc);
     }
     if (lane == 0) {
       groups[wave] = gsum[0];
