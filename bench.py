@@ -32,7 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-extras]
        python bench.py --kernel-only 10      (launches for rocprofv3 runs)
        python bench.py --gemm-only 10        (prefill GEMM launches for rocprofv3 runs)
        python bench.py --moe-only 10         (routed MoE launches for rocprofv3 runs)
-       python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (traffic summary)
+       python bench.py --pmc-summary FETCH_DIR WRITE_DIR [REQ_DIR]   (traffic summary)
 """
 from __future__ import annotations
 
@@ -189,24 +189,34 @@ def time_direct(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def gpu_clocks():
-    """Current shader (sclk) and memory (mclk) clocks of the GPU, as rocm-smi
-    reports them (read-only query), else from the sysfs DPM tables (the active
-    level is marked with '*'); None where neither is readable."""
+def gpu_clocks(busy=None):
+    """Shader (sclk) and memory (mclk) clocks as rocm-smi reports them (a
+    read-only query), taken while `busy` keeps the GPU loaded (it is called
+    over and over until the query returns, at most 20 s); from the sysfs DPM
+    tables (active level marked '*') if rocm-smi gives nothing.  Only values
+    that carry a frequency unit are kept."""
     import glob
     import subprocess
 
-    out = {"sclk": None, "mclk": None, "source": None}
+    import torch
+    out = {"sclk": None, "mclk": None, "source": None, "under_load": busy is not None}
     try:
-        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(res.stdout)
+        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+        t0 = time.perf_counter()
+        while busy is not None and proc.poll() is None and time.perf_counter() - t0 < 20:
+            busy()
+            torch.cuda.synchronize()
+        stdout, _ = proc.communicate(timeout=20)
+        data = json.loads(stdout)
         card = data[sorted(data)[0]]
         for k, v in card.items():
-            kl = k.lower()
-            if kl.startswith("sclk"):
-                out["sclk"] = v
-            elif kl.startswith("mclk"):
-                out["mclk"] = v
+            kl, vs = k.lower(), str(v)
+            if "hz" not in vs.lower():
+                continue
+            for key in ("sclk", "mclk"):
+                if kl.startswith(key):
+                    out[key] = vs
         out["source"] = "rocm-smi --showclocks"
     except Exception:
         pass
@@ -353,8 +363,12 @@ def bench_decode_1b(args, dev, report):
     # headline: the step captured in a HIP graph, median of per-replay times
     g_step = capture(lambda: step())
     ms, ms_mean, ms_min, ms_max, wall = time_graph_replays(g_step, args.steps, args.warmup)
+
+    def busy():
+        for _ in range(200):
+            g_step.replay()
+    clocks = gpu_clocks(busy)
     del g_step
-    clocks = gpu_clocks()
     value = model.step_bytes / (ms * 1e-3) / 1e9
     # the same step launched directly, back to back (no graph)
     ms_direct, _ = time_direct(lambda: step(), args.steps, args.warmup)
@@ -600,9 +614,43 @@ def moe_only(n, dev):
     print(f"[moe-only] {n} MoE steps (2 routed calls each, rotating {len(copies)} weight copies)", flush=True)
 
 
-def pmc_summary(fetch_dir, write_dir):
+def trace_summary(trace_dir):
+    """Per-kernel duration table of a rocprofv3 --kernel-trace run (csv
+    output): calls, mean, median, min and max in microseconds, plus the
+    registers and LDS of each kernel of this library, sorted by total time."""
+    import csv
+    import glob
+    import statistics
+
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    dur, res = {}, {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("void ", "", 1).split("(")[0]
+                if name.startswith("at::native::"):
+                    name = "at::native:: (torch set-up kernels)"
+                dur.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                if name.startswith("q4q8::"):
+                    res[name] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"])
+    print(f"{'kernel':58s} {'calls':>6s} {'mean us':>9s} {'median us':>10s} {'min us':>9s} {'max us':>9s}")
+    for name, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name[:58]:58s} {len(v):6d} {statistics.fmean(v):9.2f} {statistics.median(v):10.2f} "
+              f"{min(v):9.2f} {max(v):9.2f}")
+    if res:
+        print("\nresources (arch VGPRs, accumulation VGPRs, SGPRs, LDS bytes) per kernel instance:")
+        for name, (v, a, sg, lds) in sorted(res.items()):
+            print(f"  {name}: {v} / {a} / {sg} / {lds}")
+
+
+def pmc_summary(fetch_dir, write_dir, req_dir=None):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the streaming kernel,
-    scaled by what the same counters read for the 256 MiB copy."""
+    scaled by what the same counters read for the 256 MiB copy; with req_dir
+    (a pass over TCC_EA0_RDREQ_sum, TCC_EA0_RDREQ_32B_sum, TCC_EA0_RDREQ_64B_sum,
+    TCC_EA0_RDREQ_128B_sum), the read bytes are also counted directly from the
+    request sizes, which explains the fetch factor."""
     import csv
     import glob
     import statistics
@@ -652,6 +700,31 @@ def pmc_summary(fetch_dir, write_dir):
     rec = {"traffic_bytes_per_launch": int(round(traffic)), "algorithmic_bytes": step_bytes,
            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
            "source_hash": kernel_source_hash()}
+    if req_dir:
+        req = {c: read(req_dir, c) for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                                             "TCC_EA0_RDREQ_128B_sum")}
+
+        def direct(needle):
+            n = {c: pick(v, needle) for c, v in req.items()}
+            b = 32 * n["TCC_EA0_RDREQ_32B_sum"] + 64 * n["TCC_EA0_RDREQ_64B_sum"] + 128 * n["TCC_EA0_RDREQ_128B_sum"]
+            return b, n
+        cb, cn = direct("copyBuffer")
+        gb, gn = direct("gemv_kernel")
+        lines += [
+            "cross-check from the read-request sizes (bytes = 32 x 32B + 64 x 64B + 128 x 128B requests; no calibration):",
+            f"  copy: requests {cn['TCC_EA0_RDREQ_sum']:.0f} (32B {cn['TCC_EA0_RDREQ_32B_sum']:.0f}, 64B "
+            f"{cn['TCC_EA0_RDREQ_64B_sum']:.0f}, 128B {cn['TCC_EA0_RDREQ_128B_sum']:.0f}) -> {cb / 2**20:.1f} MiB "
+            f"for 256 MiB read ({cb / copy_bytes:.4f}x)",
+            f"  streaming kernel: requests {gn['TCC_EA0_RDREQ_sum']:.0f} (32B {gn['TCC_EA0_RDREQ_32B_sum']:.0f}, 64B "
+            f"{gn['TCC_EA0_RDREQ_64B_sum']:.0f}, 128B {gn['TCC_EA0_RDREQ_128B_sum']:.0f}) -> {gb / 1e6:.2f} MB read "
+            f"({(gb + gem_w * w_factor) / step_bytes:.3f}x algorithmic with the writes)",
+            f"  raw FETCH_SIZE / (64 B x requests): copy {copy_f / (64 * cn['TCC_EA0_RDREQ_sum']):.4f}, streaming "
+            f"kernel {gem_f / (64 * gn['TCC_EA0_RDREQ_sum']):.4f}: FETCH_SIZE's expression on this GPU counts a "
+            "request as 64 B unless TCC_BUBBLE marks it 128 B, and nearly every read here is a 128-byte request, "
+            "so the raw counter reads half the bytes; that is the copy's factor of 2",
+        ]
+        rec["direct_read_bytes_per_launch"] = int(round(gb))
+        rec["copy_direct_over_moved"] = round(cb / copy_bytes, 4)
     print("\n".join(lines))
     print("RESULT " + json.dumps(rec))
 
@@ -925,8 +998,8 @@ def cpu_baseline(model, seconds=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-extras", action="store_true", help="only the headline step and its roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -938,14 +1011,20 @@ def main():
                     help="launch N routed MoE steps and exit")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="launch N steps and N streaming passes (after a calibration copy) and exit")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs of --kernel-only (no GPU needed)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace csv run (no GPU needed)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [REQ_DIR]: summarise rocprofv3 --pmc runs of --kernel-only "
+                         "(no GPU needed)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the path does not shard across GPUs in this build "
+        print(f"bench.py measures one GPU only: this library runs the product on one GPU and does not shard it across GPUs "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 
