@@ -69,9 +69,12 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
-    L = ctypes.CDLL(LIB_PATH)
+    # Q4Q8_LIB: another build of the same sources (the host-sanitizer build
+    # that the test suite loads in a child process)
+    path = os.environ.get("Q4Q8_LIB", LIB_PATH)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
     vp, i64, i32, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
                                   ctypes.c_float, ctypes.c_size_t)
     L.q4q8_last_error.restype = ctypes.c_char_p

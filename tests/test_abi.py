@@ -185,6 +185,7 @@ def test_set_path_and_counters():
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import block_quantized_matmul_q8_amd as pkg
     monkeypatch.setattr(pkg, "_lib", None)
+    monkeypatch.delenv("Q4Q8_LIB", raising=False)
     monkeypatch.setattr(pkg, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         pkg.lib()
