@@ -8,8 +8,9 @@ with their own norm weights g ~ N(1, 0.1); every row goes through the fused
 RMSNorm * g -> Q8 prologue once and the products that share it read the same
 codes.  The step is one grouped call: a prologue pass over the 64 rows, then
 one streaming launch over the 112 products, captured in a HIP graph and
-replayed: value = algorithmic bytes per step / median per-replay time (HIP
-events around each replay), where the bytes are the
+replayed back to back: value = algorithmic bytes per step / mean replay time
+over the timed replays (two timing-only HIP events around them), where the
+bytes are the
 Q4 weights (18 B per 32), each matrix's Q8 activation (36 B per 32) and its
 fp32 output.
 
@@ -28,11 +29,15 @@ Also reported in the same JSON line (not part of value):
                 int8 TOPS against 5.0 POPS;
   moe           MUL_MAT_ID decode (64 experts, 16 tokens, top-8).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--skip-extras]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--skip-extras]
        python bench.py --kernel-only 10      (launches for rocprofv3 runs)
        python bench.py --gemm-only 10        (prefill GEMM launches for rocprofv3 runs)
        python bench.py --moe-only 10         (routed MoE launches for rocprofv3 runs)
+       python bench.py --q8-0-only 10        (Q8_0 weight launches for rocprofv3 runs)
+       python bench.py --decode-8b-only B 10 (Llama-3-8B-shaped decode steps at batch B for rocprofv3 runs)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [REQ_DIR]   (traffic summary)
+       python bench.py --trace-summary DIR   (kernel durations of a --kernel-trace run)
+       python bench.py --counter-summary KERNEL DIR [DIR ...]   (counters of --pmc runs)
 """
 from __future__ import annotations
 
@@ -143,30 +148,40 @@ class TimingEvents:
 
 
 def time_graph_replays(g, steps, warmup):
-    """Per-replay times of a captured step: `warmup` replays, a synchronisation,
-    then `steps` replays back to back on the current stream with a timing
-    event recorded before the first and after each one (so replay i is timed
-    by events i and i + 1), and a synchronisation.  Returns (median ms, mean
-    ms, min ms, max ms, wall seconds of the timed region)."""
+    """A captured step replayed back to back: `warmup` replays, a
+    synchronisation, then `steps` replays between two timing-only HIP events
+    on the current stream and a synchronisation (the timed region; its mean
+    per replay is the step time).  A second pass of `steps` replays records
+    an event after every replay as well, for the distribution of single
+    replays (median, min, max; those extra events cost a few microseconds per
+    replay, so the second pass is not the step time).  Returns (mean ms of the
+    timed region, wall seconds of it, median ms, min ms, max ms of pass 2)."""
     import statistics
 
     import torch
     stream = torch.cuda.current_stream()
-    ev = TimingEvents(steps + 1)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    ev = TimingEvents(2)
     t0 = time.perf_counter()
+    ev.record(0, stream)
+    for _ in range(steps):
+        g.replay()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = ev.elapsed_ms(0, 1) / steps
+    ev.close()
+    ev = TimingEvents(steps + 1)
     ev.record(0, stream)
     for i in range(steps):
         g.replay()
         ev.record(i + 1, stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [ev.elapsed_ms(i, i + 1) for i in range(steps)]
-    mean = ev.elapsed_ms(0, steps) / steps
     ev.close()
-    return statistics.median(per), mean, min(per), max(per), wall
+    return mean, wall, statistics.median(per), min(per), max(per)
 
 
 def time_direct(fn, steps, warmup):
@@ -360,9 +375,9 @@ def bench_decode_1b(args, dev, report):
 
     model = DecodeModel(wl.LLAMA_3_2_1B, 16, 1, 0, dev)
     step, stream_only = decode_1b_groups(model)
-    # headline: the step captured in a HIP graph, median of per-replay times
+    # headline: the step captured in a HIP graph, replayed back to back
     g_step = capture(lambda: step())
-    ms, ms_mean, ms_min, ms_max, wall = time_graph_replays(g_step, args.steps, args.warmup)
+    ms, wall, ms_med, ms_min, ms_max = time_graph_replays(g_step, args.steps, args.warmup)
 
     def busy():
         for _ in range(200):
@@ -393,12 +408,13 @@ def bench_decode_1b(args, dev, report):
         "step_bytes": model.step_bytes,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "launches_per_step": 2,
-        "timing": (f"the step captured in a HIP graph; {args.warmup} warm-up replays, then {args.steps} "
-                   "replays back to back with a HIP event (created with hipEventDisableSystemFence, a "
-                   "timing-only event) before the first and after each; value and ms_per_step from the "
-                   "median per-replay time"),
-        "graph_replay_stats": {"median_ms": round(ms, 5), "mean_ms": round(ms_mean, 5), "min_ms": round(ms_min, 5),
-                               "max_ms": round(ms_max, 5)},
+        "timing": (f"the step captured in a HIP graph; {args.warmup} warm-up replays and a synchronisation, "
+                   f"then {args.steps} replays back to back between two HIP events (created with "
+                   "hipEventDisableSystemFence, timing-only events) and a synchronisation; value and "
+                   "ms_per_step from the mean replay time of that region"),
+        "graph_replay_stats": {"median_ms": round(ms_med, 5), "min_ms": round(ms_min, 5), "max_ms": round(ms_max, 5),
+                               "how": (f"a second pass of {args.steps} replays with an event after each one; "
+                                       "those events add a few microseconds to every replay")},
         "direct_launches": {"GB/s": round(model.step_bytes / (ms_direct * 1e-3) / 1e9, 1),
                             "ms_per_step": round(ms_direct, 5),
                             "timing": "the same step launched directly, back to back, mean over the timed steps"},
@@ -614,6 +630,27 @@ def moe_only(n, dev):
     print(f"[moe-only] {n} MoE steps (2 routed calls each, rotating {len(copies)} weight copies)", flush=True)
 
 
+def decode_8b_only(B, n, dev):
+    """Launch sequence for profiler runs of the Llama-3-8B-shaped decode group
+    (8 layers x 7 Q4 matrices) at batch B: n grouped steps (prologue pass +
+    streaming pass)."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    model = DecodeModel(wl.LLAMA_3_8B, 8, B, 1, dev)
+    probs = []
+    for l in range(8):
+        probs += model.problems(l)
+    grp = q.Group(probs, B=B)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        grp()
+    torch.cuda.synchronize()
+    print(f"[decode-8b-only] B={B}: {n} grouped steps, {model.step_bytes} algorithmic bytes each", flush=True)
+
+
 def trace_summary(trace_dir):
     """Per-kernel duration table of a rocprofv3 --kernel-trace run (csv
     output): calls, mean, median, min and max in microseconds, plus the
@@ -643,6 +680,33 @@ def trace_summary(trace_dir):
         print("\nresources (arch VGPRs, accumulation VGPRs, SGPRs, LDS bytes) per kernel instance:")
         for name, (v, a, sg, lds) in sorted(res.items()):
             print(f"  {name}: {v} / {a} / {sg} / {lds}")
+
+
+def counter_summary(needle, dirs):
+    """Per-dispatch medians of every counter that rocprofv3 --pmc runs (csv
+    output, one directory per pass) collected for the kernels whose name
+    contains `needle`; dispatch durations come from no counter, so none here."""
+    import csv
+    import glob
+    import statistics
+
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            per = {}
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if needle not in r["Kernel_Name"]:
+                        continue
+                    key = (r["Counter_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            for (c, _), v in per.items():
+                vals.setdefault(c, []).append(v)
+    for c in sorted(vals):
+        print(f"  {c:30s} {statistics.median(vals[c]):.4e}   (median of {len(vals[c])} dispatches)")
 
 
 def pmc_summary(fetch_dir, write_dir, req_dir=None):
@@ -1011,6 +1075,11 @@ def main():
                     help="launch N routed MoE steps and exit")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="launch N steps and N streaming passes (after a calibration copy) and exit")
+    ap.add_argument("--decode-8b-only", nargs=2, type=int, default=None, metavar=("B", "N"),
+                    help="N grouped Llama-3-8B-shaped decode steps at batch B (for rocprofv3 runs)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="KERNEL_SUBSTRING DIR [DIR ...]: per-dispatch counter medians of rocprofv3 --pmc runs "
+                         "(no GPU needed)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace csv run (no GPU needed)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
@@ -1022,6 +1091,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1:])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library runs the product on one GPU and does not shard it across GPUs "
@@ -1050,6 +1122,9 @@ def main():
         return
     if args.q8_0_only:
         q8_0_only(args.q8_0_only, dev)
+        return
+    if args.decode_8b_only:
+        decode_8b_only(args.decode_8b_only[0], args.decode_8b_only[1], dev)
         return
     report = {}
     model = bench_decode_1b(args, dev, report)
@@ -1097,7 +1172,7 @@ def main():
         "data": "synthetic (seeded, device-drawn N(0,0.02) weights, N(0,1) activations, N(1,0.1) norm weights)",
         "config": {"workload": "llama-3.2-1b-shaped decode, B=1, 16 layers x 7 Q4 matrices; RMSNorm*g->Q8 "
                                "prologue pass over the 64 activation rows + one streaming launch, captured in a "
-                               "HIP graph (median per-replay time)",
+                               "HIP graph and replayed back to back (mean replay time)",
                    "hidden": 2048, "ffn": 8192, "kv_rows": 512, "layers": 16, "B": 1},
         "roofline": report.pop("roofline"),
         "roofline_gemm": report.pop("roofline_gemm", None),
