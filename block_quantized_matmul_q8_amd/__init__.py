@@ -35,6 +35,7 @@ WEIGHTS_Q8_0 = 2  # Q4Q8_WEIGHTS_Q8_0: a group product with Q8_0 weights
 PATH_AUTO = 0
 PATH_GEMV = 1
 PATH_GEMM = 2
+PATH_GEMV_LANES = 3
 
 QK = 32
 
@@ -58,7 +59,8 @@ class GroupPlan(ctypes.Structure):
                 ("n_prologue", ctypes.c_int32), ("n_windows", ctypes.c_int64), ("max_k", ctypes.c_int64),
                 ("map_offset", ctypes.c_int64), ("prologue_offset", ctypes.c_int64),
                 ("table_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("weight_formats", ctypes.c_int32), ("max_prologue_k", ctypes.c_int32)]
+                ("weight_formats", ctypes.c_int32), ("max_prologue_k", ctypes.c_int32),
+                ("mfma_columns", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None

@@ -119,15 +119,29 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
   if ((st = check_device())) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int path = g_path.load(std::memory_order_relaxed);
-  const bool gemv_ok = q4q8::gemv_supported(M, K, B);
+  // the multi-column kernel reads the scale planes in 16-byte pieces
+  const bool mfma_ok = path != Q4Q8_PATH_GEMV_LANES && q4q8::gemv_mfma_ok(M, K, B, wf) && aligned(d, 16) &&
+                       aligned(xd, 16);
+  const bool gemv_ok = B <= 8 && (mfma_ok || q4q8::gemv_supported(M, K, B));
   bool use_gemv;
-  if (path == Q4Q8_PATH_GEMV) {
+  if (path == Q4Q8_PATH_GEMV || path == Q4Q8_PATH_GEMV_LANES) {
     if (!gemv_ok) return fail(Q4Q8_E_UNSUPPORTED, "GEMV route forced but B = %lld, K = %lld does not fit it", (long long)B, (long long)K);
     use_gemv = true;
   } else if (path == Q4Q8_PATH_GEMM) {
     use_gemv = false;
   } else {
     use_gemv = gemv_ok;
+  }
+  if (use_gemv && mfma_ok) {
+    q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
+    p.xq = xq;
+    p.xd = xd;
+    p.mode = q4q8::kModeQ8;
+    p.wf = wf;
+    const int win = q4q8::gemv_mfma_window_rows();
+    p.n_win = (int32_t)((M + win - 1) / win);
+    g_counts[0].fetch_add(1, std::memory_order_relaxed);
+    return launched(q4q8::launch_gemv_mfma(p, nullptr, nullptr, p.n_win, B, I, s, wf), "gemv (multi-column)");
   }
   if (use_gemv) {
     q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
@@ -425,7 +439,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (!e.qs || !e.d || !e.y) return fail(Q4Q8_E_ARG, "descriptor %d: null pointer", i);
     if (!aligned(e.qs, 16) || !aligned(e.d, 2) || !aligned(e.y, 4)) return fail(Q4Q8_E_ALIGN, "descriptor %d: misaligned", i);
     if (e.flags & ~(Q8_NO_NORM | Q4Q8_WEIGHTS_Q8_0)) return fail(Q4Q8_E_ARG, "descriptor %d: unknown flags", i);
-    if (!tiled && !q4q8::gemv_supported(e.M, e.K, B))
+    if (!tiled && !q4q8::gemv_route_supported(e.M, e.K, B,
+                                              (e.flags & Q4Q8_WEIGHTS_Q8_0) ? q4q8::kWeightQ8 : q4q8::kWeightQ4))
       return fail(Q4Q8_E_UNSUPPORTED, "descriptor %d: K = %lld with B = %lld exceeds the streaming kernel", i,
                   (long long)e.K, (long long)B);
     if (e.xq) {
@@ -476,6 +491,26 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     }
     input_of[i] = found;
   }
+  // The streaming pass of B = 5..8 columns runs the multi-column MFMA kernel
+  // when it serves every product and all weights have one format, else the
+  // lane-per-block kernel (which must then serve every product).
+  bool mfma_group = !tiled && B >= q4q8::kGemvMfmaMinB && B <= 8 &&
+                    g_path.load(std::memory_order_relaxed) != Q4Q8_PATH_GEMV_LANES;
+  int mfma_wf = -1;
+  for (int32_t i = 0; i < n && mfma_group; ++i) {
+    const q4q8_gemv_desc& e = descs[i];
+    if (e.M == 0) continue;
+    const int wf = (e.flags & Q4Q8_WEIGHTS_Q8_0) ? q4q8::kWeightQ8 : q4q8::kWeightQ4;
+    if (mfma_wf < 0) mfma_wf = wf;
+    if (wf != mfma_wf || !q4q8::gemv_mfma_ok(e.M, e.K, B, wf) || !aligned(e.d, 16) || (e.xq && !aligned(e.xd, 16)))
+      mfma_group = false;
+  }
+  if (!tiled && !mfma_group)
+    for (int32_t i = 0; i < n; ++i)
+      if (descs[i].M > 0 && !q4q8::gemv_supported(descs[i].M, descs[i].K, B))
+        return fail(Q4Q8_E_UNSUPPORTED,
+                    "descriptor %d: K = %lld with B = %lld needs the multi-column kernel, which does not serve "
+                    "every product of the group", i, (long long)descs[i].K, (long long)B);
   // Product records in the caller's order, all in one streaming launch (the
   // kernel dispatches per product on its register-blocking class).
   std::vector<q4q8::GemvProblem> recs;
@@ -499,7 +534,7 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     if (tiled) {
       t = q4q8::gemm_tiles(e.M, B);
     } else {
-      const int win = q4q8::gemv_window_rows(e.K, B, p.wf);
+      const int win = mfma_group ? q4q8::gemv_mfma_window_rows() : q4q8::gemv_window_rows(e.K, B, p.wf);
       t = (e.M + win - 1) / win;
     }
     tiles += t;
@@ -517,11 +552,17 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t a, int32_t b) { return recs[a].K > recs[b].K; });
   {
-    int64_t first = 0;
+    // cost_begin: the cost-balanced shares of the multi-column kernel (cost
+    // of a window = K / 32 blocks per row; its windows all have 64 rows)
+    int64_t first = 0, cost = 0;
     for (int32_t r : order) {
       recs[r].win_begin = (int32_t)first;
+      recs[r].cost_begin = (int32_t)std::min<int64_t>(cost, INT32_MAX);
       first += rec_tiles[r];
+      cost += rec_tiles[r] * (recs[r].K / q4q8::kQK);
     }
+    if (mfma_group && cost > INT32_MAX)
+      return fail(Q4Q8_E_UNSUPPORTED, "group too large for the multi-column route (windows x K / 32 > 2^31)");
   }
   plan->B = (int32_t)B;
   plan->n_records = (int32_t)recs.size();
@@ -536,6 +577,8 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   for (const q4q8::GemvProblem& r : recs) plan->weight_formats |= 1 << r.wf;
   plan->max_prologue_k = 0;
   for (const Input& in : inputs) plan->max_prologue_k = std::max(plan->max_prologue_k, (int32_t)in.K);
+  plan->mfma_columns = mfma_group ? 1 : 0;
+  plan->reserved = 0;
   plan->magic = kGroupMagic;
   if (!table_host) return ok();
   const char* why = nullptr;
@@ -591,7 +634,10 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   if (plan->n_records < 0 || plan->B < 1 || plan->B > 65535 || plan->n_windows < plan->n_records ||
       plan->n_windows > INT32_MAX || plan->n_prologue < 0 || plan->n_prologue > plan->n_records ||
       plan->max_k < q4q8::kQK || plan->max_k % q4q8::kQK != 0 ||
-      (!tiled && !q4q8::gemv_supported(1, plan->max_k, plan->B)) ||
+      plan->mfma_columns < 0 || plan->mfma_columns > 1 || plan->reserved != 0 ||
+      (plan->mfma_columns && (tiled || plan->B < q4q8::kGemvMfmaMinB || plan->max_k < 512 || plan->max_k % 128 != 0 ||
+                                 plan->weight_formats == 3)) ||
+      (!tiled && !plan->mfma_columns && !q4q8::gemv_supported(1, plan->max_k, plan->B)) ||
       plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
       plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
       plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob) ||
@@ -625,6 +671,11 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
                     "mul_mat_q4q8_group (tiled)");
   }
   g_counts[0].fetch_add(1, std::memory_order_relaxed);
+  if (plan->mfma_columns)
+    return launched(q4q8::launch_gemv_mfma(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
+                                           reinterpret_cast<const int32_t*>(base + plan->map_offset),
+                                           plan->n_windows, plan->B, nullptr, s, wf),
+                    "mul_mat_q4q8_group (multi-column)");
   return launched(q4q8::launch_gemv_table(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                           reinterpret_cast<const int32_t*>(base + plan->map_offset),
                                           plan->n_windows, plan->max_k, plan->B, false, nullptr, s, wf),
@@ -632,7 +683,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
 }
 
 Q4Q8_EXPORT int q4q8_set_path(int path) {
-  if (path != Q4Q8_PATH_AUTO && path != Q4Q8_PATH_GEMV && path != Q4Q8_PATH_GEMM)
+  if (path != Q4Q8_PATH_AUTO && path != Q4Q8_PATH_GEMV && path != Q4Q8_PATH_GEMM && path != Q4Q8_PATH_GEMV_LANES)
     return fail(Q4Q8_E_ARG, "unknown path %d", path);
   g_path.store(path, std::memory_order_relaxed);
   return ok();

@@ -162,7 +162,7 @@ struct alignas(16) GemvProblem {
   int32_t win_begin;   // index of this problem's first window in the launch
   int32_t n_win;       // windows of this problem (ceil(M / window rows))
   int32_t wf;          // weight format of qs (WeightFormat)
-  int32_t pad;
+  int32_t cost_begin;  // grouped launches: sum of n_win * K / 32 over the records before this one
 };
 static_assert(sizeof(GemvProblem) == 96, "GemvProblem layout");
 
@@ -185,8 +185,24 @@ static_assert(sizeof(PrologueJob) == 48, "PrologueJob layout");
 // of the __global__ function), per calling thread, for q4q8_last_kernel().
 Q4Q8_HIDDEN void note_launch(const void* kernel);
 
-// Route selection helpers (host).
+// Route selection helpers (host).  gemv_supported: the lane-per-block
+// streaming kernel (gemv_dev.h, also the routed MoE kernel) serves K with B
+// columns; gemv_route_supported: either streaming kernel serves the product
+// (the MFMA kernel of gemv_mfma.hip takes B = 5..8 where gemv_mfma_ok).
 Q4Q8_HIDDEN bool gemv_supported(int64_t M, int64_t K, int64_t B);
+Q4Q8_HIDDEN bool gemv_route_supported(int64_t M, int64_t K, int64_t B, int wf);
+// The multi-column MFMA kernel serves B = 5..8 columns on Q8 planes with
+// rows of at least four whole 128-byte segments (K a multiple of 256 and at
+// least 1024 for Q4, a multiple of 128 and at least 512 for Q8_0)
+// and weight planes under 2 GiB (32-bit buffer offsets); its callers also
+// require d and xd 16-byte aligned, and one weight format per launch.
+constexpr int kGemvMfmaMinB = 5;
+Q4Q8_HIDDEN bool gemv_mfma_ok(int64_t M, int64_t K, int64_t B, int wf);
+// Rows per window of the MFMA multi-column kernel, and its launcher (same
+// table / map conventions as launch_gemv_table; records carry cost_begin).
+Q4Q8_HIDDEN int gemv_mfma_window_rows();
+Q4Q8_HIDDEN hipError_t launch_gemv_mfma(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
+                                        int64_t n_windows, int64_t B, int32_t* I, hipStream_t s, int wf);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
 // Rows per window (the unit a workgroup streams) for a product with K and B;
 // wf: weight format (kWeightQ4 or kWeightQ8); fold: the folded-prologue form.

@@ -113,6 +113,22 @@ bool gemv_supported(int64_t M, int64_t K, int64_t B) {
   return gemv_class_of(K, B).J != 0;
 }
 
+bool gemv_mfma_ok(int64_t M, int64_t K, int64_t B, int wf) {
+  // rows of at least four whole 128-byte segments (Q4: K a multiple of 256,
+  // at least 1024; Q8_0: a multiple of 128, at least 512).  Five or more
+  // columns: up to four, the lane-per-block kernel streams faster (it runs
+  // four columns without padding; the matrix kernel pays for the activation
+  // operands and the exchange of partial sums whatever B is).
+  const int64_t row_bytes = wf == kWeightQ8 ? K : K / 2;
+  return (wf == kWeightQ4 || wf == kWeightQ8) && B >= kGemvMfmaMinB && B <= 8 && row_bytes >= 512 &&
+         row_bytes % 128 == 0 &&
+         K % 64 == 0 && M >= 1 && M * row_bytes < ((int64_t)1 << 31) && B * K < ((int64_t)1 << 30);
+}
+
+bool gemv_route_supported(int64_t M, int64_t K, int64_t B, int wf) {
+  return gemv_mfma_ok(M, K, B, wf) || gemv_class_of(K, B).J != 0;
+}
+
 bool gemv_fused_supported(int64_t K, int64_t B) {
   const GemvClass c = gemv_class_unsplit(K, B);
   return B <= 4 && c.J != 0 && c.S == 1 && fused_lds_bytes(K, B) <= kGemvMaxLds;

@@ -258,6 +258,12 @@ typedef struct q4q8_group_plan {
   int32_t weight_formats;  /* 1: all products Q4, 2: all Q8_0, 3: both (selects the kernel instance) */
   int32_t max_prologue_k;  /* largest K among the fp32 inputs of the prologue pass (0 if none);
                               sizes that pass's LDS, which Q8-plane products never enter */
+  int32_t mfma_columns;    /* 1: the streaming pass runs the multi-column int8-MFMA kernel (B = 5..8,
+                              one weight format, every K a multiple of 256 and >= 1024 for Q4, or
+                              of 128 and >= 512 for Q8_0,
+                              d and xd 16-byte aligned; windows of 64 rows), 0: the
+                              lane-per-block one */
+  int32_t reserved;        /* 0 */
 } q4q8_group_plan;
 /* Every field is written by q4q8_group_build and read as it left them: a
  * launch checks their consistency but cannot detect every edited value. */
@@ -354,9 +360,13 @@ int moe_expert_sum_f32(const float* y, const float* w, int64_t T, int64_t top_k,
 #define Q4Q8_PATH_AUTO 0
 #define Q4Q8_PATH_GEMV 1
 #define Q4Q8_PATH_GEMM 2
+#define Q4Q8_PATH_GEMV_LANES 3
 
 /* Force the route taken by mul_mat_q4q8 and mul_mat_q8_0_q8 (process-wide).
- * Forcing GEMV for a shape it cannot hold returns Q4Q8_E_UNSUPPORTED. */
+ * Forcing GEMV for a shape it cannot hold returns Q4Q8_E_UNSUPPORTED.
+ * Q4Q8_PATH_GEMV_LANES forces the streaming route with the lane-per-block
+ * kernel, never the multi-column MFMA one; group plans built while it is
+ * set use the lane-per-block kernel too (plan->mfma_columns == 0). */
 int q4q8_set_path(int path);
 
 /* Like mul_mat_q4q8, and also writes the exact per-block integer sums

@@ -176,7 +176,9 @@ def test_set_path_and_counters():
     L = q.lib()
     assert L.q4q8_set_path(9) == q.Q4Q8_E_ARG
     assert L.q4q8_dispatch_counts(None, 0) == q.Q4Q8_E_ARG
+    assert L.q4q8_set_path(4) == q.Q4Q8_E_ARG
     q.q4q8_set_path(q.PATH_GEMM)
+    q.q4q8_set_path(q.PATH_GEMV_LANES)
     q.q4q8_set_path(q.PATH_AUTO)
     c = q.q4q8_dispatch_counts()
     assert set(c) == {"gemv", "gemm", "routed", "prologue"}
@@ -341,7 +343,9 @@ def test_group_build_validation_is_host_only():
         ([_desc()], 70000, q.Q4Q8_E_UNSUPPORTED),                   # B beyond a grouped launch
         ([_desc(xq=None, xd=None, x=512, g=768, K=262144)], 300, q.Q4Q8_E_ARG),  # fp32 rows too long
         ([_desc(K=131072)], 1, q.Q4Q8_E_UNSUPPORTED),               # K beyond the register blocking
-        ([_desc(xq=None, xd=None, x=512, g=768, K=32768)], 8, q.Q4Q8_E_UNSUPPORTED),
+        # K of an odd number of blocks beyond the lane-per-block kernel at B = 8 (the
+        # multi-column kernel takes whole block pairs only)
+        ([_desc(xq=None, xd=None, x=512, g=768, K=32800)], 8, q.Q4Q8_E_UNSUPPORTED),
     ]
     for descs, B, code in bad:
         with pytest.raises(q.Q4Q8Error) as ei:

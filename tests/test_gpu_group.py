@@ -44,10 +44,11 @@ def test_fused_codes_equal_standalone_prologue(M, K, B, raw):
     """The folded-in prologue produces the codes of the standalone prologue
     bit for bit: with identical codes the product kernel does identical
     arithmetic in both modes, so the outputs must agree bit for bit.  The
-    exception is one column with K > 8192 and two with K > 4096: there the
+    exceptions are one column with K > 8192 and two with K > 4096, where the
     plain product splits K over waves while the folded form keeps K in one
-    wave, so the two fp32 sums differ in rounding order and both are held to
-    the oracle instead."""
+    wave, and three or more columns, where the plain product may run the
+    multi-column MFMA kernel: there the two fp32 sums differ in rounding
+    order and both are held to the oracle instead."""
     qs, d = _weights(44, 0, M % 5, M, K)
     x = workloads.activation(44, 0, 1, B, K) * np.float32(2.5)
     g = workloads.norm_weight(44, 0, 1, K)
@@ -58,7 +59,8 @@ def test_fused_codes_equal_standalone_prologue(M, K, B, raw):
     xq, xd, _ = q.q8_quantize_rmsnorm(x_d, g_d, workloads.RMS_EPS, flags=flags)
     y_u = q.mul_mat_q4q8(qs_d, d_d, xq, xd)
     torch.cuda.synchronize()
-    if (B == 1 and K > 8192) or (B == 2 and K > 4096):
+    plain_mfma = "gemv_mfma_kernel" in q.q4q8_last_kernel()
+    if (B == 1 and K > 8192) or (B == 2 and K > 4096) or plain_mfma:
         ref = _ref(qs, d, x, None if raw else g, no_norm=raw)
         assert_close(y_f.cpu().numpy(), ref, f"folded M={M} K={K}")
         assert_close(y_u.cpu().numpy(), ref, f"plain M={M} K={K}")
@@ -128,8 +130,13 @@ def test_group_mixed(B):
             assert_close(p["y"].cpu().numpy(), ref, f"rep {rep} M={p['qs'].shape[0]}")
     # the group's prologue pass gives the codes of q8_quantize_rmsnorm and
     # the streaming pass runs the single-product arithmetic, so the outputs
-    # agree bit for bit with the two standalone calls
-    for p in problems:
+    # agree bit for bit with the two standalone calls -- where both take the
+    # same streaming kernel: a single product of B = 5..8 columns with rows of
+    # four or more whole 128-byte segments takes the multi-column one, a group only when
+    # every product can (grp.plan.mfma_columns)
+    group_mfma = "gemv_mfma_kernel" in q.q4q8_last_kernel()
+    assert group_mfma == bool(grp.plan.mfma_columns)
+    for p, ref in zip(problems, refs):
         if "x" in p:
             raw = p.get("flags", 0) == q.Q8_NO_NORM
             xq, xd, _ = q.q8_quantize_rmsnorm(p["x"], None if raw else p["g"], workloads.RMS_EPS,
@@ -138,7 +145,10 @@ def test_group_mixed(B):
             xq, xd = p["xq"], p["xd"]
         single = q.mul_mat_q4q8(p["qs"], p["d"], xq, xd)
         torch.cuda.synchronize()
-        assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
+        if ("gemv_mfma_kernel" in q.q4q8_last_kernel()) == group_mfma:
+            assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32))
+        else:
+            assert_close(single.cpu().numpy(), ref, "single call")
 
 
 @pytest.mark.parametrize("k_max", [32768, 32800])
