@@ -279,6 +279,16 @@ def per_launch_ms(fn, reps):
     return a.elapsed_time(b) / reps
 
 
+def per_launch_graph_ms(fn, reps=20, replays=20):
+    """Average GPU time of one launch of fn: `reps` calls captured back to
+    back in one HIP graph, the graph replayed `replays` times between two
+    HIP events (per_launch_ms over direct calls measures the host's call
+    rate for launches this short)."""
+    g = capture(lambda: [fn() for _ in range(reps)])
+    ms, _ = time_graph(g, replays, 3)
+    return ms / reps
+
+
 class DecodeModel:
     """Quantised weights, activations and outputs of a decode workload."""
 
@@ -935,7 +945,7 @@ def bench_q8_0(args, dev):
 def bench_prologues(args, dev):
     """The standalone activation prologues on Llama-3-8B-shaped rows
     (K = 4096): RMS_NORM+MUL -> Q8 and RMS_NORM+MUL+ADD -> Q8 (one addend row
-    per input row), per launch.  Bytes: x (and the addend) read, g read once,
+    per input row), GPU time per launch from graph replays.  Bytes: x (and the addend) read, g read once,
     codes and scales written."""
     import torch
 
@@ -950,8 +960,8 @@ def bench_prologues(args, dev):
         g = wl.norm_weight_device(6, 0, 0, K, dev)
         xq = torch.empty((B, K), dtype=torch.int8, device=dev)
         xd = torch.empty((B, K // 32), dtype=torch.float32, device=dev)
-        ms_n = per_launch_ms(lambda: q.q8_quantize_rmsnorm(x, g, wl.RMS_EPS, xq=xq, xd=xd), 20)
-        ms_a = per_launch_ms(lambda: q.q8_quantize_rmsnorm_add(x, g, a, wl.RMS_EPS, xq=xq, xd=xd), 20)
+        ms_n = per_launch_graph_ms(lambda: q.q8_quantize_rmsnorm(x, g, wl.RMS_EPS, xq=xq, xd=xd))
+        ms_a = per_launch_graph_ms(lambda: q.q8_quantize_rmsnorm_add(x, g, a, wl.RMS_EPS, xq=xq, xd=xd))
         b_n = B * K * 4 + K * 4 + B * K * 9 // 8
         b_a = b_n + B * K * 4
         out[f"B={B}"] = {"rmsnorm_mul_q8": {"us": round(ms_n * 1e3, 2), "GB/s": round(b_n / (ms_n * 1e-3) / 1e9, 1)},
@@ -963,11 +973,12 @@ def bench_prologues(args, dev):
         buf = wl.activation_device(7, 0, 0, rows, 2 * F, dev)
         xq = torch.empty((rows, F), dtype=torch.int8, device=dev)
         xd = torch.empty((rows, F // 32), dtype=torch.float32, device=dev)
-        ms = per_launch_ms(lambda: q.q8_quantize_swiglu(buf[:, :F], buf[:, F:], xq=xq, xd=xd), 20)
+        ms = per_launch_graph_ms(lambda: q.q8_quantize_swiglu(buf[:, :F], buf[:, F:], xq=xq, xd=xd))
         nbytes = rows * F * 8 + rows * F * 9 // 8
         out[name] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-    out["note"] = ("norm prologues: one workgroup per row, latency-bound (a few us); "
-                   "swiglu_q8: one thread per 32-block, no row reduction")
+    out["note"] = ("per launch: 20 launches captured in one HIP graph, replayed; norm prologues: one "
+                   "1024-thread workgroup per row for up to 8 rows, latency-bound; swiglu_q8: eight lanes "
+                   "per 32-block, no row reduction")
     return out
 
 
@@ -1010,7 +1021,7 @@ def bench_moe(args, dev):
     y_down = mats[1][2]
     w = torch.from_numpy(wl.expert_weights(0, cfg.T, cfg.top_k)).to(dev)
     out = torch.empty((cfg.T, cfg.hidden), dtype=torch.float32, device=dev)
-    ms_sum = per_launch_ms(lambda: q.moe_expert_sum_f32(y_down, w, out=out), 20)
+    ms_sum = per_launch_graph_ms(lambda: q.moe_expert_sum_f32(y_down, w, out=out))
     sum_bytes = cfg.T * cfg.top_k * (cfg.hidden + 1) * 4 + cfg.T * cfg.hidden * 4
     return {"GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
             "distinct_experts": distinct, "bytes": nbytes,

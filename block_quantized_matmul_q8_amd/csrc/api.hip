@@ -249,7 +249,8 @@ Q4Q8_EXPORT int q8_quantize_swiglu(const float* gate, const float* up, int64_t B
   if ((st = check_k(F)) || (st = check_dims(1, B))) return st;
   if (row_stride < F || row_stride % 4)
     return fail(Q4Q8_E_ARG, "row_stride = %lld must be >= F and a multiple of 4", (long long)row_stride);
-  if (B * (F / 32) > (int64_t)INT32_MAX * 64) return fail(Q4Q8_E_ARG, "B * F too large");
+  // eight lanes per 32-block, 256 per workgroup: the grid stays within 2^31
+  if (B * (F / 32) > (int64_t)INT32_MAX * 8) return fail(Q4Q8_E_ARG, "B * F / 32 > 2^34");
   if (B == 0) return ok();
   if (!gate || !up || !xq || !xd) return fail(Q4Q8_E_ARG, "null pointer argument");
   if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(xq, 16) || !aligned(xd, 4) || (xs && !aligned(xs, 4)))

@@ -281,4 +281,184 @@ __device__ __forceinline__ void wg_q8_row_fast(const float* __restrict__ xr,
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// The same prologue on a 1024-thread workgroup, for the latency-bound decode
+// rows (a handful of rows per call, each on its own workgroup): more lanes per
+// row shorten every serial stretch of the row's work.  Bit for bit the steps
+// above: per-block sums in index order, the pairwise tree over the padded
+// block sums, then s, v and the Q8 block rule.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kWideThreads = 1024;
+constexpr int kWideWaves = kWideThreads / kWave;
+constexpr int kQuadMaxK = kQK * kWideThreads / 4;  // 8192: four lanes per block
+constexpr int kWideMaxK = kQK * kWideThreads;      // 32768: one lane per block
+
+// DPP within each quad of lanes: quad_perm [0,0,1,2] hands lane r the value
+// of lane r - 1; [1,0,3,2] and [2,3,0,1] swap neighbours and pairs.
+__device__ __forceinline__ float quad_from_prev(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x90, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_max(float m) {
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+}
+
+// s from the per-wave partial trees: lane 0 of every wave publishes its
+// wave's sum, one barrier, and every thread finishes the tree over the 16
+// wave slots (slots past the row's padded block count hold +0, and adding +0
+// to a non-negative sum is exact, so the fixed four-level tree gives the bits
+// of the tree over next_pow2(nb) blocks).
+__device__ __forceinline__ float wide_rms_scale(float wave_sum, int K, float eps, float* groups, int tid) {
+  if ((tid & (kWave - 1)) == 0) groups[tid / kWave] = wave_sum;
+  __syncthreads();
+  float t[kWideWaves];
+#pragma unroll
+  for (int i = 0; i < kWideWaves; ++i) t[i] = groups[i];
+#pragma unroll
+  for (int h = kWideWaves / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i) t[i] = __fadd_rn(t[2 * i], t[2 * i + 1]);
+  const float mean = __fdiv_rn(t[0], (float)K);
+  return __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(mean, eps)));
+}
+
+// One row of at most 256 blocks (K <= 8192), four lanes per block: lane r of
+// quad b holds elements 8r .. 8r + 7 of block b.
+//   - the block's squares are formed in parallel and summed in index order
+//     by passing the running sum along the quad (four rounds of eight adds);
+//   - lane 3's sum is the block's p_b; with the other lanes at +0, the
+//     wave's xor butterfly pairs exactly the tree's pairs of blocks (the
+//     first two levels add exact zeros);
+//   - amax over the quad by DPP, then each lane codes its eight values.
+// Writes codes to xq [K], scales to xd [nb] and, when xs is not null, code
+// sums to xs [nb]; ar: the row's addend (RMS_NORM+MUL+ADD) or null; groups:
+// LDS of 16 floats.
+__device__ __forceinline__ void wide_q8_row_quad(const float* __restrict__ xr, const float* __restrict__ g, int K,
+                                                 float eps, bool raw, int8_t* __restrict__ xq,
+                                                 float* __restrict__ xd, int32_t* __restrict__ xs, float* groups,
+                                                 int tid, const float* __restrict__ ar = nullptr) {
+  const int nb = K / kQK;
+  const int b = tid >> 2, r = tid & 3;
+  const bool on = b < nb;
+  float xv[8], gv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xv[j] = gv[j] = 0.0f;
+  if (on) {
+    const Q4Q8_GLOBAL f32x4* px = gptr(reinterpret_cast<const f32x4*>(xr + b * kQK + 8 * r));
+    const f32x4 a0 = px[0], a1 = px[1];
+    xv[0] = a0.x, xv[1] = a0.y, xv[2] = a0.z, xv[3] = a0.w;
+    xv[4] = a1.x, xv[5] = a1.y, xv[6] = a1.z, xv[7] = a1.w;
+    if (!raw) {
+      const Q4Q8_GLOBAL f32x4* pg = gptr(reinterpret_cast<const f32x4*>(g + b * kQK + 8 * r));
+      const f32x4 c0 = pg[0], c1 = pg[1];
+      gv[0] = c0.x, gv[1] = c0.y, gv[2] = c0.z, gv[3] = c0.w;
+      gv[4] = c1.x, gv[5] = c1.y, gv[6] = c1.z, gv[7] = c1.w;
+    }
+  }
+  float s = 1.0f;
+  if (!raw) {
+    float sq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sq[j] = __fmul_rn(xv[j], xv[j]);
+    // round k: lane k continues the block's sum from lane k - 1's result
+    float cin = 0.0f, t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      t = cin;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t = __fadd_rn(t, sq[j]);
+      const float prev = quad_from_prev(t);
+      cin = r == k + 1 ? prev : cin;
+    }
+    s = wide_rms_scale(wave_tree_sum(r == 3 ? t : 0.0f), K, eps, groups, tid);
+  }
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = raw ? xv[j] : __fmul_rn(__fmul_rn(xv[j], s), gv[j]);
+  if (ar && on) {
+    const Q4Q8_GLOBAL f32x4* pa = gptr(reinterpret_cast<const f32x4*>(ar + b * kQK + 8 * r));
+    const f32x4 a0 = pa[0], a1 = pa[1];
+    v[0] = __fadd_rn(v[0], a0.x), v[1] = __fadd_rn(v[1], a0.y), v[2] = __fadd_rn(v[2], a0.z);
+    v[3] = __fadd_rn(v[3], a0.w), v[4] = __fadd_rn(v[4], a1.x), v[5] = __fadd_rn(v[5], a1.y);
+    v[6] = __fadd_rn(v[6], a1.z), v[7] = __fadd_rn(v[7], a1.w);
+  }
+  float m[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1]));
+  const float amax = quad_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+  const float d = __fdiv_rn(amax, 127.0f);
+  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  uint32_t w[2];
+  int csum = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int qi = (int)roundf(__fmul_rn(v[4 * h + k], id));
+      qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+      csum += qi;
+      word |= ((uint32_t)qi & 0xFFu) << (8 * k);
+    }
+    w[h] = word;
+  }
+  if (xs) {  // the block's code sum over the quad (exact integer adds)
+    csum += __builtin_amdgcn_update_dpp(0, csum, 0xB1, 0xF, 0xF, false);
+    csum += __builtin_amdgcn_update_dpp(0, csum, 0x4E, 0xF, 0xF, false);
+  }
+  if (on) {
+    *gptr_w(reinterpret_cast<u32x2_t*>(xq + b * kQK + 8 * r)) = u32x2_t{w[0], w[1]};
+    if (r == 0) {
+      gptr_w(xd)[b] = d;
+      if (xs) gptr_w(xs)[b] = csum;
+    }
+  }
+}
+
+// One row of at most 1024 blocks (K <= 32768), one lane per block: the
+// register form of wg_q8_row_fast on 16 waves.
+__device__ __forceinline__ void wide_q8_row_single(const float* __restrict__ xr, const float* __restrict__ g, int K,
+                                                   float eps, bool raw, int8_t* __restrict__ xq,
+                                                   float* __restrict__ xd, int32_t* __restrict__ xs, float* groups,
+                                                   int tid, const float* __restrict__ ar = nullptr) {
+  const int nb = K / kQK;
+  const int b = tid;
+  const bool on = b < nb;
+  float xv[kQK], gv[kQK];
+#pragma unroll
+  for (int j = 0; j < kQK; ++j) xv[j] = gv[j] = 0.0f;
+  if (on) {
+    load_block32(xr + b * kQK, xv);
+    if (!raw) load_block32(g + b * kQK, gv);
+  }
+  float s = 1.0f;
+  if (!raw) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(xv[j], xv[j]));
+    s = wide_rms_scale(wave_tree_sum(acc), K, eps, groups, tid);
+  }
+  if (on) {
+    float v[kQK];
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) v[j] = raw ? xv[j] : __fmul_rn(__fmul_rn(xv[j], s), gv[j]);
+    if (ar) {
+      float av[kQK];
+      load_block32(ar + b * kQK, av);
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) v[j] = __fadd_rn(v[j], av[j]);
+    }
+    float d;
+    int sum;
+    uint32_t packed[8];
+    q8_pack_block(v, packed, d, sum);
+    u32x4* dst = reinterpret_cast<u32x4*>(xq + (size_t)b * kQK);
+    gptr_w(dst)[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    gptr_w(dst)[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+    gptr_w(xd)[b] = d;
+    if (xs) gptr_w(xs)[b] = sum;
+  }
+}
+
 }  // namespace q4q8

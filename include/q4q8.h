@@ -139,6 +139,7 @@ int q8_quantize_rmsnorm_add(const float* x, int64_t B, int64_t K, const float* g
  *             (a stacked [B][2F] gate|up buffer: up = gate + F, row_stride = 2F);
  *             16-byte aligned, row_stride >= F and a multiple of 4
  *   xq [B][F] i8 (16-byte aligned), xd [B][F/32] f32, xs [B][F/32] i32 or NULL
+ *   B * F / 32 <= 2^34 (else Q4Q8_E_ARG)
  * Outputs must not overlap the inputs.  Non-finite inputs give unspecified codes.
  */
 int q8_quantize_swiglu(const float* gate, const float* up, int64_t B, int64_t F, int64_t row_stride, int8_t* xq,

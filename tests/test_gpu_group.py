@@ -361,3 +361,50 @@ def test_full_decode_step_sampled():
             x, g = acts[m["slot"]]
             y_o = _ref(qs, d, x, g)
             assert_close(m["y"].cpu().numpy()[:, rows], y_o, f"layer {l} {m['name']}")
+
+
+_PROLOGUE_CASES = ([(1, K) for K in (32, 96, 1408, 2048, 8192, 8224, 14336, 32768, 32800)] +
+                   [(3, K) for K in (96, 2048, 8192, 8224, 14336)] +
+                   [(8, K) for K in (96, 2048, 8192, 8224, 14336, 32768)] +
+                   [(9, K) for K in (2048, 14336)])
+
+
+@pytest.mark.parametrize("raw", [False, True])
+@pytest.mark.parametrize("B,K", _PROLOGUE_CASES)
+def test_group_prologue_planes_bit_exact(B, K, raw):
+    """The grouped prologue pass's own Q8 planes (read out of the group's
+    workspace, where the first fp32 input's codes [B][K] start at offset 0 and
+    its scales [B][K/32] at the next 16-byte boundary) equal the oracle's bit
+    for bit: the 1024-thread forms for B <= 8 (four lanes per block up to K =
+    8192, one lane per block up to 32768, the LDS tree beyond) and the
+    256-thread form above; zero rows, tiny rows and a lone spike included."""
+    print(f"[group prologue] B={B} K={K} raw={raw}", flush=True)
+    x = workloads.activation(48, B, K % 97, B, K) * np.float32(1.7)
+    if B >= 3:
+        x[1] = 0.0
+        x[2] *= np.float32(1e-20)
+        x[0, K // 3] = np.float32(3000.0)
+    g = workloads.norm_weight(48, 0, K % 89, K)
+    M = 16
+    qs, d = _weights(48, 0, 0, M, K)
+    y = torch.full((B, M), float("nan"), device="cuda:0")
+    p = {"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": to_dev(x)}
+    if raw:
+        p["flags"] = q.Q8_NO_NORM
+    else:
+        p.update(g=to_dev(g), eps=workloads.RMS_EPS)
+    grp = q.Group([p], B=B)
+    assert grp.plan.n_prologue == 1
+    grp.workspace.fill_(0xA5)
+    grp()
+    torch.cuda.synchronize()
+    ws = grp.workspace.cpu().numpy()
+    off = (B * K + 15) // 16 * 16
+    xq = ws[:B * K].view(np.int8).reshape(B, K)
+    xd = ws[off:off + B * (K // 32) * 4].view(np.uint32).reshape(B, K // 32)
+    xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, None if raw else g, workloads.RMS_EPS, no_norm=raw)
+    assert np.array_equal(xq, xq_o)
+    assert np.array_equal(xd, xd_o.view(np.uint32))
+    y_o, _ = oracle.mul_mat(qs, d, xq_o, xd_o, nthreads=16, want_y64=False)
+    assert np.isfinite(y.cpu().numpy()).all()
+    assert_close(y.cpu().numpy(), y_o, f"B={B} K={K}")
