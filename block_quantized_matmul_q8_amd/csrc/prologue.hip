@@ -184,7 +184,11 @@ __global__ __launch_bounds__(kWideThreads) void rmsnorm_q8_wide_kernel(
   float* xdr = xd + row * nb;
   int32_t* xsr = xs ? xs + row * nb : nullptr;
   if (K <= kQuadMaxK) {
-    wide_q8_row_quad(xr, g, K, eps, no_norm != 0, xqr, xdr, xsr, groups, tid, ar);
+    wide_q8_row_lanes<4>(xr, g, K, eps, no_norm != 0, xqr, xdr, xsr, groups, tid, ar);
+    return;
+  }
+  if (K <= kPairMaxK) {
+    wide_q8_row_lanes<2>(xr, g, K, eps, no_norm != 0, xqr, xdr, xsr, groups, tid, ar);
     return;
   }
   if (K <= kWideMaxK) {
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(256) void swiglu_q8_kernel(const float* __restrict_
   int csum = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int qi = (int)roundf(__fmul_rn(v[k], id));
+    int qi = round_half_away_i32(__fmul_rn(v[k], id));
     qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
     csum += qi;
     word |= ((uint32_t)qi & 0xFFu) << (8 * k);
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(kPrologueThreads) void group_prologue_kernel(
 
 // The same pass for a few columns (decode): 1024-thread workgroups, so that
 // each row's serial stretches are short -- four lanes per block up to K =
-// 8192, one lane per block up to 32768, the LDS-tree form beyond.
+// 8192, two up to 16384, one up to 32768, the LDS-tree form beyond.
 __global__ __launch_bounds__(kWideThreads) void group_prologue_wide_kernel(const PrologueJob* __restrict__ jobs) {
   extern __shared__ float red[];
   __shared__ float s_slot;
@@ -329,7 +333,11 @@ __global__ __launch_bounds__(kWideThreads) void group_prologue_wide_kernel(const
   int8_t* xq = J.xq + (int64_t)c * K;
   float* xd = J.xd + (int64_t)c * nb;
   if (K <= kQuadMaxK) {
-    wide_q8_row_quad(xr, J.g, K, J.eps, J.raw != 0, xq, xd, nullptr, groups, tid);
+    wide_q8_row_lanes<4>(xr, J.g, K, J.eps, J.raw != 0, xq, xd, nullptr, groups, tid);
+    return;
+  }
+  if (K <= kPairMaxK) {
+    wide_q8_row_lanes<2>(xr, J.g, K, J.eps, J.raw != 0, xq, xd, nullptr, groups, tid);
     return;
   }
   if (K <= kWideMaxK) {

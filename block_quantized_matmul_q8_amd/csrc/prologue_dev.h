@@ -110,6 +110,18 @@ __device__ __forceinline__ float wg_rms_scale(const float* __restrict__ xr, int 
   return *s_slot;
 }
 
+// roundf(t) (halves away from zero) as an int, for any finite t whose
+// rounded value fits an int: fl(t + copysign(0.5 - 2^-25, t)) truncated.
+// Adding the largest float below one half, with round-to-nearest-even, never
+// carries t past the next integer unless roundf does: for frac(t) < 1/2 the
+// sum stays more than a rounding step below it, for frac(t) >= 1/2 it lands
+// within half a step of it (the tie at t = 1/2 goes to the even 1.0); at
+// 2^23 and above every float is an integer and the sum rounds back to t.
+// Two instructions and a truncating convert instead of roundf's six.
+__device__ __forceinline__ int round_half_away_i32(float t) {
+  return (int)__fadd_rn(t, __builtin_copysignf(0.49999997f, t));
+}
+
 // The Q8 block rule on 32 values: d = amax(|v|) / 127, id = 1 / d (0 for an
 // all-zero block), q = roundf(v * id) clamped to [-127, 127].  packed[8]
 // holds the codes in index order (4 per dword, little-endian), sum their sum.
@@ -123,7 +135,7 @@ __device__ __forceinline__ void q8_pack_block(const float (&v)[kQK], uint32_t (&
     uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int qi = (int)roundf(__fmul_rn(v[4 * i + k], id));
+      int qi = round_half_away_i32(__fmul_rn(v[4 * i + k], id));
       qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
       sum += qi;
       word |= ((uint32_t)qi & 0xFFu) << (8 * k);
@@ -292,17 +304,33 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWideThreads = 1024;
 constexpr int kWideWaves = kWideThreads / kWave;
 constexpr int kQuadMaxK = kQK * kWideThreads / 4;  // 8192: four lanes per block
+constexpr int kPairMaxK = kQK * kWideThreads / 2;  // 16384: two lanes per block
 constexpr int kWideMaxK = kQK * kWideThreads;      // 32768: one lane per block
 
-// DPP within each quad of lanes: quad_perm [0,0,1,2] hands lane r the value
-// of lane r - 1; [1,0,3,2] and [2,3,0,1] swap neighbours and pairs.
-__device__ __forceinline__ float quad_from_prev(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x90, 0xF, 0xF, false));
+// DPP within each group of L lanes (L = 2 or 4; groups aligned in quads):
+// lane_from_prev hands lane r the value of lane r - 1 (quad_perm [0,0,1,2]
+// for L = 4, [0,0,2,2] for L = 2); group_max and group_isum combine the
+// group by swapping neighbours ([1,0,3,2]) and, for L = 4, pairs
+// ([2,3,0,1]).
+template <int L>
+__device__ __forceinline__ float lane_from_prev(float v) {
+  constexpr int sel = L == 4 ? 0x90 : 0xA0;
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), sel, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float quad_max(float m) {
+template <int L>
+__device__ __forceinline__ float group_max(float m) {
   m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
-  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+  if constexpr (L == 4)
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+  return m;
 }
+template <int L>
+__device__ __forceinline__ int group_isum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  if constexpr (L == 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  return v;
+}
+__device__ __forceinline__ float quad_max(float m) { return group_max<4>(m); }
 
 // s from the per-wave partial trees: lane 0 of every wave publishes its
 // wave's sum, one barrier, and every thread finishes the tree over the 16
@@ -323,92 +351,103 @@ __device__ __forceinline__ float wide_rms_scale(float wave_sum, int K, float eps
   return __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(mean, eps)));
 }
 
-// One row of at most 256 blocks (K <= 8192), four lanes per block: lane r of
-// quad b holds elements 8r .. 8r + 7 of block b.
+// One row of at most 1024 / L blocks, L = 4 or 2 lanes per block: lane r of
+// group b holds elements E r .. E r + E - 1 of block b (E = 32 / L).
 //   - the block's squares are formed in parallel and summed in index order
-//     by passing the running sum along the quad (four rounds of eight adds);
-//   - lane 3's sum is the block's p_b; with the other lanes at +0, the
-//     wave's xor butterfly pairs exactly the tree's pairs of blocks (the
-//     first two levels add exact zeros);
-//   - amax over the quad by DPP, then each lane codes its eight values.
+//     by passing the running sum along the group (L rounds of E adds);
+//   - the group's last lane holds p_b; with the other lanes at +0, the
+//     wave's xor butterfly pairs exactly the tree's pairs of blocks (its
+//     first log2 L levels add exact zeros);
+//   - amax (and the code sum) over the group by DPP, then each lane codes
+//     its E values.
 // Writes codes to xq [K], scales to xd [nb] and, when xs is not null, code
 // sums to xs [nb]; ar: the row's addend (RMS_NORM+MUL+ADD) or null; groups:
 // LDS of 16 floats.
-__device__ __forceinline__ void wide_q8_row_quad(const float* __restrict__ xr, const float* __restrict__ g, int K,
-                                                 float eps, bool raw, int8_t* __restrict__ xq,
-                                                 float* __restrict__ xd, int32_t* __restrict__ xs, float* groups,
-                                                 int tid, const float* __restrict__ ar = nullptr) {
+template <int L>
+__device__ __forceinline__ void wide_q8_row_lanes(const float* __restrict__ xr, const float* __restrict__ g, int K,
+                                                  float eps, bool raw, int8_t* __restrict__ xq,
+                                                  float* __restrict__ xd, int32_t* __restrict__ xs, float* groups,
+                                                  int tid, const float* __restrict__ ar = nullptr) {
+  static_assert(L == 2 || L == 4, "two or four lanes per block");
+  constexpr int E = kQK / L;
   const int nb = K / kQK;
-  const int b = tid >> 2, r = tid & 3;
+  const int b = tid / L, r = tid % L;
   const bool on = b < nb;
-  float xv[8], gv[8];
+  float xv[E], gv[E];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) xv[j] = gv[j] = 0.0f;
+  for (int j = 0; j < E; ++j) xv[j] = gv[j] = 0.0f;
   if (on) {
-    const Q4Q8_GLOBAL f32x4* px = gptr(reinterpret_cast<const f32x4*>(xr + b * kQK + 8 * r));
-    const f32x4 a0 = px[0], a1 = px[1];
-    xv[0] = a0.x, xv[1] = a0.y, xv[2] = a0.z, xv[3] = a0.w;
-    xv[4] = a1.x, xv[5] = a1.y, xv[6] = a1.z, xv[7] = a1.w;
+    const Q4Q8_GLOBAL f32x4* px = gptr(reinterpret_cast<const f32x4*>(xr + b * kQK + E * r));
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const f32x4 t = px[i];
+      xv[4 * i] = t.x, xv[4 * i + 1] = t.y, xv[4 * i + 2] = t.z, xv[4 * i + 3] = t.w;
+    }
     if (!raw) {
-      const Q4Q8_GLOBAL f32x4* pg = gptr(reinterpret_cast<const f32x4*>(g + b * kQK + 8 * r));
-      const f32x4 c0 = pg[0], c1 = pg[1];
-      gv[0] = c0.x, gv[1] = c0.y, gv[2] = c0.z, gv[3] = c0.w;
-      gv[4] = c1.x, gv[5] = c1.y, gv[6] = c1.z, gv[7] = c1.w;
+      const Q4Q8_GLOBAL f32x4* pg = gptr(reinterpret_cast<const f32x4*>(g + b * kQK + E * r));
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) {
+        const f32x4 t = pg[i];
+        gv[4 * i] = t.x, gv[4 * i + 1] = t.y, gv[4 * i + 2] = t.z, gv[4 * i + 3] = t.w;
+      }
     }
   }
   float s = 1.0f;
   if (!raw) {
-    float sq[8];
+    float sq[E];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sq[j] = __fmul_rn(xv[j], xv[j]);
+    for (int j = 0; j < E; ++j) sq[j] = __fmul_rn(xv[j], xv[j]);
     // round k: lane k continues the block's sum from lane k - 1's result
     float cin = 0.0f, t = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < L; ++k) {
       t = cin;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t = __fadd_rn(t, sq[j]);
-      const float prev = quad_from_prev(t);
+      for (int j = 0; j < E; ++j) t = __fadd_rn(t, sq[j]);
+      const float prev = lane_from_prev<L>(t);
       cin = r == k + 1 ? prev : cin;
     }
-    s = wide_rms_scale(wave_tree_sum(r == 3 ? t : 0.0f), K, eps, groups, tid);
+    s = wide_rms_scale(wave_tree_sum(r == L - 1 ? t : 0.0f), K, eps, groups, tid);
   }
-  float v[8];
+  float v[E];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = raw ? xv[j] : __fmul_rn(__fmul_rn(xv[j], s), gv[j]);
+  for (int j = 0; j < E; ++j) v[j] = raw ? xv[j] : __fmul_rn(__fmul_rn(xv[j], s), gv[j]);
   if (ar && on) {
-    const Q4Q8_GLOBAL f32x4* pa = gptr(reinterpret_cast<const f32x4*>(ar + b * kQK + 8 * r));
-    const f32x4 a0 = pa[0], a1 = pa[1];
-    v[0] = __fadd_rn(v[0], a0.x), v[1] = __fadd_rn(v[1], a0.y), v[2] = __fadd_rn(v[2], a0.z);
-    v[3] = __fadd_rn(v[3], a0.w), v[4] = __fadd_rn(v[4], a1.x), v[5] = __fadd_rn(v[5], a1.y);
-    v[6] = __fadd_rn(v[6], a1.z), v[7] = __fadd_rn(v[7], a1.w);
-  }
-  float m[4];
+    const Q4Q8_GLOBAL f32x4* pa = gptr(reinterpret_cast<const f32x4*>(ar + b * kQK + E * r));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) m[j] = fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1]));
-  const float amax = quad_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+    for (int i = 0; i < E / 4; ++i) {
+      const f32x4 t = pa[i];
+      v[4 * i] = __fadd_rn(v[4 * i], t.x), v[4 * i + 1] = __fadd_rn(v[4 * i + 1], t.y);
+      v[4 * i + 2] = __fadd_rn(v[4 * i + 2], t.z), v[4 * i + 3] = __fadd_rn(v[4 * i + 3], t.w);
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < E; j += 2) m = fmaxf(m, fmaxf(fabsf(v[j]), fabsf(v[j + 1])));
+  const float amax = group_max<L>(m);
   const float d = __fdiv_rn(amax, 127.0f);
   const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
-  uint32_t w[2];
+  uint32_t w[E / 4];
   int csum = 0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < E / 4; ++h) {
     uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int qi = (int)roundf(__fmul_rn(v[4 * h + k], id));
+      int qi = round_half_away_i32(__fmul_rn(v[4 * h + k], id));
       qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
       csum += qi;
       word |= ((uint32_t)qi & 0xFFu) << (8 * k);
     }
     w[h] = word;
   }
-  if (xs) {  // the block's code sum over the quad (exact integer adds)
-    csum += __builtin_amdgcn_update_dpp(0, csum, 0xB1, 0xF, 0xF, false);
-    csum += __builtin_amdgcn_update_dpp(0, csum, 0x4E, 0xF, 0xF, false);
-  }
+  if (xs) csum = group_isum<L>(csum);  // exact integer adds
   if (on) {
-    *gptr_w(reinterpret_cast<u32x2_t*>(xq + b * kQK + 8 * r)) = u32x2_t{w[0], w[1]};
+    if constexpr (E == 8) {
+      *gptr_w(reinterpret_cast<u32x2_t*>(xq + b * kQK + E * r)) = u32x2_t{w[0], w[1]};
+    } else {
+      *gptr_w(reinterpret_cast<u32x4*>(xq + b * kQK + E * r)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
     if (r == 0) {
       gptr_w(xd)[b] = d;
       if (xs) gptr_w(xs)[b] = csum;
