@@ -37,6 +37,7 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--skip-extras]
        python bench.py --decode-8b-only B 10 (Llama-3-8B-shaped decode steps at batch B for rocprofv3 runs)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [REQ_DIR]   (traffic summary)
        python bench.py --trace-summary DIR   (kernel durations of a --kernel-trace run)
+       python bench.py --trace-calls DIR KERNEL ROLE [ROLE ...]   (one kernel's dispatches by role, in order)
        python bench.py --counter-summary KERNEL DIR [DIR ...]   (counters of --pmc runs)
 """
 from __future__ import annotations
@@ -687,9 +688,37 @@ def trace_summary(trace_dir):
         print(f"{name[:58]:58s} {len(v):6d} {statistics.fmean(v):9.2f} {statistics.median(v):10.2f} "
               f"{min(v):9.2f} {max(v):9.2f}")
     if res:
-        print("\nresources (arch VGPRs, accumulation VGPRs, SGPRs, LDS bytes) per kernel instance:")
+        print("\nresources per kernel instance, as the trace records them: VGPR_Count (on gfx950 half the\n"
+              "compiler's per-lane VGPR count, e.g. 234 -> 120), accumulation VGPRs, SGPRs, LDS bytes:")
         for name, (v, a, sg, lds) in sorted(res.items()):
             print(f"  {name}: {v} / {a} / {sg} / {lds}")
+
+
+def trace_calls(trace_dir, needle, roles):
+    """Durations of the dispatches of the kernel whose name contains `needle`
+    in a --kernel-trace run, in launch order, dispatch i counted for role
+    roles[i % len(roles)] (e.g. the two routed calls of a MoE step, which
+    launch the same kernel instance): calls, mean, median, min, max in us."""
+    import csv
+    import glob
+    import statistics
+
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if needle in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = {k: [] for k in roles}
+    for i, r in enumerate(rows):
+        per[roles[i % len(roles)]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"{'call':20s} {'calls':>6s} {'mean us':>9s} {'median us':>10s} {'min us':>9s} {'max us':>9s}")
+    for k in roles:
+        v = per[k]
+        print(f"{k:20s} {len(v):6d} {statistics.fmean(v):9.2f} {statistics.median(v):10.2f} {min(v):9.2f} "
+              f"{max(v):9.2f}")
 
 
 def counter_summary(needle, dirs):
@@ -1088,6 +1117,8 @@ def main():
                     help="launch N steps and N streaming passes (after a calibration copy) and exit")
     ap.add_argument("--decode-8b-only", nargs=2, type=int, default=None, metavar=("B", "N"),
                     help="N grouped Llama-3-8B-shaped decode steps at batch B (for rocprofv3 runs)")
+    ap.add_argument("--trace-calls", nargs="+", metavar="ARG",
+                    help="DIR KERNEL ROLE [ROLE ...]: per-role durations of one kernel's dispatches in launch order")
     ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
                     help="KERNEL_SUBSTRING DIR [DIR ...]: per-dispatch counter medians of rocprofv3 --pmc runs "
                          "(no GPU needed)")
@@ -1102,6 +1133,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.trace_calls:
+        trace_calls(args.trace_calls[0], args.trace_calls[1], args.trace_calls[2:])
         return
     if args.counter_summary:
         counter_summary(args.counter_summary[0], args.counter_summary[1:])
