@@ -60,7 +60,7 @@ class GroupPlan(ctypes.Structure):
                 ("map_offset", ctypes.c_int64), ("prologue_offset", ctypes.c_int64),
                 ("table_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("weight_formats", ctypes.c_int32), ("max_prologue_k", ctypes.c_int32),
-                ("mfma_columns", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("mfma_columns", ctypes.c_int32), ("mfma_grid", ctypes.c_int32)]
 
 
 _lib = None

@@ -141,7 +141,7 @@ int matmul_common(const uint8_t* qs, const uint16_t* d, int64_t M, int64_t K, co
     const int win = q4q8::gemv_mfma_window_rows();
     p.n_win = (int32_t)((M + win - 1) / win);
     g_counts[0].fetch_add(1, std::memory_order_relaxed);
-    return launched(q4q8::launch_gemv_mfma(p, nullptr, nullptr, p.n_win, B, I, s, wf), "gemv (multi-column)");
+    return launched(q4q8::launch_gemv_mfma(p, nullptr, nullptr, p.n_win, 0, B, I, s, wf), "gemv (multi-column)");
   }
   if (use_gemv) {
     q4q8::GemvProblem p = single_problem(qs, d, M, K, y);
@@ -552,34 +552,49 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   if (tiled)
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t a, int32_t b) { return recs[a].K > recs[b].K; });
-  {
-    // cost_begin: the cost-balanced shares of the multi-column kernel (cost
-    // of a window = K / 32 blocks per row; its windows all have 64 rows)
-    int64_t first = 0, cost = 0;
+  // Multi-column groups: the windows are packed into one bin per workgroup
+  // (cost of a window = K / 32 blocks per row, its 64 rows being common), and
+  // each run of consecutive windows of one product in a bin becomes a record
+  // of its own (win_off: its first window within the product).  Other
+  // routes: one record per product, its windows consecutive.
+  std::vector<q4q8::MfRun> runs;
+  std::vector<int64_t> bounds;
+  int64_t mfma_grid = 0;
+  if (mfma_group && !recs.empty()) {
+    std::vector<int64_t> cost(recs.size());
+    int64_t total = 0;
+    for (size_t r = 0; r < recs.size(); ++r) {
+      cost[r] = recs[r].K / q4q8::kQK;
+      total += rec_tiles[r] * cost[r];
+    }
+    if (total > INT32_MAX)
+      return fail(Q4Q8_E_UNSUPPORTED, "group too large for the multi-column route (windows x K / 32 > 2^31)");
+    mfma_grid = std::min<int64_t>(q4q8::gemv_mfma_group_grid(mfma_wf), tiles);
+    q4q8::gemv_mfma_pack(rec_tiles, cost, mfma_grid, runs, bounds);
+  } else {
+    int64_t first = 0;
     for (int32_t r : order) {
       recs[r].win_begin = (int32_t)first;
-      recs[r].cost_begin = (int32_t)std::min<int64_t>(cost, INT32_MAX);
       first += rec_tiles[r];
-      cost += rec_tiles[r] * (recs[r].K / q4q8::kQK);
     }
-    if (mfma_group && cost > INT32_MAX)
-      return fail(Q4Q8_E_UNSUPPORTED, "group too large for the multi-column route (windows x K / 32 > 2^31)");
   }
+  const int64_t n_records = mfma_grid ? (int64_t)runs.size() : (int64_t)recs.size();
   plan->B = (int32_t)B;
-  plan->n_records = (int32_t)recs.size();
+  plan->n_records = (int32_t)n_records;
   plan->n_prologue = (int32_t)inputs.size();
   plan->n_windows = tiles;
   plan->max_k = max_k;
-  plan->map_offset = (int64_t)(recs.size() * sizeof(q4q8::GemvProblem));
-  plan->prologue_offset = (plan->map_offset + tiles * (int64_t)sizeof(int32_t) + 15) / 16 * 16;
+  plan->map_offset = n_records * (int64_t)sizeof(q4q8::GemvProblem);
+  plan->prologue_offset =
+      (plan->map_offset + (tiles + (mfma_grid ? mfma_grid + 1 : 0)) * (int64_t)sizeof(int32_t) + 15) / 16 * 16;
   plan->table_bytes = plan->prologue_offset + (int64_t)(inputs.size() * sizeof(q4q8::PrologueJob));
   plan->workspace_bytes = ws_total;
   plan->weight_formats = 0;
   for (const q4q8::GemvProblem& r : recs) plan->weight_formats |= 1 << r.wf;
   plan->max_prologue_k = 0;
   for (const Input& in : inputs) plan->max_prologue_k = std::max(plan->max_prologue_k, (int32_t)in.K);
-  plan->mfma_columns = mfma_group ? 1 : 0;
-  plan->reserved = 0;
+  plan->mfma_columns = mfma_grid ? 1 : 0;
+  plan->mfma_grid = (int32_t)mfma_grid;
   plan->magic = kGroupMagic;
   if (!table_host) return ok();
   const char* why = nullptr;
@@ -603,11 +618,25 @@ Q4Q8_EXPORT int q4q8_group_build(const q4q8_gemv_desc* descs, int32_t n, int64_t
   }
   char* out = static_cast<char*>(table_host);
   memset(out, 0, (size_t)plan->table_bytes);
-  memcpy(out, recs.data(), recs.size() * sizeof(q4q8::GemvProblem));
   int32_t* map = reinterpret_cast<int32_t*>(out + plan->map_offset);
-  int64_t m = 0;
-  for (int32_t r : order)
-    for (int64_t t = 0; t < rec_tiles[r]; ++t) map[m++] = r;
+  if (mfma_grid) {
+    q4q8::GemvProblem* rec_out = reinterpret_cast<q4q8::GemvProblem*>(out);
+    int64_t m = 0;
+    for (size_t i = 0; i < runs.size(); ++i) {
+      q4q8::GemvProblem p = recs[runs[i].rec];
+      p.win_begin = (int32_t)m;
+      p.n_win = runs[i].count;
+      p.win_off = runs[i].first;
+      rec_out[i] = p;
+      for (int32_t t = 0; t < runs[i].count; ++t) map[m++] = (int32_t)i;
+    }
+    for (size_t g = 0; g < bounds.size(); ++g) map[tiles + g] = (int32_t)bounds[g];
+  } else {
+    memcpy(out, recs.data(), recs.size() * sizeof(q4q8::GemvProblem));
+    int64_t m = 0;
+    for (int32_t r : order)
+      for (int64_t t = 0; t < rec_tiles[r]; ++t) map[m++] = r;
+  }
   q4q8::PrologueJob* jobs = reinterpret_cast<q4q8::PrologueJob*>(out + plan->prologue_offset);
   for (size_t k = 0; k < inputs.size(); ++k) {
     const Input& in = inputs[k];
@@ -635,12 +664,16 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   if (plan->n_records < 0 || plan->B < 1 || plan->B > 65535 || plan->n_windows < plan->n_records ||
       plan->n_windows > INT32_MAX || plan->n_prologue < 0 || plan->n_prologue > plan->n_records ||
       plan->max_k < q4q8::kQK || plan->max_k % q4q8::kQK != 0 ||
-      plan->mfma_columns < 0 || plan->mfma_columns > 1 || plan->reserved != 0 ||
+      plan->mfma_columns < 0 || plan->mfma_columns > 1 ||
+      (plan->mfma_columns ? plan->mfma_grid < 1 || plan->mfma_grid > plan->n_windows : plan->mfma_grid != 0) ||
       (plan->mfma_columns && (tiled || plan->B < q4q8::kGemvMfmaMinB || plan->max_k < 512 || plan->max_k % 128 != 0 ||
                                  plan->weight_formats == 3)) ||
       (!tiled && !plan->mfma_columns && !q4q8::gemv_supported(1, plan->max_k, plan->B)) ||
       plan->map_offset != (int64_t)plan->n_records * (int64_t)sizeof(q4q8::GemvProblem) ||
-      plan->prologue_offset != (plan->map_offset + plan->n_windows * (int64_t)sizeof(int32_t) + 15) / 16 * 16 ||
+      plan->prologue_offset != (plan->map_offset +
+                                (plan->n_windows + (plan->mfma_columns ? plan->mfma_grid + 1 : 0)) *
+                                    (int64_t)sizeof(int32_t) +
+                                15) / 16 * 16 ||
       plan->table_bytes != plan->prologue_offset + plan->n_prologue * (int64_t)sizeof(q4q8::PrologueJob) ||
       plan->weight_formats < 1 || plan->weight_formats > 3 || plan->max_prologue_k < 0 ||
       plan->max_prologue_k > plan->max_k || plan->max_prologue_k % q4q8::kQK != 0 ||
@@ -675,7 +708,7 @@ Q4Q8_EXPORT int mul_mat_q4q8_group(const void* table_dev, const q4q8_group_plan*
   if (plan->mfma_columns)
     return launched(q4q8::launch_gemv_mfma(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                            reinterpret_cast<const int32_t*>(base + plan->map_offset),
-                                           plan->n_windows, plan->B, nullptr, s, wf),
+                                           plan->n_windows, plan->mfma_grid, plan->B, nullptr, s, wf),
                     "mul_mat_q4q8_group (multi-column)");
   return launched(q4q8::launch_gemv_table(unused, reinterpret_cast<const q4q8::GemvProblem*>(base),
                                           reinterpret_cast<const int32_t*>(base + plan->map_offset),

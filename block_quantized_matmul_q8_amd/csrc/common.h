@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #define Q4Q8_HIDDEN __attribute__((visibility("hidden")))
 
 namespace q4q8 {
@@ -162,7 +164,8 @@ struct alignas(16) GemvProblem {
   int32_t win_begin;   // index of this problem's first window in the launch
   int32_t n_win;       // windows of this problem (ceil(M / window rows))
   int32_t wf;          // weight format of qs (WeightFormat)
-  int32_t cost_begin;  // grouped launches: sum of n_win * K / 32 over the records before this one
+  int32_t win_off;     // index, within its product, of this record's first window (multi-column
+                       // groups split a product's windows over several records; else 0)
 };
 static_assert(sizeof(GemvProblem) == 96, "GemvProblem layout");
 
@@ -198,11 +201,28 @@ Q4Q8_HIDDEN bool gemv_route_supported(int64_t M, int64_t K, int64_t B, int wf);
 // require d and xd 16-byte aligned, and one weight format per launch.
 constexpr int kGemvMfmaMinB = 5;
 Q4Q8_HIDDEN bool gemv_mfma_ok(int64_t M, int64_t K, int64_t B, int wf);
-// Rows per window of the MFMA multi-column kernel, and its launcher (same
-// table / map conventions as launch_gemv_table; records carry cost_begin).
+// Rows per window of the MFMA multi-column kernel, and its launcher.  A
+// single product (table == nullptr) is split into equal shares of its
+// windows; a group launches `groups` workgroups over a table whose map
+// (window -> record, n_windows entries) is followed by groups + 1 window
+// indices: workgroup g streams windows [bounds[g], bounds[g + 1]).
 Q4Q8_HIDDEN int gemv_mfma_window_rows();
 Q4Q8_HIDDEN hipError_t launch_gemv_mfma(const GemvProblem& p, const GemvProblem* table, const int32_t* map,
-                                        int64_t n_windows, int64_t B, int32_t* I, hipStream_t s, int wf);
+                                        int64_t n_windows, int64_t groups, int64_t B, int32_t* I, hipStream_t s,
+                                        int wf);
+// Workgroups a grouped multi-column launch takes on the current device (all
+// resident at once; 2 per CU x 256 CUs when no device answers).
+Q4Q8_HIDDEN int64_t gemv_mfma_group_grid(int wf);
+// Packs the windows of a multi-column group into `groups` workgroup bins of
+// near-equal cost (a window of record r costs cost[r] = K / 32, its 64 rows
+// being common).  Output, in launch order: runs of consecutive windows of one
+// record (rec, first window within it, count), and groups + 1 bounds (bin g
+// holds launch windows [bounds[g], bounds[g + 1])).
+struct MfRun {
+  int32_t rec, first, count;
+};
+Q4Q8_HIDDEN void gemv_mfma_pack(const std::vector<int64_t>& n_win, const std::vector<int64_t>& cost, int64_t groups,
+                                std::vector<MfRun>& runs, std::vector<int64_t>& bounds);
 Q4Q8_HIDDEN bool gemv_fused_supported(int64_t K, int64_t B);
 // Rows per window (the unit a workgroup streams) for a product with K and B;
 // wf: weight format (kWeightQ4 or kWeightQ8); fold: the folded-prologue form.

@@ -43,9 +43,13 @@
 // serves well (a wave alone on a window would read 128 bytes per row and 16
 // bytes of scales, and the scale lines, revisited chunk after chunk, leave
 // L2 in between).  At a window's end the four partial sums meet in LDS and
-// are added in wave order, so results do not depend on timing.  Each
-// workgroup takes a contiguous share of the windows of the launch, balanced
-// by cost (rows x K), so products with long and short K mix evenly.
+// are added in wave order, so results do not depend on timing.  A single
+// product is split into equal shares of its windows.  A group's windows are
+// packed on the host into one bin per workgroup, of near-equal cost (rows x
+// K), so that products with long and short K mix evenly: a row's sum never
+// depends on which workgroup streams its window, so the packing leaves every
+// result bit-identical.
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -101,13 +105,11 @@ __device__ __forceinline__ MfWindow mf_window(const GemvProblem& P, int w) {
   W.M = P.M;
   W.K = P.K;
   W.nb = P.K >> 5;
-  W.row0 = (w - P.win_begin) * kMfRows;
+  W.row0 = (w - P.win_begin + P.win_off) * kMfRows;
   W.nch = (P.K >> 6) / mf_pairs_per_chunk<WF>();  // the route takes K of >= 4 whole chunks only
   return W;
 }
 
-// Cost of a window of record P, in blocks per row (its 64 rows are common).
-__device__ __forceinline__ int64_t mf_win_cost(const GemvProblem& P) { return P.K >> 5; }
 
 // Load addresses of a window for the wave's lanes, at chunk 0 (chunk c adds
 // a uniform offset).  Weight stream (direct-to-LDS):
@@ -416,30 +418,6 @@ __device__ __forceinline__ void mf_store(const MfOut& O, int lane, int B) {
   }
 }
 
-// First window whose start cost is >= c (windows are in record order and a
-// record's windows are consecutive): records are scanned 64 at a time.
-__device__ __forceinline__ int mf_first_window(const GemvProblem* __restrict__ table, int n_rec, int64_t c,
-                                               int n_windows, int lane) {
-  for (int base = 0; base < n_rec; base += kWave) {
-    const int k = base + lane;
-    int64_t end = 0;
-    if (k < n_rec) {
-      const GemvProblem& P = table[k];
-      end = (int64_t)P.cost_begin + (int64_t)P.n_win * mf_win_cost(P);
-    }
-    const uint64_t mask = __ballot(k < n_rec && end > c);
-    if (mask) {
-      const int rec = base + __builtin_ctzll(mask);
-      const GemvProblem& P = table[rec];
-      const int64_t wc = mf_win_cost(P);
-      const int64_t off = c - P.cost_begin;
-      const int64_t j = off <= 0 ? 0 : (off + wc - 1) / wc;
-      return P.win_begin + (int)j;  // j < n_win because end > c
-    }
-  }
-  return n_windows;
-}
-
 template <bool GROUPED, bool WRITE_I, int WF>
 __global__ __launch_bounds__(kMfThreads, 2) void gemv_mfma_kernel(GemvProblem p0,
                                                                   const GemvProblem* __restrict__ table,
@@ -449,15 +427,16 @@ __global__ __launch_bounds__(kMfThreads, 2) void gemv_mfma_kernel(GemvProblem p0
   __shared__ __align__(16) uint8_t lds[kMfWaves * 2 * kMfBufBytes + sizeof(MfExchange)];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  // this workgroup's share of the windows
+  // The window -> record map (and, after it, the workgroups' window bounds)
+  // is read through the constant address space: scalar loads, which do not
+  // wait behind the vector loads in flight.
+  const __attribute__((address_space(4))) int32_t* cmap = (const __attribute__((address_space(4))) int32_t*)win_map;
+  // this workgroup's windows
   const int64_t G = gridDim.x, gi = blockIdx.x;
   int w_lo, w_hi;
   if constexpr (GROUPED) {
-    const int n_rec = win_map[n_windows - 1] + 1;
-    const GemvProblem& last = table[n_rec - 1];
-    const int64_t C = (int64_t)last.cost_begin + (int64_t)last.n_win * mf_win_cost(last);
-    w_lo = mf_first_window(table, n_rec, C * gi / G, n_windows, lane);
-    w_hi = mf_first_window(table, n_rec, C * (gi + 1) / G, n_windows, lane);
+    w_lo = cmap[n_windows + gi];
+    w_hi = cmap[n_windows + gi + 1];
   } else {
     w_lo = (int)(n_windows * gi / G);
     w_hi = (int)(n_windows * (gi + 1) / G);
@@ -465,9 +444,6 @@ __global__ __launch_bounds__(kMfThreads, 2) void gemv_mfma_kernel(GemvProblem p0
   w_lo = __builtin_amdgcn_readfirstlane(w_lo);
   w_hi = __builtin_amdgcn_readfirstlane(w_hi);
   if (w_lo >= w_hi) return;  // the whole workgroup: no barrier is left waiting
-  // the window -> record map is read through the constant address space:
-  // scalar loads, which do not wait behind the vector loads in flight
-  const __attribute__((address_space(4))) int32_t* cmap = (const __attribute__((address_space(4))) int32_t*)win_map;
   auto window = [&](int w) -> MfWindow {
     if constexpr (GROUPED)
       return mf_window<WF>(table[cmap[w]], w);
@@ -604,31 +580,44 @@ __global__ __launch_bounds__(kMfThreads, 2) void gemv_mfma_kernel(GemvProblem p0
 
 int gemv_mfma_window_rows() { return kMfRows; }
 
+// Workgroups of `kernel` resident at once on the current device.  Without a
+// device (a plan built on a host with no GPU) the figure is the launch bound
+// of these kernels on gfx950: 2 per CU x 256 CUs.
 static int64_t mf_resident_workgroups(const void* kernel) {
   static std::mutex mu;
   static std::vector<std::pair<std::pair<const void*, int>, int64_t>> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 2 * 256;
   std::lock_guard<std::mutex> lk(mu);
   for (const auto& e : cache)
     if (e.first.first == kernel && e.first.second == dev) return e.second;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMfThreads, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
+    per_cu = 2;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
   const int64_t n = (int64_t)per_cu * cus;
   cache.push_back({{kernel, dev}, n});
   return n;
 }
 
+int64_t gemv_mfma_group_grid(int wf) {
+  return mf_resident_workgroups(wf == kWeightQ8 ? (const void*)gemv_mfma_kernel<true, false, kWeightQ8>
+                                                : (const void*)gemv_mfma_kernel<true, false, kWeightQ4>);
+}
+
 hipError_t launch_gemv_mfma(const GemvProblem& p, const GemvProblem* table, const int32_t* map, int64_t n_windows,
-                            int64_t B, int32_t* I, hipStream_t s, int wf) {
+                            int64_t groups, int64_t B, int32_t* I, hipStream_t s, int wf) {
   if (B < 1 || B > 8 || n_windows < 1 || n_windows > INT32_MAX) return hipErrorInvalidValue;
-  if (table && I) return hipErrorInvalidValue;
+  if (table && (I || groups < 1 || groups > n_windows)) return hipErrorInvalidValue;
   auto go = [&](auto kernel) {
-    // every workgroup streams whole windows: no more workgroups than windows
-    int64_t grid = mf_resident_workgroups((const void*)kernel);
-    if (grid > n_windows) grid = n_windows;
+    // a group: one workgroup per bin of the table; a single product: the
+    // resident workgroups, each streaming whole windows (no more workgroups
+    // than windows)
+    int64_t grid = groups;
+    if (!table) {
+      grid = mf_resident_workgroups((const void*)kernel);
+      if (grid > n_windows) grid = n_windows;
+    }
     note_launch((const void*)kernel);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kMfThreads), 0, s, p, table, map, (int)n_windows, (int)B,
                        I);
@@ -644,6 +633,95 @@ hipError_t launch_gemv_mfma(const GemvProblem& p, const GemvProblem* table, cons
   if (wf == kWeightQ8)
     return I ? go(gemv_mfma_kernel<false, true, kWeightQ8>) : go(gemv_mfma_kernel<false, false, kWeightQ8>);
   return hipErrorInvalidValue;
+}
+
+// Bins are filled in launch order.  Bin g aims to bring the running cost to
+// C * (g + 1) / G (C: the group's total), so a bin that falls short leaves
+// the difference to the next one.  A bin takes the combination of windows
+// whose cost comes closest to its room without exceeding it; among equal
+// totals, the one with more of the costlier windows (those are the hard ones
+// to place late).  Combinations are searched costliest class first, with a
+// node budget past which the rest of a search takes the largest counts that
+// fit.  Within a cost class, windows go in record order, so a bin holds few
+// runs.  The last bin takes whatever is left.
+void gemv_mfma_pack(const std::vector<int64_t>& n_win, const std::vector<int64_t>& cost, int64_t groups,
+                    std::vector<MfRun>& runs, std::vector<int64_t>& bounds) {
+  struct Seg {
+    int32_t rec;
+    int64_t n;
+  };
+  struct Cls {
+    int64_t c = 0, avail = 0, off = 0;
+    size_t si = 0;
+    std::vector<Seg> segs;
+  };
+  std::vector<Cls> cls;
+  int64_t C = 0;
+  for (size_t r = 0; r < n_win.size(); ++r) {
+    if (n_win[r] <= 0) continue;
+    size_t k = 0;
+    while (k < cls.size() && cls[k].c != cost[r]) ++k;
+    if (k == cls.size()) {
+      cls.emplace_back();
+      cls.back().c = cost[r];
+    }
+    cls[k].segs.push_back({(int32_t)r, n_win[r]});
+    cls[k].avail += n_win[r];
+    C += n_win[r] * cost[r];
+  }
+  std::stable_sort(cls.begin(), cls.end(), [](const Cls& a, const Cls& b) { return a.c > b.c; });
+  const int m = (int)cls.size();
+  runs.clear();
+  bounds.assign(1, 0);
+  int64_t placed = 0, n_placed = 0;
+  auto take = [&](Cls& k, int64_t cnt) {
+    while (cnt > 0) {
+      const Seg& sg = k.segs[k.si];
+      const int64_t t = std::min(cnt, sg.n - k.off);
+      if (!runs.empty() && runs.back().rec == sg.rec && runs.back().first + runs.back().count == k.off)
+        runs.back().count += (int32_t)t;
+      else
+        runs.push_back({sg.rec, (int32_t)k.off, (int32_t)t});
+      k.off += t;
+      k.avail -= t;
+      cnt -= t;
+      n_placed += t;
+      placed += t * k.c;
+      if (k.off == sg.n) {
+        ++k.si;
+        k.off = 0;
+      }
+    }
+  };
+  constexpr int64_t kNodeBudget = 1 << 14;
+  std::vector<int64_t> x(m), best(m);
+  for (int64_t g = 0; g < groups; ++g) {
+    if (g + 1 == groups) {
+      for (Cls& k : cls) take(k, k.avail);
+    } else {
+      const int64_t room = C * (g + 1) / groups - placed;
+      int64_t best_sum = -1, nodes = 0;
+      auto search = [&](auto&& self, int i, int64_t rem, int64_t sum) -> void {
+        if (i == m) {
+          if (sum > best_sum) {
+            best_sum = sum;
+            best = x;
+          }
+          return;
+        }
+        const int64_t hi = std::min(cls[i].avail, rem > 0 ? rem / cls[i].c : 0);
+        for (int64_t v = hi; v >= 0; --v) {
+          x[i] = v;
+          self(self, i + 1, rem - v * cls[i].c, sum + v * cls[i].c);
+          if (best_sum == room || ++nodes > kNodeBudget) break;
+        }
+        x[i] = 0;
+      };
+      search(search, 0, room, 0);
+      for (int i = 0; i < m; ++i) take(cls[i], best[i]);
+    }
+    bounds.push_back(n_placed);
+  }
 }
 
 }  // namespace q4q8

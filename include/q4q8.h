@@ -248,7 +248,8 @@ typedef struct q4q8_gemv_desc {
 typedef struct q4q8_group_plan {
   uint32_t magic;          /* set by q4q8_group_build */
   int32_t B;
-  int32_t n_records;       /* product records in the table image */
+  int32_t n_records;       /* records in the table image: one per product, or on the multi-column
+                              route one per run of a product's windows within a bin */
   int32_t n_prologue;      /* distinct fp32 inputs the prologue pass quantises */
   int64_t n_windows;       /* work windows of the streaming pass (rows of ~32 KiB of weights) */
   int64_t max_k;           /* largest K of a product (also selects the kernel instance) */
@@ -264,7 +265,12 @@ typedef struct q4q8_group_plan {
                               of 128 and >= 512 for Q8_0,
                               d and xd 16-byte aligned; windows of 64 rows), 0: the
                               lane-per-block one */
-  int32_t reserved;        /* 0 */
+  int32_t mfma_grid;       /* multi-column route: workgroups of the streaming launch, the ones
+                              resident at once on the device current at build time (2 per CU;
+                              512 when no device answers).  The host packs the windows into one bin
+                              of near-equal cost (rows x K) per workgroup; a product's windows may
+                              then span several records, and the map is followed by mfma_grid + 1
+                              window indices (the bins' bounds).  0 on the other routes. */
 } q4q8_group_plan;
 /* Every field is written by q4q8_group_build and read as it left them: a
  * launch checks their consistency but cannot detect every edited value. */

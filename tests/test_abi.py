@@ -209,7 +209,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     src.write_text('#include "q4q8.h"\n#include <stdio.h>\n#include <stddef.h>\n'
                    'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(q4q8_gemv_desc), sizeof(q4q8_group_plan),'
                    ' offsetof(q4q8_gemv_desc, y), offsetof(q4q8_group_plan, workspace_bytes),'
-                   ' offsetof(q4q8_group_plan, weight_formats));return 0;}\n')
+                   ' offsetof(q4q8_group_plan, weight_formats));'
+                   'printf("%zu\\n", offsetof(q4q8_group_plan, mfma_grid));return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
@@ -218,6 +219,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     assert int(out[2]) == q.GemvDesc.y.offset
     assert int(out[3]) == q.GroupPlan.workspace_bytes.offset
     assert int(out[4]) == q.GroupPlan.weight_formats.offset
+    assert int(out[5]) == q.GroupPlan.mfma_grid.offset
 
 
 def _desc(M=64, K=2048, qs=256, d=256, xq=256, xd=256, x=None, g=None, y=256, flags=0, eps=1e-5):
@@ -373,6 +375,80 @@ def test_group_prologue_lds_sized_by_prologue_inputs_only():
     assert plan.max_prologue_k == 0 and plan.n_prologue == 0
 
 
+def _mfma_bins(image, plan):
+    """Per-bin window lists of a multi-column plan: [(product qs, window within it, K)] per bin,
+    after checking the records, the map and the bounds against each other."""
+    n, W, G = plan.n_records, plan.n_windows, plan.mfma_grid
+    assert plan.mfma_columns == 1 and 1 <= G <= W
+    assert plan.map_offset == n * 96
+    assert plan.prologue_offset == (plan.map_offset + 4 * (W + G + 1) + 15) // 16 * 16
+    recs = image[:plan.map_offset].view(np.int32).reshape(n, 24)
+    ptrs = image[:plan.map_offset].view(np.int64).reshape(n, 12)
+    words = image[plan.map_offset:plan.map_offset + 4 * (W + G + 1)].view(np.int32)
+    wmap, bounds = words[:W], words[W:]
+    # records in launch order, each a run of consecutive windows
+    assert recs[0, 18] == 0 and (recs[1:, 18] == np.cumsum(recs[:-1, 19])).all() and recs[:, 19].sum() == W
+    assert (wmap == np.repeat(np.arange(n), recs[:, 19])).all()
+    assert bounds[0] == 0 and bounds[-1] == W and (np.diff(bounds) >= 0).all()
+    windows = []
+    for r in range(n):
+        windows += [(int(ptrs[r, 0]), int(recs[r, 21]) + j, int(recs[r, 15])) for j in range(recs[r, 19])]
+    return [windows[bounds[g]:bounds[g + 1]] for g in range(G)]
+
+
+def test_group_build_multicolumn_packs_windows():
+    """B = 5..8 groups on the multi-column route: the host packs the windows
+    (64 rows each, cost K / 32) into one bin per workgroup.  Every window of
+    every product is listed once; for eight Llama-3-8B-shaped layers the bins
+    come out exactly equal (two down-projection windows and six of K = 4096,
+    or thirteen of K = 4096: 1664 each), where contiguous cost shares of the
+    caller's order leave up to 1792."""
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
+    descs, products = [], {}
+    for l in range(8):
+        for i, (M, K) in enumerate(shapes):
+            qs = 4096 * (1 + 7 * l + i)
+            descs.append(_desc(M=M, K=K, qs=qs))
+            products[qs] = (M, K)
+    image, plan = _build(descs, 8)
+    bins = _mfma_bins(image, plan)
+    listed = sorted((qs, w) for b in bins for (qs, w, _) in b)
+    assert listed == sorted((qs, w) for qs, (M, K) in products.items() for w in range((M + 63) // 64))
+    for b in bins:
+        for qs, w, K in b:
+            assert products[qs][1] == K
+    costs = [sum(K // 32 for (_, _, K) in b) for b in bins]
+    total = sum(costs)
+    if plan.mfma_grid == 512:
+        assert max(costs) == min(costs) == total // 512 == 1664
+    assert max(costs) <= -(-total // plan.mfma_grid) + 448
+    # a product's windows keep their order within each record
+    assert plan.n_records < 2 * plan.mfma_grid + len(descs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_build_multicolumn_random_groups(seed):
+    """Random groups of Q4 or Q8_0 products: every window listed once, and no
+    bin above the mean bin cost by more than one window of the costliest K."""
+    rng = np.random.default_rng(seed)
+    wf = q.WEIGHTS_Q8_0 if seed % 2 else 0
+    kq = 128 if wf else 256
+    descs, products = [], {}
+    for i in range(int(rng.integers(1, 40))):
+        M = int(rng.integers(1, 20000))
+        K = kq * int(rng.integers(1024 // kq, 60))
+        qs = 4096 * (i + 1)
+        descs.append(_desc(M=M, K=K, qs=qs, flags=wf))
+        products[qs] = (M, K)
+    image, plan = _build(descs, int(rng.integers(5, 9)))
+    bins = _mfma_bins(image, plan)
+    listed = sorted((qs, w) for b in bins for (qs, w, _) in b)
+    assert listed == sorted((qs, w) for qs, (M, K) in products.items() for w in range((M + 63) // 64))
+    costs = [sum(K // 32 for (_, _, K) in b) for b in bins]
+    kmax = max(K for (M, K) in products.values()) // 32
+    assert max(costs) <= -(-sum(costs) // plan.mfma_grid) + kmax
+
+
 def test_group_launch_rejects_foreign_plans():
     L = q.lib()
     plan = q.GroupPlan()
@@ -385,6 +461,15 @@ def test_group_launch_rejects_foreign_plans():
         bad = q.GroupPlan.from_buffer_copy(good)
         setattr(bad, field, value)
         assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, field
+    # the multi-column route's workgroup count must lie in [1, n_windows], and is 0 elsewhere
+    _, mc = _build([_desc(M=4096, K=4096)], 8)
+    for value in (0, mc.n_windows + 1):
+        bad = q.GroupPlan.from_buffer_copy(mc)
+        bad.mfma_grid = value
+        assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG, value
+    bad = q.GroupPlan.from_buffer_copy(good)
+    bad.mfma_grid = 1
+    assert L.mul_mat_q4q8_group(ctypes.c_void_p(256), ctypes.byref(bad), None) == q.Q4Q8_E_ARG
 
 
 def test_fused_single_validation():
