@@ -36,14 +36,16 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr size_t kGemvMaxLds = 64 * 1024;
 
-// Butterfly sum of N values per lane over the 64 lanes.  Lane L returns the
-// total of value index L >> (6 - log2 N); each exchange step halves the
-// number of values a lane carries, so the cost is N - 1 + 6 - log2 N
-// shuffles instead of 6 N.
-template <int N>
+// Butterfly sum of N values per lane over each group of L consecutive lanes
+// (L = 64: the whole wave).  Lane l returns the total, over its group, of
+// value index (l % L) >> (log2 L - log2 N) (N <= L); each exchange step
+// halves the number of values a lane carries, so the cost is
+// N - 1 + log2 L - log2 N shuffles instead of N log2 L.
+template <int N, int L = kWave>
 __device__ __forceinline__ float multi_reduce(float (&v)[N], int lane) {
+  static_assert(N <= L, "more values than lanes in a group");
 #pragma unroll
-  for (int s = N / 2, off = 32; s >= 1; s /= 2, off /= 2) {
+  for (int s = N / 2, off = L / 2; s >= 1; s /= 2, off /= 2) {
     const bool upper = (lane & off) != 0;
 #pragma unroll
     for (int i = 0; i < s; ++i) {
@@ -59,7 +61,7 @@ __device__ __forceinline__ float multi_reduce(float (&v)[N], int lane) {
   }
   float r = v[0];
 #pragma unroll
-  for (int off = 32 / N; off >= 1; off /= 2) r += __shfl_xor(r, off, kWave);
+  for (int off = L / 2 / N; off >= 1; off /= 2) r += __shfl_xor(r, off, kWave);
   return r;
 }
 
@@ -159,15 +161,20 @@ __host__ __device__ inline int gemv_window_rows_bt(int64_t K, int BT, int rif = 
 }
 
 // rif: 16-byte loads per lane in flight per row group (fewer rows per wave
-// leave registers for a second workgroup per CU).
-template <int BT, int J, int S, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT>
+// leave registers for a second workgroup per CU).  LPR: lanes per row.  With
+// LPR = 64 a row's blocks are spread over the whole wave; with LPR < 64 a
+// load instruction covers 64 / LPR rows, one per group of LPR lanes, so rows
+// of fewer than 64 blocks fill the wave (a row slot then holds 64 / LPR rows).
+template <int BT, int J, int S, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT, int LPR = kWave>
 struct GemvShape {
-  static constexpr int RU = gemv_rows_per_wave(BT, J, RIF);
+  static constexpr int RPI = kWave / LPR;        // rows per load instruction
+  static constexpr int RU = gemv_rows_per_wave(BT, J, RIF);  // row slots per wave
   static constexpr int SLOTS = kGemvWaves / S;  // row groups per window
-  static constexpr int WIN = SLOTS * RU;        // rows per window
-  static constexpr int NV = RU * BT;            // values reduced per row group
+  static constexpr int WIN = SLOTS * RU * RPI;  // rows per window
+  static constexpr int NV = RU * BT;            // values reduced per lane group
   static constexpr int NP = pow2_ceil_c(NV);
-  static constexpr int SHIFT = 6 - ilog2_c(NP);
+  static constexpr int SHIFT = ilog2_c(LPR) - ilog2_c(NP);
+  static_assert(NP <= LPR, "a lane group holds at most one value per lane");
 };
 constexpr int kMaxNP = 32;  // largest NP over all classes (checked below)
 
@@ -218,21 +225,36 @@ struct RoutedCols {
 // every compute of the workgroup (also across products) so that a K-split
 // exchange never overwrites values a slower wave has yet to read.  WF: the
 // weight format; a Q8_0 block is two loads, so the caller passes half the
-// rows in flight (RIF) for the same bytes in flight.
+// rows in flight (RIF) for the same bytes in flight.  LPR: lanes per row
+// (GemvShape); lane l takes blocks kb0 + l % LPR + LPR j of row slot rows
+// r * 64 / LPR + l / LPR.
 template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT,
-          int WF = kWeightQ4>
+          int WF = kWeightQ4, int LPR = kWave>
 __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& cols, int B, int wl0, int wl1,
                                              unsigned char* smem, SplitScratch* split, int& parity,
                                              int32_t* __restrict__ Iout) {
-  using Sh = GemvShape<BT, J, S, RIF>;
-  constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT;
+  using Sh = GemvShape<BT, J, S, RIF, LPR>;
+  constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT, RPI = Sh::RPI;
   static_assert(NP <= kMaxNP, "split scratch too small");
   static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");
   static_assert(!FOLD || WF == kWeightQ4, "the folded prologue serves Q4 weights");
+  static_assert(LPR == kWave || (S == 1 && !FOLD), "rows shared by lane groups are neither split nor folded");
   constexpr int NL = WF == kWeightQ8 ? 2 : 1;  // 16-byte loads per block and lane
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  int bl = lane, rl = 0;  // lane within its row's lane group; the group's row within a row slot
+  if constexpr (LPR != kWave) {
+    bl = lane & (LPR - 1);
+    rl = lane / LPR;
+  }
+  if constexpr (LPR != kWave || Cols::kWeightsFirst) {
+    // Opaque from here on (routed segments, which a caller runs in loops
+    // beside the other widths' segments): otherwise the compiler hoists the
+    // segment's per-lane 64-bit addresses out of those loops, where they stay
+    // live across the other segments and spill.
+    asm volatile("" : "+v"(bl), "+v"(rl));
+  }
   const int rs = wave / S, kp = wave % S;
-  const int kb0 = kp * kWave * J;
+  const int kb0 = kp * LPR * J;
   const int M = P.M, K = P.K, nb = K >> 5;
   const int64_t row_bytes = WF == kWeightQ8 ? K : K >> 1;
 
@@ -249,10 +271,10 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
   auto load_group = [&](int row0, u32x4 (&w)[RU][J * NL], uint32_t (&dw)[RU][J]) {
 #pragma unroll
     for (int r = 0; r < RU; ++r) {
-      const int rowc = min(row0 + r, row_last);
+      const int rowc = min(row0 + r * RPI + rl, row_last);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int bc = min(kb0 + lane + kWave * j, nb - 1);
+        const int bc = min(kb0 + bl + LPR * j, nb - 1);
 #pragma unroll
         for (int h = 0; h < NL; ++h)
           w[r][j * NL + h] = __builtin_nontemporal_load(
@@ -275,15 +297,15 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
     // their rows up in the routing list (two dependent reads), so there the
     // weight windows are requested before that lookup.
     if constexpr (Cols::kWeightsFirst) {
-      load_group(wl0 * WIN + rs * RU, wA, dA);
-      load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
+      load_group(wl0 * WIN + rs * RU * RPI, wA, dA);
+      load_group((wl0 + 1) * WIN + rs * RU * RPI, wB, dB);
     }
 #pragma unroll
     for (int c = 0; c < BT; ++c)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int cc = min(c, B - 1);
-        const int bc = min(kb0 + lane + kWave * j, nb - 1);
+        const int bc = min(kb0 + bl + LPR * j, nb - 1);
         const Q4Q8_GLOBAL i32x4* src =
             gptr(reinterpret_cast<const i32x4*>(cols.act(cc) + (int64_t)bc * kQK));
         xa[c][j] = src[0];
@@ -291,14 +313,14 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
         xdr[c][j] = gptr(cols.scale(cc))[bc];
       }
     if constexpr (!Cols::kWeightsFirst) {
-      load_group(wl0 * WIN + rs * RU, wA, dA);
-      load_group((wl0 + 1) * WIN + rs * RU, wB, dB);
+      load_group(wl0 * WIN + rs * RU * RPI, wA, dA);
+      load_group((wl0 + 1) * WIN + rs * RU * RPI, wB, dB);
     }
 #pragma unroll
     for (int c = 0; c < BT; ++c)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const bool valid = c < B && kb0 + lane + kWave * j < nb;
+        const bool valid = c < B && kb0 + bl + LPR * j < nb;
         const i32x4 zero = {0, 0, 0, 0};
         xa[c][j] = valid ? xa[c][j] : zero;
         xb[c][j] = valid ? xb[c][j] : zero;
@@ -342,8 +364,8 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
   }
 
   // The column a lane stores is fixed for the segment (value index
-  // lane >> SHIFT of every row group), so its output row is looked up once.
-  const int my_k = lane >> SHIFT, my_c = my_k % BT;
+  // bl >> SHIFT of every row group), so its output row is looked up once.
+  const int my_k = bl >> SHIFT, my_c = my_k % BT;
   float* const my_out = cols.out(min(my_c, B - 1));
 
   // One row group: block sums, scale, multi-row reduction, store (through
@@ -375,16 +397,16 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
           acc[r * BT + c] = __builtin_fmaf(t, xdr[c][j], acc[r * BT + c]);
           if (WRITE_I) {
             const int I = Fb - kMagicBits;
-            const int b = kb0 + lane + kWave * j;
-            const int row = row0 + r;
+            const int b = kb0 + bl + LPR * j;
+            const int row = row0 + r * RPI + rl;
             if (c < B && b < nb && row <= row_last) Iout[((int64_t)c * M + row) * nb + b] = I;
           }
         }
       }
-    const float v = multi_reduce<NP>(acc, lane);
+    const float v = multi_reduce<NP, LPR>(acc, lane);
     const int k = my_k, c = my_c;
-    const bool holder = (lane & ((1 << SHIFT) - 1)) == 0 && k < NV;
-    const int row = row0 + k / BT;
+    const bool holder = (bl & ((1 << SHIFT) - 1)) == 0 && k < NV;
+    const int row = row0 + (k / BT) * RPI + rl;
     if constexpr (S == 1) {
       if (holder && c < B && row <= row_last) gptr_w(my_out)[row] = v;
     } else {
@@ -403,7 +425,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
   // Ping-pong over two register buffers: while one window is computed the
   // other is in flight; a buffer is refilled right after it is consumed.
   for (int wi = wl0; wi < wl1; wi += 2) {
-    const int r0 = wi * WIN + rs * RU;
+    const int r0 = wi * WIN + rs * RU * RPI;
     compute_group(r0, wA, dA);
     load_group(r0 + 2 * WIN, wA, dA);
     if (wi + 1 >= wl1) break;

@@ -164,8 +164,26 @@ __host__ __device__ constexpr int64_t moe_fused_route_ints(int64_t E, int64_t n)
   return 5 * (E + 1) + E + 2 * n + kGemvThreads / 64 + 2;
 }
 
+// Blocking of a column width BT in a K band: J blocks per lane, K split over
+// S waves, LPR lanes per row (GemvShape).  Rows of up to 48 blocks (the 1536
+// band, e.g. K = 1408: 44 blocks) take 16 lanes per row and 3 blocks per lane
+// for up to four columns, so a load instruction covers four rows and 44 of
+// its 48 block slots carry data, where a row per instruction keeps 20 of 64
+// lanes idle; eight columns would need 3 x 8 activation blocks per lane and
+// keep a row per instruction.
+struct MoeClass {
+  int J, S, LPR;
+};
+__host__ __device__ constexpr MoeClass moe_class(int band, int BT) {
+  if (band == 1536 && BT <= 4) return {3, 1, 16};
+  const GemvClass c = gemv_class_of(band == 1536 ? 2048 : band, BT);
+  return {c.J, c.S, kWave};
+}
+
 // 16-byte weight loads each lane keeps in flight per row group, per column
-// width (1, 2, 4, 8 routed pairs per pass) and K band.  One kernel instance
+// width (1, 2, 4, 8 routed pairs per pass) and K band.  The 1536 band keeps
+// two row slots (8 rows, 6 loads per lane) at one and two columns and two
+// (12 loads) at four: 32-row windows like the 2048 band's.  One kernel instance
 // holds the segments of all four widths, so its register allocation is the
 // largest of theirs.  The 2048 band takes 8 / 8 / 16 / 8, which fits two
 // workgroups per CU (245 VGPRs) and measured fastest: 4.1 TB/s for the MoE
@@ -174,6 +192,7 @@ __host__ __device__ constexpr int64_t moe_fused_route_ints(int64_t E, int64_t n)
 // 8 / 8 / 16 / 16 at one workgroup per CU, and the 16384 band keeps width 4
 // at 8 so that its instance stays free of scratch spills.
 __host__ __device__ constexpr int moe_rif(int BT, int band) {
+  if (band == 1536) return moe_class(band, BT).LPR != kWave ? (BT <= 2 ? 6 : 12) : moe_rif(BT, 2048);
   if (band <= 2048) return BT <= 2 ? 8 : BT <= 4 ? 16 : 8;
   return BT <= 2 ? 8 : BT <= 4 ? (band >= 16384 ? 8 : 16) : 16;
 }
@@ -181,23 +200,38 @@ __host__ __device__ constexpr int moe_rif(int BT, int band) {
 // Workgroups per CU the streaming instance of a K band is built for.
 __host__ __device__ constexpr int moe_waves_per_simd(int band) { return band <= 2048 ? 2 : 1; }
 
-// The power-of-two band of K whose blocking classes an instance compiles:
-// 2048, 4096, 8192 or 16384 (0: K too large).  Within a band every column
-// width has one class.
+// The band of K whose blocking classes an instance compiles: 1536, 2048,
+// 4096, 8192 or 16384 (0: K too large).  Within a band every column width
+// has one class.
 static int moe_band(int64_t K) {
-  return K <= 2048 ? 2048 : K <= 4096 ? 4096 : K <= 8192 ? 8192 : K <= 16384 ? 16384 : 0;
+  return K <= 1536 ? 1536 : K <= 2048 ? 2048 : K <= 4096 ? 4096 : K <= 8192 ? 8192 : K <= 16384 ? 16384 : 0;
+}
+
+template <int BAND, int BT>
+constexpr int moe_win() {
+  constexpr MoeClass c = moe_class(BAND, BT);
+  return GemvShape<BT, c.J, c.S, moe_rif(BT, BAND), c.LPR>::WIN;
 }
 
 // Rows per window of the routed launch: the largest streaming window over the
 // column widths; every width's window divides it (all are powers of two).
+template <int BAND>
+constexpr int moe_window_rows_c() {
+  constexpr int w1 = moe_win<BAND, 1>(), w2 = moe_win<BAND, 2>(), w4 = moe_win<BAND, 4>(), w8 = moe_win<BAND, 8>();
+  constexpr int u = w1 > w2 ? w1 : w2, v = w4 > w8 ? w4 : w8;
+  constexpr int m = u > v ? u : v;
+  static_assert(m % w1 == 0 && m % w2 == 0 && m % w4 == 0 && m % w8 == 0, "windows must divide the unit");
+  return m;
+}
 static int moe_window_rows(int64_t K) {
-  const int band = moe_band(K);
-  int u = 1;
-  for (int bt = 1; bt <= 8; bt *= 2) {
-    const int w = gemv_window_rows_bt(band, bt, moe_rif(bt, band));
-    if (w > u) u = w;
+  switch (moe_band(K)) {
+    case 1536: return moe_window_rows_c<1536>();
+    case 2048: return moe_window_rows_c<2048>();
+    case 4096: return moe_window_rows_c<4096>();
+    case 8192: return moe_window_rows_c<8192>();
+    case 16384: return moe_window_rows_c<16384>();
+    default: return 1;
   }
-  return u;
 }
 
 // Static cost-balanced schedule: window j of selected expert i starts at
@@ -301,12 +335,12 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
       cols.top_k = top_k;
       cols.per_slot = per_slot;
       auto run = [&]<int BT>() {
-        constexpr GemvClass cls = gemv_class_of(KMAX, BT);
+        constexpr MoeClass cls = moe_class(KMAX, BT);
         static_assert(cls.J != 0, "unsupported band");
         constexpr int RIF = moe_rif(BT, KMAX);
-        const int f = unit / GemvShape<BT, cls.J, cls.S, RIF>::WIN;
-        gemv_segment<BT, cls.J, cls.S, false, false, RoutedCols, RIF>(P, cols, nc, wl0 * f, wl1 * f, nullptr,
-                                                                      &split, parity, nullptr);
+        const int f = unit / GemvShape<BT, cls.J, cls.S, RIF, cls.LPR>::WIN;
+        gemv_segment<BT, cls.J, cls.S, false, false, RoutedCols, RIF, kWeightQ4, cls.LPR>(
+            P, cols, nc, wl0 * f, wl1 * f, nullptr, &split, parity, nullptr);
       };
       if (nc == 1)
         run.template operator()<1>();
@@ -418,6 +452,7 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
       go(k_ws);
   };
   switch (moe_band(K)) {
+    case 1536: band(moe_stream_kernel<1536, true>, moe_stream_kernel<1536, false>); break;
     case 2048: band(moe_stream_kernel<2048, true>, moe_stream_kernel<2048, false>); break;
     case 4096: band(moe_stream_kernel<4096, true>, moe_stream_kernel<4096, false>); break;
     case 8192: band(moe_stream_kernel<8192, true>, moe_stream_kernel<8192, false>); break;

@@ -128,6 +128,23 @@ def test_expert_loads_and_k_bands(E, M, K, T, top_k, S):
     _check_rows(y, y_o, ids, E)
 
 
+@pytest.mark.parametrize("mode", ["broadcast", "per_slot"])
+@pytest.mark.parametrize("K", [1408, 1440, 1536, 1024, 96])
+def test_short_rows_every_width(mode, K):
+    """Rows of at most 48 blocks (K <= 1536) take 16 lanes per row and 3
+    blocks per lane for one to four routed pairs per pass, a row per load
+    instruction for eight: experts with 1, 2, 3 and 6 pairs (widths 1, 2, 4,
+    8), 77 rows (a partial last window), block counts below and at 48."""
+    E, M, T, top_k = 4, 77, 6, 2
+    S = 1 if mode == "broadcast" else top_k
+    _, qs, d = _experts(38, E, M, K)
+    xq, xd = _acts(38, T, S, K)
+    ids = np.array([[3, 2], [3, 2], [3, 2], [3, 1], [3, 1], [3, 0]], np.int32)
+    y = _gpu(qs, d, xq, xd, ids)
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(y, y_o, ids, E)
+
+
 def test_many_bad_ids():
     """Half of the pairs carry ids outside [0, E): their rows are NaN, the
     others are computed as usual."""

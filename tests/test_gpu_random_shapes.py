@@ -79,7 +79,9 @@ def test_random_single_products(q8_0):
 def test_random_groups(case):
     """A group of random products at one random width, each product's format
     drawn at random: outputs match the oracle and equal the single calls bit
-    for bit."""
+    for bit, each single call on the group's route (a group of 5..8 columns
+    that mixes formats or shapes runs the lane-per-block kernel, where a
+    single call could take the multi-column one)."""
     rng = np.random.default_rng(7200 + case)
     B = int(rng.integers(1, 9)) if case < 3 else int(rng.integers(9, 48))
     dev = torch.device("cuda:0")
@@ -100,8 +102,11 @@ def test_random_groups(case):
         w = p["qw"] if q8_0 else p["qs"]
         tag = f"case {case} B={B} M={w.shape[0]} q8_0={q8_0}"
         assert_close(p["y"].cpu().numpy(), y_o, tag)
+        lanes = B <= 8 and not grp.plan.mfma_columns
+        q.q4q8_set_path(q.PATH_GEMV_LANES if lanes else q.PATH_AUTO)
         single = (q.mul_mat_q8_0_q8 if q8_0 else q.mul_mat_q4q8)(w, p["d"], p["xq"], p["xd"])
         torch.cuda.synchronize()
+        q.q4q8_set_path(q.PATH_AUTO)
         assert np.array_equal(single.cpu().numpy().view(np.uint32), p["y"].cpu().numpy().view(np.uint32)), tag
 
 
