@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kWideThreads) void rmsnorm_q8_wide_kernel(
   int8_t* xqr = xq + row * (int64_t)K;
   float* xdr = xd + row * nb;
   int32_t* xsr = xs ? xs + row * nb : nullptr;
+  if (K <= kWideMaxK && tid / kWave >= wide_active_waves(K)) return;  // holds no lane of the row
   if (K <= kQuadMaxK) {
     wide_q8_row_lanes<4>(xr, g, K, eps, no_norm != 0, xqr, xdr, xsr, groups, tid, ar);
     return;
@@ -332,6 +333,7 @@ __global__ __launch_bounds__(kWideThreads) void group_prologue_wide_kernel(const
   const float* xr = J.x + (int64_t)c * K;
   int8_t* xq = J.xq + (int64_t)c * K;
   float* xd = J.xd + (int64_t)c * nb;
+  if (K <= kWideMaxK && tid / kWave >= wide_active_waves(K)) return;  // holds no lane of the row
   if (K <= kQuadMaxK) {
     wide_q8_row_lanes<4>(xr, J.g, K, J.eps, J.raw != 0, xq, xd, nullptr, groups, tid);
     return;

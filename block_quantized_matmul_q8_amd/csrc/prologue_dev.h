@@ -307,6 +307,16 @@ constexpr int kQuadMaxK = kQK * kWideThreads / 4;  // 8192: four lanes per block
 constexpr int kPairMaxK = kQK * kWideThreads / 2;  // 16384: two lanes per block
 constexpr int kWideMaxK = kQK * kWideThreads;      // 32768: one lane per block
 
+// Waves of the 1024-thread workgroup that hold lanes of a row of K (K <=
+// kWideMaxK): 4, 2 or 1 lanes per block by the row forms below.  The others
+// have no part in the row; the kernels let them leave the workgroup before
+// any barrier (a barrier waits for the waves that have not ended only).
+__host__ __device__ constexpr int wide_active_waves(int K) {
+  const int nb = K / kQK;
+  const int lanes = nb * (K <= kQuadMaxK ? 4 : K <= kPairMaxK ? 2 : 1);
+  return lanes <= kWave ? 1 : (lanes + kWave - 1) / kWave;
+}
+
 // DPP within each group of L lanes (L = 2 or 4; groups aligned in quads):
 // lane_from_prev hands lane r the value of lane r - 1 (quad_perm [0,0,1,2]
 // for L = 4, [0,0,2,2] for L = 2); group_max and group_isum combine the
@@ -336,13 +346,16 @@ __device__ __forceinline__ float quad_max(float m) { return group_max<4>(m); }
 // wave's sum, one barrier, and every thread finishes the tree over the 16
 // wave slots (slots past the row's padded block count hold +0, and adding +0
 // to a non-negative sum is exact, so the fixed four-level tree gives the bits
-// of the tree over next_pow2(nb) blocks).
-__device__ __forceinline__ float wide_rms_scale(float wave_sum, int K, float eps, float* groups, int tid) {
+// of the tree over next_pow2(nb) blocks).  Only the first n_waves waves hold
+// lanes of the row (wide_active_waves); the others have left the workgroup,
+// and their slots are taken as +0.
+__device__ __forceinline__ float wide_rms_scale(float wave_sum, int K, float eps, float* groups, int tid,
+                                                int n_waves) {
   if ((tid & (kWave - 1)) == 0) groups[tid / kWave] = wave_sum;
   __syncthreads();
   float t[kWideWaves];
 #pragma unroll
-  for (int i = 0; i < kWideWaves; ++i) t[i] = groups[i];
+  for (int i = 0; i < kWideWaves; ++i) t[i] = i < n_waves ? groups[i] : 0.0f;
 #pragma unroll
   for (int h = kWideWaves / 2; h >= 1; h /= 2)
 #pragma unroll
@@ -407,7 +420,7 @@ __device__ __forceinline__ void wide_q8_row_lanes(const float* __restrict__ xr, 
       const float prev = lane_from_prev<L>(t);
       cin = r == k + 1 ? prev : cin;
     }
-    s = wide_rms_scale(wave_tree_sum(r == L - 1 ? t : 0.0f), K, eps, groups, tid);
+    s = wide_rms_scale(wave_tree_sum(r == L - 1 ? t : 0.0f), K, eps, groups, tid, wide_active_waves(K));
   }
   float v[E];
 #pragma unroll
@@ -476,7 +489,7 @@ __device__ __forceinline__ void wide_q8_row_single(const float* __restrict__ xr,
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(xv[j], xv[j]));
-    s = wide_rms_scale(wave_tree_sum(acc), K, eps, groups, tid);
+    s = wide_rms_scale(wave_tree_sum(acc), K, eps, groups, tid, wide_active_waves(K));
   }
   if (on) {
     float v[kQK];
