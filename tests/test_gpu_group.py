@@ -408,3 +408,49 @@ def test_group_prologue_planes_bit_exact(B, K, raw):
     y_o, _ = oracle.mul_mat(qs, d, xq_o, xd_o, nthreads=16, want_y64=False)
     assert np.isfinite(y.cpu().numpy()).all()
     assert_close(y.cpu().numpy(), y_o, f"B={B} K={K}")
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_group_prologue_packed_rows_mixed(B):
+    """A decode group's prologue pass over fp32 inputs of different K (one
+    32-block to 14336), raw rows beside normalised ones: every input's planes,
+    read out of the workspace, equal the oracle's bit for bit, and the outputs
+    the oracle's product."""
+    print(f"[packed prologue] B={B}", flush=True)
+    ks = [2048, 2048, 1024, 96, 8192, 4096, 4096, 14336, 32, 2048]
+    M = 16
+    probs, refs, layout = [], [], []
+    off = 0
+    for i, K in enumerate(ks):
+        raw = i % 3 == 1
+        x = workloads.activation(49, B, i, B, K) * np.float32(1.3)
+        if B >= 3:
+            x[1] = 0.0
+        g = workloads.norm_weight(49, 0, i, K)
+        qs, d = _weights(49, 0, i, M, K)
+        y = torch.full((B, M), float("nan"), device="cuda:0")
+        p = {"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": to_dev(x)}
+        if raw:
+            p["flags"] = q.Q8_NO_NORM
+        else:
+            p.update(g=to_dev(g), eps=workloads.RMS_EPS)
+        probs.append(p)
+        xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, None if raw else g, workloads.RMS_EPS, no_norm=raw)
+        refs.append((qs, d, xq_o, xd_o))
+        xd_off = off + (B * K + 15) // 16 * 16
+        layout.append((off, xd_off, K))
+        off = xd_off + (B * (K // 32) * 4 + 15) // 16 * 16
+    grp = q.Group(probs, B=B)
+    assert grp.plan.n_prologue == len(ks)
+    grp.workspace.fill_(0xA5)
+    grp()
+    torch.cuda.synchronize()
+    ws = grp.workspace.cpu().numpy()
+    for i, ((qs, d, xq_o, xd_o), (xo, xdo, K), p) in enumerate(zip(refs, layout, probs)):
+        xq = ws[xo:xo + B * K].view(np.int8).reshape(B, K)
+        xd = ws[xdo:xdo + B * (K // 32) * 4].view(np.uint32).reshape(B, K // 32)
+        assert np.array_equal(xq, xq_o), f"input {i} K={K}"
+        assert np.array_equal(xd, xd_o.view(np.uint32)), f"input {i} K={K}"
+        y_o, _ = oracle.mul_mat(qs, d, xq_o, xd_o, nthreads=16, want_y64=False)
+        assert np.isfinite(p["y"].cpu().numpy()).all()
+        assert_close(p["y"].cpu().numpy(), y_o, f"input {i} K={K}")
