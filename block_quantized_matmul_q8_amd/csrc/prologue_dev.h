@@ -420,7 +420,7 @@ __device__ __forceinline__ void wide_q8_row_lanes(const float* __restrict__ xr, 
       const float prev = lane_from_prev<L>(t);
       cin = r == k + 1 ? prev : cin;
     }
-    s = wide_rms_scale(wave_tree_sum(r == L - 1 ? t : 0.0f), K, eps, groups, tid, wide_active_waves(K));
+    s = wide_rms_scale(wave_tree_sum(r == L - 1 ? t : 0.0f), K, eps, groups, tid, (nb * L + kWave - 1) / kWave);
   }
   float v[E];
 #pragma unroll
@@ -489,7 +489,7 @@ __device__ __forceinline__ void wide_q8_row_single(const float* __restrict__ xr,
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < kQK; ++j) acc = __fadd_rn(acc, __fmul_rn(xv[j], xv[j]));
-    s = wide_rms_scale(wave_tree_sum(acc), K, eps, groups, tid, wide_active_waves(K));
+    s = wide_rms_scale(wave_tree_sum(acc), K, eps, groups, tid, (nb + kWave - 1) / kWave);
   }
   if (on) {
     float v[kQK];
