@@ -8,7 +8,10 @@
 // fp32 is F = 1.5 * 2^23 + I exactly (|I| < 2^22), and the per-block rescale
 // is two fp32 fmas per output element: t = fma(F, d_w, -1.5 * 2^23 * d_w) =
 // fl(I * d_w) (the product 1.5 * 2^23 * d_w is exact for an fp16 d_w), then
-// acc = fma(t, d_x, acc).
+// acc = fma(t, d_x, acc).  Q4 weights enter the MFMA as the bytes 16 (q - 8)
+// (two bit operations per four codes, no add), so F = 1.5 * 2^23 + 16 I
+// (|16 I| < 2^22 still) and the fmas take d_w / 16 and -1.5 * 2^23 * d_w / 16,
+// both exact: t keeps the bits of fl(I * d_w).
 //
 // What bounds it on gfx950 (measured): a 32x32x32 i8 MFMA occupies its SIMD
 // for about 33.5 cycles, and an fp32 fma issues every ~2.35 cycles when two
@@ -38,7 +41,7 @@
 // with padded block planes spreads the stage writes over the banks.  Two LDS
 // stage buffers: while stage s is computed, stage s + 1 travels from global
 // memory into registers and then into the other buffer (Q4 codes unpacked to
-// signed int8 once, shared by all 128 tokens), so each stage costs one
+// 16 (q - 8) once, shared by all 128 tokens), so each stage costs one
 // barrier.  Global loads are shaped for few cache lines per instruction
 // (whole 128-byte lines of a token or row; the 4 scales of a token or row of
 // a stage in one load) and take no vector instructions in a full stage (a
@@ -72,10 +75,11 @@ constexpr int kKB = 4;              // 32-blocks per stage
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ uint32_t nib_to_s8(uint32_t n) {
-  // bytes in [0,15] -> signed bytes n - 8 (no carries cross byte lanes)
-  return (n + 0x78787878u) ^ 0x80808080u;
-}
+// Four Q4 codes held in the high nibbles of v's bytes -> the signed bytes
+// 16 (q - 8): the low nibbles cleared and each byte's top bit flipped (no
+// carries cross byte lanes).  The MFMA then sums 16 I, which the rescale
+// takes with d_w / 16 (both exact: powers of two).
+__device__ __forceinline__ uint32_t nib_hi_to_s8x16(uint32_t v) { return (v ^ 0x80808080u) & 0xF0F0F0F0u; }
 
 // Block planes are padded (activation codes by 32 bytes, weight codes by
 // 64), so that the stage writes of 16 consecutive lanes -- 2 tokens x 4
@@ -227,15 +231,15 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
         *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, hh)) = f.w[i];
       }
     } else {
-      const uint32_t m4 = 0x0F0F0F0Fu;
 #pragma unroll
       for (int i = 0; i < kNW; ++i) {
         const int c = 256 * i + tid;
         const int r = c / 4, blk = c % 4;
         const u32x4 qv = f.w[i];
-        const u32x4 lo = {nib_to_s8(qv.x & m4), nib_to_s8(qv.y & m4), nib_to_s8(qv.z & m4), nib_to_s8(qv.w & m4)};
-        const u32x4 hi = {nib_to_s8((qv.x >> 4) & m4), nib_to_s8((qv.y >> 4) & m4), nib_to_s8((qv.z >> 4) & m4),
-                          nib_to_s8((qv.w >> 4) & m4)};
+        const u32x4 lo = {nib_hi_to_s8x16(qv.x << 4), nib_hi_to_s8x16(qv.y << 4), nib_hi_to_s8x16(qv.z << 4),
+                          nib_hi_to_s8x16(qv.w << 4)};
+        const u32x4 hi = {nib_hi_to_s8x16(qv.x), nib_hi_to_s8x16(qv.y), nib_hi_to_s8x16(qv.z),
+                          nib_hi_to_s8x16(qv.w)};
         *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, 0)) = lo;
         *reinterpret_cast<u32x4*>(&sg.w[blk].v[r / 32][0][0][0] + piece_off(r, 1)) = hi;
       }
@@ -251,8 +255,10 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
     } else {
       const uint32_t b0 = packed ? f.sw.x & 0xFFFFu : f.sx.x, b1 = packed ? f.sw.x >> 16 : f.sx.y;
       const uint32_t b2 = packed ? f.sw.y & 0xFFFFu : f.sx.z, b3 = packed ? f.sw.y >> 16 : f.sx.w;
-      const float w0 = f16_bits_to_f32((uint16_t)b0), w1 = f16_bits_to_f32((uint16_t)b1);
-      const float w2 = f16_bits_to_f32((uint16_t)b2), w3 = f16_bits_to_f32((uint16_t)b3);
+      // Q4: the MFMA sums 16 I, so the scale is taken as d_w / 16 (exact)
+      constexpr float ws = WF == kWeightQ8 ? 1.0f : 0.0625f;
+      const float w0 = ws * f16_bits_to_f32((uint16_t)b0), w1 = ws * f16_bits_to_f32((uint16_t)b1);
+      const float w2 = ws * f16_bits_to_f32((uint16_t)b2), w3 = ws * f16_bits_to_f32((uint16_t)b3);
       sg.dwc[0][sr] = f32x2{w0, -kMagic * w0};
       sg.dwc[1][sr] = f32x2{w1, -kMagic * w1};
       sg.dwc[2][sr] = f32x2{w2, -kMagic * w2};
@@ -333,7 +339,9 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
             for (int r = 0; r < 16; ++r) {
               const int n = n0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
               const int m = m0 + jt * 32 + l32;
-              if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = Di[r] - kMagicBits;
+              // Q4 operands carry 16 (q - 8): the exact multiple of 16 is shifted back
+              const int I = WF == kWeightQ8 ? Di[r] - kMagicBits : (Di[r] - kMagicBits) >> 4;
+              if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = I;
             }
           }
           // Two passes, so that no fma waits on the one just before it
