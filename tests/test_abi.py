@@ -449,6 +449,26 @@ def test_group_build_multicolumn_random_groups(seed):
     assert max(costs) <= -(-sum(costs) // plan.mfma_grid) + kmax
 
 
+@pytest.mark.parametrize("shapes,B", [([(1, 1024)], 8), ([(64, 1024)], 5), ([(65, 4096), (3, 1024)], 6),
+                                      ([(130000, 1024)], 8), ([(640, 16384), (64, 1024)] * 3, 7)])
+def test_group_build_multicolumn_edges(shapes, B):
+    """Packing at the edges: one window (one workgroup), fewer windows than
+    resident workgroups (one window each), ragged last windows, and a single
+    product of many windows (equal bins)."""
+    descs = [_desc(M=M, K=K, qs=4096 * (i + 1)) for i, (M, K) in enumerate(shapes)]
+    image, plan = _build(descs, B)
+    bins = _mfma_bins(image, plan)
+    n_win = sum((M + 63) // 64 for M, _ in shapes)
+    assert plan.n_windows == n_win and plan.mfma_grid == min(n_win, plan.mfma_grid)
+    listed = sorted((qs, w) for b in bins for (qs, w, _) in b)
+    assert listed == sorted((4096 * (i + 1), w) for i, (M, _) in enumerate(shapes) for w in range((M + 63) // 64))
+    costs = [sum(K // 32 for (_, _, K) in b) for b in bins]
+    if n_win <= plan.mfma_grid:
+        # as many workgroups as windows: no bin above the costliest window
+        assert max(costs) == max(K for _, K in shapes) // 32
+    assert max(costs) <= -(-sum(costs) // plan.mfma_grid) + max(K for _, K in shapes) // 32
+
+
 def test_group_launch_rejects_foreign_plans():
     L = q.lib()
     plan = q.GroupPlan()
