@@ -642,8 +642,10 @@ hipError_t launch_gemv_mfma(const GemvProblem& p, const GemvProblem* table, cons
 // totals, the one with more of the costlier windows (those are the hard ones
 // to place late).  Combinations are searched costliest class first, with a
 // node budget past which the rest of a search takes the largest counts that
-// fit.  Within a cost class, windows go in record order, so a bin holds few
-// runs.  The last bin takes whatever is left.
+// fit; past 32 distinct costs (the search recurses once per cost) every bin
+// takes the largest counts that fit, costliest first.  Within a cost class,
+// windows go in record order, so a bin holds few runs.  The last bin takes
+// whatever is left.
 void gemv_mfma_pack(const std::vector<int64_t>& n_win, const std::vector<int64_t>& cost, int64_t groups,
                     std::vector<MfRun>& runs, std::vector<int64_t>& bounds) {
   struct Seg {
@@ -694,6 +696,7 @@ void gemv_mfma_pack(const std::vector<int64_t>& n_win, const std::vector<int64_t
     }
   };
   constexpr int64_t kNodeBudget = 1 << 14;
+  constexpr int kMaxSearchClasses = 32;
   std::vector<int64_t> x(m), best(m);
   for (int64_t g = 0; g < groups; ++g) {
     if (g + 1 == groups) {
@@ -717,7 +720,15 @@ void gemv_mfma_pack(const std::vector<int64_t>& n_win, const std::vector<int64_t
         }
         x[i] = 0;
       };
-      search(search, 0, room, 0);
+      if (m <= kMaxSearchClasses) {
+        search(search, 0, room, 0);
+      } else {
+        int64_t rem = room;
+        for (int i = 0; i < m; ++i) {
+          best[i] = std::min(cls[i].avail, rem > 0 ? rem / cls[i].c : 0);
+          rem -= best[i] * cls[i].c;
+        }
+      }
       for (int i = 0; i < m; ++i) take(cls[i], best[i]);
     }
     bounds.push_back(n_placed);

@@ -469,6 +469,16 @@ def test_group_build_multicolumn_edges(shapes, B):
     assert max(costs) <= -(-sum(costs) // plan.mfma_grid) + max(K for _, K in shapes) // 32
 
 
+def test_group_build_multicolumn_many_distinct_k():
+    """More distinct window costs than the packer searches (300 products, each
+    its own K): the bins are filled greedily, every window still listed once."""
+    descs = [_desc(M=64 + 64 * (i % 5), K=1024 + 256 * i, qs=4096 * (i + 1)) for i in range(300)]
+    image, plan = _build(descs, 8)
+    bins = _mfma_bins(image, plan)
+    listed = sorted((qs, w) for b in bins for (qs, w, _) in b)
+    assert listed == sorted((d.qs, w) for d in descs for w in range((d.M + 63) // 64))
+
+
 def test_group_launch_rejects_foreign_plans():
     L = q.lib()
     plan = q.GroupPlan()
