@@ -30,16 +30,24 @@ size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
   return (words * sizeof(int32_t) + 15) & ~(size_t)15;
 }
 
-// Relative cost of streaming one window of an expert with c routed pairs:
-// the pairs are taken up to 8 per pass, and a pass of width 1 / 2 / 4 / 8
-// costs about 16 / 16 / 21 / 33 units (the routed kernel's measured time per
-// window at each width, every expert of a 64-expert layer taking that width).
-constexpr int kMoeMaxWindowCost = 33;
-__host__ __device__ inline int moe_window_cost(int c) {
+// Relative cost of streaming one window of an expert with c routed pairs in
+// K band `band`: the pairs are taken up to 8 per pass, and a pass of width
+// 1 / 2 / 4 / 8 costs (the routed kernel's time per call with every expert of
+// a 64-expert layer at that width, less a few microseconds of fixed cost):
+//   1536 band (16 lanes per row up to width 4): 16 / 17 / 20 / 43 units
+//     (21.8 / 22.5 / 25.8 / 50 us per call, K = 1408, 2048 rows);
+//   2048 band: 16 / 16 / 18 / 28 (37.3 / 38.3 / 41.5 / 62.3 us, K = 2048,
+//     2816 rows);
+//   wider bands: 16 / 16 / 21 / 33 (an earlier calibration of the 2048 band).
+constexpr int kMoeMaxWindowCost = 43;
+__host__ __device__ inline int moe_window_cost(int c, int band) {
+  const int w2 = band == 1536 ? 17 : 16;
+  const int w4 = band == 1536 ? 20 : band == 2048 ? 18 : 21;
+  const int w8 = band == 1536 ? 43 : band == 2048 ? 28 : 33;
   int cost = 0;
   for (int c0 = 0; c0 < c; c0 += 8) {
     const int nc = min(8, c - c0);
-    cost += nc <= 2 ? 16 : nc <= 4 ? 21 : kMoeMaxWindowCost;
+    cost += nc == 1 ? 16 : nc == 2 ? w2 : nc <= 4 ? w4 : w8;
   }
   return cost;
 }
@@ -91,7 +99,7 @@ __device__ void block_exclusive_scan(int* v, int count, int* wave_tot, int tid) 
 // wave_tot NT / 64, n_bad one; the outputs (offsets .. ctl, the workspace
 // layout above) may live in LDS or global memory.
 template <int NT>
-__device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n, int E, int n_win, int* cnt,
+__device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n, int E, int n_win, int band, int* cnt,
                                           int* sidx, int* cpre, int* wave_tot, int* n_bad, int32_t* offsets,
                                           int32_t* list, int32_t* rank, int32_t* sel, int32_t* costp,
                                           int32_t* ctl, bool nan_rows, int M, float* __restrict__ y) {
@@ -110,7 +118,7 @@ __device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n
   for (int e = tid; e < E; e += NT) {
     const int c = cnt[e];
     sidx[e] = c > 0 ? 1 : 0;
-    cpre[e] = c > 0 ? n_win * moe_window_cost(c) : 0;
+    cpre[e] = c > 0 ? n_win * moe_window_cost(c, band) : 0;
   }
   __syncthreads();
   block_exclusive_scan<NT>(cnt, E, wave_tot, tid);
@@ -146,12 +154,12 @@ __device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n
 // The routing as its own launch (one workgroup), results in the workspace.
 // LDS: counts, selected indices, cost prefix (E + 1 each) | wave totals.
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int n_win, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ids, int n, int E, int n_win, int band, int32_t* __restrict__ offsets,
     int32_t* __restrict__ list, int32_t* __restrict__ rank, int32_t* __restrict__ sel,
     int32_t* __restrict__ costp, int32_t* __restrict__ ctl, int M, float* __restrict__ y) {
   extern __shared__ int lds[];
   __shared__ int n_bad;
-  moe_route<kRouteThreads>(ids, n, E, n_win, lds, lds + E + 1, lds + 2 * (E + 1), lds + 3 * (E + 1), &n_bad,
+  moe_route<kRouteThreads>(ids, n, E, n_win, band, lds, lds + E + 1, lds + 2 * (E + 1), lds + 3 * (E + 1), &n_bad,
                            offsets, list, rank, sel, costp, ctl, true, M, y);
 }
 
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
     int* wave_tot = l_rank + n;
     int* n_bad = wave_tot + kGemvThreads / 64;
     int* l_ctl = n_bad + 1;
-    moe_route<kGemvThreads>(ids, n, E, n_win, cnt, sidx, cpre, wave_tot, n_bad, l_off, l_list, l_rank, l_sel,
+    moe_route<kGemvThreads>(ids, n, E, n_win, KMAX, cnt, sidx, cpre, wave_tot, n_bad, l_off, l_list, l_rank, l_sel,
                             l_costp, l_ctl, blockIdx.x == 0, M, y);
     __syncthreads();
     offsets = l_off;
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
   for (; i >= 0 && i < n_sel && costp[i] < c_hi; ++i) {
     const int e = sel[i];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-    const int64_t wc = moe_window_cost(cnt);
+    const int64_t wc = moe_window_cost(cnt, KMAX);
     // windows of this expert whose start cost lies in [c_lo, c_hi)
     const int64_t r_lo = c_lo - costp[i], r_hi = c_hi - costp[i];
     const int wl0 = r_lo <= 0 ? 0 : (int)((r_lo + wc - 1) / wc);
@@ -433,7 +441,7 @@ hipError_t launch_moe(const uint8_t* qs, const uint16_t* d, int64_t E, int64_t M
     const size_t route_lds = (3 * ((size_t)E + 1) + kRouteThreads / 64) * sizeof(int);
     note_launch((const void*)moe_route_kernel);
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), route_lds, s, ids, n, (int)E, (int)n_win,
-                       offsets, list, rank, sel, costp, ctl, (int)M, y);
+                       moe_band(K), offsets, list, rank, sel, costp, ctl, (int)M, y);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
