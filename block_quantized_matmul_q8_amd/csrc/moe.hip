@@ -39,14 +39,18 @@ size_t moe_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
 //   2048 band: 16 / 16 / 18 / 28 (37.3 / 38.3 / 41.5 / 62.3 us, K = 2048,
 //     2816 rows);
 //   wider bands: 16 / 16 / 21 / 33 (an earlier calibration of the 2048 band).
+// In the 1536 band two passes of width 4 cost less than one of width 8 (40
+// against 43 units, and 5 pairs as 4 + 1 cost 36), so its passes take at
+// most 4 pairs and the instance holds no width-8 segment.
 constexpr int kMoeMaxWindowCost = 43;
+__host__ __device__ constexpr int moe_max_pass(int band) { return band == 1536 ? 4 : 8; }
 __host__ __device__ inline int moe_window_cost(int c, int band) {
   const int w2 = band == 1536 ? 17 : 16;
   const int w4 = band == 1536 ? 20 : band == 2048 ? 18 : 21;
   const int w8 = band == 1536 ? 43 : band == 2048 ? 28 : 33;
   int cost = 0;
-  for (int c0 = 0; c0 < c; c0 += 8) {
-    const int nc = min(8, c - c0);
+  for (int c0 = 0; c0 < c; c0 += moe_max_pass(band)) {
+    const int nc = min(moe_max_pass(band), c - c0);
     cost += nc == 1 ? 16 : nc == 2 ? w2 : nc <= 4 ? w4 : w8;
   }
   return cost;
@@ -329,8 +333,8 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
     P.mode = kModeQ8;
     P.win_begin = 0;
     P.n_win = n_win;
-    for (int c0 = 0; c0 < cnt; c0 += 8) {
-      const int nc = min(8, cnt - c0);
+    for (int c0 = 0; c0 < cnt; c0 += moe_max_pass(KMAX)) {
+      const int nc = min(moe_max_pass(KMAX), cnt - c0);
       RoutedCols cols;
       cols.xq = xq;
       cols.xd = xd;
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
         run.template operator()<1>();
       else if (nc == 2)
         run.template operator()<2>();
-      else if (nc <= 4)
+      else if (KMAX == 1536 || nc <= 4)
         run.template operator()<4>();
       else
         run.template operator()<8>();

@@ -132,9 +132,9 @@ def test_expert_loads_and_k_bands(E, M, K, T, top_k, S):
 @pytest.mark.parametrize("K", [1408, 1440, 1536, 1024, 96])
 def test_short_rows_every_width(mode, K):
     """Rows of at most 48 blocks (K <= 1536) take 16 lanes per row and 3
-    blocks per lane for one to four routed pairs per pass, a row per load
-    instruction for eight: experts with 1, 2, 3 and 6 pairs (widths 1, 2, 4,
-    8), 77 rows (a partial last window), block counts below and at 48."""
+    blocks per lane, in passes of at most four routed pairs: experts with 1,
+    2, 3 and 6 pairs (widths 1, 2, 4, then 4 + 2), 77 rows (a partial last
+    window), block counts below and at 48."""
     E, M, T, top_k = 4, 77, 6, 2
     S = 1 if mode == "broadcast" else top_k
     _, qs, d = _experts(38, E, M, K)
