@@ -33,6 +33,7 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--skip-extras]
        python bench.py --kernel-only 10      (launches for rocprofv3 runs)
        python bench.py --gemm-only 10        (prefill GEMM launches for rocprofv3 runs)
        python bench.py --moe-only 10         (routed MoE launches for rocprofv3 runs)
+       python bench.py --moe-widths          (routed call time per pass width, the MoE schedule's window costs)
        python bench.py --q8-0-only 10        (Q8_0 weight launches for rocprofv3 runs)
        python bench.py --decode-8b-only B 10 (Llama-3-8B-shaped decode steps at batch B for rocprofv3 runs)
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR [REQ_DIR]   (traffic summary)
@@ -613,6 +614,41 @@ def moe_weight_copies(dev, n_copies=4):
     return copies
 
 
+def moe_widths(dev):
+    """The measurements behind the routed schedule's window costs: one routed
+    call with every expert of a 64-expert layer at exactly w pairs (token t
+    selects experts 8t .. 8t + 7 mod 64, 8w tokens), for w = 1, 2, 3, 4, 5, 8,
+    in the 1536 band (the down projection's shape, K = 1408, one row per
+    (token, slot)) and the 2048 band (the stacked gate/up shape, 2816 rows,
+    K = 2048, one row per token); GPU time per call from 10 calls captured in
+    a HIP graph and replayed."""
+    import torch
+
+    import block_quantized_matmul_q8_amd as q
+    import workloads as wl
+
+    E = 64
+    for M, K, S in ((2048, 1408, 8), (2816, 2048, 1)):
+        w = wl.weight_device(5, 0, 0, E * M, K, dev)
+        qs, d = q.q4_quantize(w)
+        del w
+        qs, d = qs.view(E, M, K // 2), d.view(E, M, K // 32)
+        times = []
+        for width in (1, 2, 3, 4, 5, 8):
+            T = 8 * width
+            ids = torch.tensor([[(8 * t + j) % E for j in range(8)] for t in range(T)], dtype=torch.int32,
+                               device=dev)
+            x = wl.activation_device(5, 1, width, T * S, K, dev)
+            g = wl.norm_weight_device(5, 1, 0, K, dev)
+            xq, xd, _ = q.q8_quantize_rmsnorm(x, g, 1e-5)
+            xq, xd = xq.view(T, S, K), xd.view(T, S, K // 32)
+            y = torch.empty((T, 8, M), dtype=torch.float32, device=dev)
+            ws = torch.empty(q.mul_mat_id_q4q8_workspace(E, T, 8), dtype=torch.uint8, device=dev)
+            ms = per_launch_graph_ms(lambda: q.mul_mat_id_q4q8(qs, d, xq, xd, ids, y=y, ws=ws), reps=10, replays=10)
+            times.append(f"{width} pairs {ms * 1e3:.1f} us")
+        print(f"M = {M}, K = {K}: " + " | ".join(times), flush=True)
+
+
 def moe_only(n, dev):
     """Launch sequence for profiler runs of the routed MoE step (stacked
     gate/up and down routed calls on the 64-expert, 16-token, top-8 shape),
@@ -1113,6 +1149,8 @@ def main():
                     help="launch N grouped Q8_0 decode launches (B=1) and N grouped Q8_0 prefill launches, and exit")
     ap.add_argument("--moe-only", type=int, default=0, metavar="N",
                     help="launch N routed MoE steps and exit")
+    ap.add_argument("--moe-widths", action="store_true",
+                    help="routed call time per pass width in the 1536 and 2048 bands, and exit")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="launch N steps and N streaming passes (after a calibration copy) and exit")
     ap.add_argument("--decode-8b-only", nargs=2, type=int, default=None, metavar=("B", "N"),
@@ -1164,6 +1202,9 @@ def main():
         return
     if args.moe_only:
         moe_only(args.moe_only, dev)
+        return
+    if args.moe_widths:
+        moe_widths(dev)
         return
     if args.q8_0_only:
         q8_0_only(args.q8_0_only, dev)
