@@ -454,3 +454,51 @@ def test_group_prologue_packed_rows_mixed(B):
         y_o, _ = oracle.mul_mat(qs, d, xq_o, xd_o, nthreads=16, want_y64=False)
         assert np.isfinite(p["y"].cpu().numpy()).all()
         assert_close(p["y"].cpu().numpy(), y_o, f"input {i} K={K}")
+
+
+@pytest.mark.parametrize("B", [4, 8])
+def test_group_eight_llama_8b_layers(B):
+    """The Llama-3-8B decode step as the benchmark launches it: eight layers'
+    56 products in one grouped call with fp32 rows (the layers share one set of
+    weights; each has its own activation rows and outputs), so B = 8 takes the
+    multi-column kernel with the windows of all eight layers packed into
+    workgroup bins (products split over several records) and B = 4 the lane
+    kernel.  Every output is written and finite and equals the single call on
+    the same planes bit for bit; sampled rows of every product match the
+    oracle."""
+    print(f"[eight 8B layers] B={B}", flush=True)
+    dev = torch.device("cuda:0")
+    layer = workloads.LLAMA_3_8B
+    weights = [_weights(5, 0, mi, m.M, m.K) for mi, m in enumerate(layer)]
+    weights_d = [(to_dev(qs), to_dev(d.view(np.int16))) for qs, d in weights]
+    problems, meta = [], []
+    for l in range(8):
+        xs = {s: workloads.activation(6, l, s, B, K) for s, K in workloads.slot_k(layer).items()}
+        gs = {s: workloads.norm_weight(6, l, s, K) for s, K in workloads.slot_k(layer).items()}
+        xs_d = {s: to_dev(v) for s, v in xs.items()}
+        gs_d = {s: to_dev(v) for s, v in gs.items()}
+        for mi, m in enumerate(layer):
+            y = torch.full((B, m.M), float("nan"), dtype=torch.float32, device=dev)
+            problems.append({"qs": weights_d[mi][0], "d": weights_d[mi][1], "y": y, "x": xs_d[m.slot],
+                             "g": gs_d[m.slot], "eps": workloads.RMS_EPS})
+            meta.append((l, mi, m, xs[m.slot], gs[m.slot]))
+    grp = q.Group(problems, B=B)
+    assert bool(grp.plan.mfma_columns) == (B == 8)
+    if B == 8:
+        assert grp.plan.n_records > len(problems)      # products split over several records
+    grp()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(60 + B)
+    for p, (l, mi, m, x, g) in zip(problems, meta):
+        tag = f"B={B} layer {l} {m.name}"
+        y = p["y"].cpu().numpy()
+        assert np.isfinite(y).all(), tag
+        xq, xd, _ = q.q8_quantize_rmsnorm(p["x"], p["g"], workloads.RMS_EPS)
+        single = q.mul_mat_q4q8(p["qs"], p["d"], xq, xd)
+        torch.cuda.synchronize()
+        assert np.array_equal(single.cpu().numpy().view(np.uint32), y.view(np.uint32)), tag
+        rows = np.unique(np.concatenate([[0, m.M - 1], rng.integers(0, m.M, 14)]))
+        qs, d = weights[mi]
+        xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
+        y_o, _ = oracle.mul_mat(qs[rows], d[rows], xq_o, xd_o, nthreads=16, want_y64=False)
+        assert_close(y[:, rows], y_o, tag)
