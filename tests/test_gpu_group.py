@@ -502,3 +502,46 @@ def test_group_eight_llama_8b_layers(B):
         xq_o, xd_o, _ = oracle.q8_quantize_rmsnorm(x, g, workloads.RMS_EPS)
         y_o, _ = oracle.mul_mat(qs[rows], d[rows], xq_o, xd_o, nthreads=16, want_y64=False)
         assert_close(y[:, rows], y_o, tag)
+
+
+def test_group_multicolumn_in_hip_graph():
+    """The packed multi-column route (B = 8) captured in a HIP graph: the
+    prologue pass and the streaming launch over a group whose products are
+    split over workgroup bins.  Replayed five times with eager work on the
+    same buffers in between; every replay equals the eager launch bit for
+    bit."""
+    B = 8
+    dev = torch.device("cuda:0")
+    specs = [(4096, 4096, 0), (1024, 4096, 0), (2816, 2048, 1), (2048, 8192, 2), (1000, 1024, 3)]
+    problems = []
+    for i, (M, K, slot) in enumerate(specs):
+        qs, d = _weights(50, 0, i, M, K)
+        x = workloads.activation(50, 0, slot, B, K)
+        g = workloads.norm_weight(50, 0, slot, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        problems.append({"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": to_dev(x), "g": to_dev(g),
+                         "eps": workloads.RMS_EPS})
+    grp = q.Group(problems, B=B)
+    assert grp.plan.mfma_columns == 1 and grp.plan.n_records > len(problems)
+    grp()
+    torch.cuda.synchronize()
+    eager = [p["y"].clone() for p in problems]
+    assert all(torch.isfinite(e).all() for e in eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        grp()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp()
+    for rep in range(5):
+        for p in problems:
+            p["y"].fill_(float("nan"))
+        grp.workspace.fill_(0x5A)          # eager work on the prologue planes between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, e in zip(problems, eager):
+            assert torch.equal(p["y"].view(torch.int32), e.view(torch.int32)), f"replay {rep}"
