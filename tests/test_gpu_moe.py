@@ -252,3 +252,44 @@ def test_moe_chain_gate_up_swiglu_down_sum():
     # the quantisation-level tolerance of one extra Q8 rounding (2^-8 relative)
     err = np.abs(out.cpu().numpy().astype(np.float64) - out_o).max() / np.abs(out_o).max()
     assert err < 2e-3, err
+
+
+@pytest.mark.parametrize("E", [64, 900])
+def test_routed_call_in_hip_graph(E):
+    """A routed call captured in a HIP graph (routing inside the streaming
+    launch for 64 experts, its own launch for 900) and replayed three times,
+    the workspace overwritten with garbage between replays: every replay
+    equals the eager call bit for bit, so the routing keeps nothing from an
+    earlier call."""
+    M, K, T, top_k = 96, 1408, 16, 8
+    _, qs40, d40 = _experts(39, 40, M, K)
+    qs = np.zeros((E, M, K // 2), np.uint8)
+    d = np.zeros((E, M, K // 32), np.uint16)
+    qs[:40], d[:40] = qs40, d40
+    xq, xd = _acts(39, T, top_k, K)
+    ids = workloads.expert_ids(39, T, 40, top_k)
+    ids[3, 2] = E                                   # one invalid id: a NaN row
+    args = [to_dev(qs), to_dev(d.view(np.int16)), to_dev(xq), to_dev(xd), to_dev(ids)]
+    ws = torch.empty(q.mul_mat_id_q4q8_workspace(E, T, top_k), dtype=torch.uint8, device="cuda:0")
+    y = torch.empty((T, top_k, M), dtype=torch.float32, device="cuda:0")
+    q.mul_mat_id_q4q8(*args, y=y, ws=ws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q.mul_mat_id_q4q8(*args, y=y, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        q.mul_mat_id_q4q8(*args, y=y, ws=ws)
+    for rep in range(3):
+        y.fill_(-1.0)
+        ws.fill_(0xC3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
+    y_o = oracle.mul_mat_id(qs, d, xq, xd, ids, nthreads=8)
+    _check_rows(eager.cpu().numpy(), y_o, ids, E)
