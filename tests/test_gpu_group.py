@@ -545,3 +545,44 @@ def test_group_multicolumn_in_hip_graph():
         torch.cuda.synchronize()
         for p, e in zip(problems, eager):
             assert torch.equal(p["y"].view(torch.int32), e.view(torch.int32)), f"replay {rep}"
+
+
+def test_group_tiled_in_hip_graph():
+    """The tiled route (B = 300: the 256-thread prologue pass, then one tiled
+    MFMA launch) captured in a HIP graph and replayed three times with eager
+    work on the same buffers in between; every replay equals the eager launch
+    bit for bit."""
+    B = 300
+    dev = torch.device("cuda:0")
+    specs = [(300, 4096), (130, 1408), (257, 2048)]
+    problems = []
+    for i, (M, K) in enumerate(specs):
+        qs, d = _weights(51, 0, i, M, K)
+        x = workloads.activation(51, 0, i, B, K)
+        g = workloads.norm_weight(51, 0, i, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        problems.append({"qs": to_dev(qs), "d": to_dev(d.view(np.int16)), "y": y, "x": to_dev(x), "g": to_dev(g),
+                         "eps": workloads.RMS_EPS})
+    grp = q.Group(problems, B=B)
+    grp()
+    torch.cuda.synchronize()
+    eager = [p["y"].clone() for p in problems]
+    assert all(torch.isfinite(e).all() for e in eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        grp()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp()
+    for rep in range(3):
+        for p in problems:
+            p["y"].fill_(float("nan"))
+        grp.workspace.fill_(0x3C)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, e in zip(problems, eager):
+            assert torch.equal(p["y"].view(torch.int32), e.view(torch.int32)), f"replay {rep}"
