@@ -227,18 +227,22 @@ struct RoutedCols {
 // weight format; a Q8_0 block is two loads, so the caller passes half the
 // rows in flight (RIF) for the same bytes in flight.  LPR: lanes per row
 // (GemvShape); lane l takes blocks kb0 + l % LPR + LPR j of row slot rows
-// r * 64 / LPR + l / LPR.
+// r * 64 / LPR + l / LPR.  PW: windows of one wave (RU * 64 / LPR rows; K in
+// one wave only): the caller gives each wave its own window range, so the
+// waves of a workgroup stream independently.
 template <int BT, int J, int S, bool FOLD, bool WRITE_I, class Cols, int RIF = Q4Q8_GEMV_ROWS_IN_FLIGHT,
-          int WF = kWeightQ4, int LPR = kWave>
+          int WF = kWeightQ4, int LPR = kWave, bool PW = false>
 __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& cols, int B, int wl0, int wl1,
                                              unsigned char* smem, SplitScratch* split, int& parity,
                                              int32_t* __restrict__ Iout) {
   using Sh = GemvShape<BT, J, S, RIF, LPR>;
-  constexpr int RU = Sh::RU, WIN = Sh::WIN, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT, RPI = Sh::RPI;
+  constexpr int RU = Sh::RU, NV = Sh::NV, NP = Sh::NP, SHIFT = Sh::SHIFT, RPI = Sh::RPI;
+  constexpr int WIN = PW ? RU * RPI : Sh::WIN;  // rows per window (of the workgroup, or of this wave)
   static_assert(NP <= kMaxNP, "split scratch too small");
   static_assert(!FOLD || S == 1, "the folded prologue serves unsplit products");
   static_assert(!FOLD || WF == kWeightQ4, "the folded prologue serves Q4 weights");
   static_assert(LPR == kWave || (S == 1 && !FOLD), "rows shared by lane groups are neither split nor folded");
+  static_assert(!PW || (S == 1 && !FOLD), "per-wave windows keep K in one wave");
   constexpr int NL = WF == kWeightQ8 ? 2 : 1;  // 16-byte loads per block and lane
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   int bl = lane, rl = 0;  // lane within its row's lane group; the group's row within a row slot
@@ -253,7 +257,7 @@ __device__ __forceinline__ void gemv_segment(const GemvProblem& P, const Cols& c
     // live across the other segments and spill.
     asm volatile("" : "+v"(bl), "+v"(rl));
   }
-  const int rs = wave / S, kp = wave % S;
+  const int rs = PW ? 0 : wave / S, kp = wave % S;
   const int kb0 = kp * LPR * J;
   const int M = P.M, K = P.K, nb = K >> 5;
   const int64_t row_bytes = WF == kWeightQ8 ? K : K >> 1;

@@ -219,10 +219,21 @@ static int moe_band(int64_t K) {
   return K <= 1536 ? 1536 : K <= 2048 ? 2048 : K <= 4096 ? 4096 : K <= 8192 ? 8192 : K <= 16384 ? 16384 : 0;
 }
 
+// Bands whose every width keeps K in one wave (S = 1) schedule per wave:
+// each wave of a workgroup takes its own share of the cost, in windows of
+// its own rows (a quarter of a workgroup window), so the shares end within a
+// small window of their target.
+template <int BAND>
+constexpr bool moe_per_wave() {
+  return moe_class(BAND, 1).S == 1 && moe_class(BAND, 2).S == 1 && moe_class(BAND, 4).S == 1 &&
+         moe_class(BAND, 8).S == 1;
+}
+
 template <int BAND, int BT>
 constexpr int moe_win() {
   constexpr MoeClass c = moe_class(BAND, BT);
-  return GemvShape<BT, c.J, c.S, moe_rif(BT, BAND), c.LPR>::WIN;
+  using Sh = GemvShape<BT, c.J, c.S, moe_rif(BT, BAND), c.LPR>;
+  return moe_per_wave<BAND>() ? Sh::RU * Sh::RPI : Sh::WIN;
 }
 
 // Rows per window of the routed launch: the largest streaming window over the
@@ -299,7 +310,11 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
   const int n_sel = ctl[0];
   if (n_sel == 0) return;
   const int64_t C = costp[n_sel];
-  const int64_t G = gridDim.x, g = blockIdx.x;
+  // per-wave shares (moe_per_wave): wave w of workgroup b takes share 4 b + w
+  constexpr bool PW = moe_per_wave<KMAX>();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int64_t G = (int64_t)gridDim.x * (PW ? kGemvWaves : 1), g = PW ? (int64_t)blockIdx.x * kGemvWaves + wave
+                                                                         : (int64_t)blockIdx.x;
   const int64_t c_lo = C * g / G, c_hi = C * (g + 1) / G;
   // first selected expert whose cost range reaches past c_lo (wave-wide ballot)
   int i = -1;
@@ -350,8 +365,8 @@ __global__ __launch_bounds__(kGemvThreads, moe_waves_per_simd(KMAX)) void moe_st
         constexpr MoeClass cls = moe_class(KMAX, BT);
         static_assert(cls.J != 0, "unsupported band");
         constexpr int RIF = moe_rif(BT, KMAX);
-        const int f = unit / GemvShape<BT, cls.J, cls.S, RIF, cls.LPR>::WIN;
-        gemv_segment<BT, cls.J, cls.S, false, false, RoutedCols, RIF, kWeightQ4, cls.LPR>(
+        const int f = unit / moe_win<KMAX, BT>();
+        gemv_segment<BT, cls.J, cls.S, false, false, RoutedCols, RIF, kWeightQ4, cls.LPR, PW>(
             P, cols, nc, wl0 * f, wl1 * f, nullptr, &split, parity, nullptr);
       };
       if (nc == 1)
