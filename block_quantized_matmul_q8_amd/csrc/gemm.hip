@@ -13,18 +13,19 @@
 // (|16 I| < 2^22 still) and the fmas take d_w / 16 and -1.5 * 2^23 * d_w / 16,
 // both exact: t keeps the bits of fl(I * d_w).
 //
-// What bounds it on gfx950 (measured): a 32x32x32 i8 MFMA occupies its SIMD
-// for about 33.5 cycles, and an fp32 fma issues every ~2.35 cycles when two
-// or more waves feed the SIMD (one wave alone issues one every ~4.6 cycles,
-// and one that depends on the fma just before it waits) -- but the two do
-// not overlap once the vector ALU is saturated.  A 32 x 32 tile-block
-// therefore costs about 33.5 + 32 x 2.35 = 109 SIMD cycles (about 30% of the
-// int8 peak); every other vector instruction adds to it, and LDS reads
-// (about 5 cycles per contiguous 1 KiB wave read, 8 for strided ones and 4x
-// that for 4-way bank conflicts, per CU) must stay under it.  With two waves
-// per SIMD (the register budget of this tiling), the stage fetch, the stage
-// store and the barrier leave a SIMD with one ready wave about a third of the
-// time, and then its vector ALU runs at half rate.
+// What bounds it on gfx950 (measured): a 32x32x32 i8 MFMA occupies the
+// matrix core of its SIMD for 32-37 cycles, and a SIMD's vector ALU retires
+// one wave64 fp32 fma about every 4 cycles when two or more waves feed it
+// (one wave alone: one every ~6 cycles).  The matrix core and the vector ALU
+// run concurrently (instructions of other waves, or independent ones of the
+// same wave, issue while an MFMA executes), so a 32 x 32 tile-block costs
+// about 4 x 32 = 128 vector-ALU cycles against 32 on the matrix core: the
+// rescale fmas are the bound (near 25% of the int8 peak at 2.4 GHz, less at
+// the clock the chip holds under this load), and every other vector
+// instruction adds to it.  Waves stall where an MFMA or fma waits for an
+// LDS read or for the MFMA result it consumes; with two waves per SIMD (the
+// register budget of this tiling) such stalls leave the vector ALU idle
+// unless the other wave has work, so LDS operands are read one MFMA ahead.
 //
 // Operand roles: A = activations (MFMA rows = tokens), B = weights (MFMA
 // columns = weight rows).  Each lane then holds one weight row per 32-row
@@ -290,81 +291,126 @@ __device__ __forceinline__ void gemm_tile(const GemvProblem& P, int L, int n_nt,
   fetch_any(0, f);
   store_stage(st[0], false, f);
   __syncthreads();
-  int buf = 0;
-  for (int kb0 = 0; kb0 < nb; kb0 += kKB) {
-    const bool more = kb0 + kKB < nb;
-    const bool fast = fast_ok && kb0 + 2 * kKB <= nb;
-    if (more) {  // in flight during this stage's compute
-      if (fast)
-        fetch_fast(kb0 + kKB, f);
-      else
-        fetch_any(kb0 + kKB, f);
-    }
-    const GemmStage& sg = st[buf];
+  // Q4 tiles without block-sum output take two stages per iteration of the
+  // outer loop (the inner loop unrolled), so that the buffer index is a
+  // constant and every LDS address a per-lane offset plus a constant (fewer
+  // vector instructions per stage); the other instances have no registers to
+  // spare for the second set of addresses.
+  constexpr int kUnroll = (!WRITE_I && WF == kWeightQ4) ? 2 : 1;
+  for (int kb00 = 0; kb00 < nb; kb00 += kUnroll * kKB) {
 #pragma unroll
-    for (int blk = 0; blk < kKB; ++blk) {
-      if (kb0 + blk < nb) {
-        const v4i a = *reinterpret_cast<const v4i*>(&sg.a[blk].v[wave][0][0][0] + loff);
-        float dx[16];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int kb0 = kb00 + u * kKB;
+      if (kb0 >= nb) break;
+      const int buf = kUnroll == 2 ? u : (kb0 / kKB) & 1;
+      const bool more = kb0 + kKB < nb;
+      const bool fast = fast_ok && kb0 + 2 * kKB <= nb;
+      if (more) {  // in flight during this stage's compute
+        if (fast)
+          fetch_fast(kb0 + kKB, f);
+        else
+          fetch_any(kb0 + kKB, f);
+      }
+      const GemmStage& sg = st[buf];
+      auto lds_a = [&](int blk) { return *reinterpret_cast<const v4i*>(&sg.a[blk].v[wave][0][0][0] + loff); };
+      auto lds_w = [&](int blk, int jt) { return *reinterpret_cast<const v4i*>(&sg.w[blk].v[jt][0][0][0] + loff); };
+      auto lds_dwc = [&](int blk, int jt) { return sg.dwc[blk][jt * 32 + l32]; };
+      // LDS operands are read one MFMA ahead of their use (kAhead): a block's
+      // first two weight fragments (and the activation fragment) during the
+      // previous block's last tiles, fragments 2 and 3 while tile 0 is
+      // rescaled, so that no MFMA waits for an LDS read that was issued just
+      // before it.  The block-sum instances read each fragment just before its
+      // MFMA: their block-sum stores leave no registers for operands in flight.
+      constexpr bool kAhead = !WRITE_I;
+      v4i a, bf[kJT];
+      f32x2 dwf[kJT];
+      if constexpr (kAhead) {
+        a = lds_a(0);
+        bf[0] = lds_w(0, 0);
+        bf[1] = lds_w(0, 1);
+        dwf[0] = lds_dwc(0, 0);
+        dwf[1] = lds_dwc(0, 1);
+      }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wave * 32 + 8 * g + 4 * h]);
-          dx[4 * g + 0] = v.x;
-          dx[4 * g + 1] = v.y;
-          dx[4 * g + 2] = v.z;
-          dx[4 * g + 3] = v.w;
-        }
-        // The 4 tiles of the block in a pipeline: tile jt + 1's operands are
-        // read and its MFMA issued before tile jt is rescaled, so at most two
-        // results and two weight fragments are live (the register budget of
-        // two workgroups per CU).  Scheduling barriers keep that order.
-        v4i b = *reinterpret_cast<const v4i*>(&sg.w[blk].v[0][0][0][0] + loff);
-        f32x2 dwc = sg.dwc[blk][l32];
-        // Whole result vectors are reinterpreted: hipcc (ROCm 7.2)
-        // miscompiles a per-element int <-> float bit cast of an MFMA
-        // result, propagating element 0 to every element.
-        v16i Di = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, seed, 0, 0, 0);
+      for (int blk = 0; blk < kKB; ++blk) {
+        if (kb0 + blk < nb) {
+          float dx[16];
 #pragma unroll
-        for (int jt = 0; jt < kJT; ++jt) {
-          v16i Dn;
-          f32x2 dwn;
-          if (jt + 1 < kJT) {
-            const v4i bn = *reinterpret_cast<const v4i*>(&sg.w[blk].v[jt + 1][0][0][0] + loff);
-            dwn = sg.dwc[blk][(jt + 1) * 32 + l32];
-            Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bn, seed, 0, 0, 0);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&sg.dx[blk][wave * 32 + 8 * g + 4 * h]);
+            dx[4 * g + 0] = v.x;
+            dx[4 * g + 1] = v.y;
+            dx[4 * g + 2] = v.z;
+            dx[4 * g + 3] = v.w;
           }
-          __builtin_amdgcn_sched_barrier(0);
-          if (WRITE_I) {
+          // The 4 tiles of the block in a pipeline: tile jt + 1's MFMA is
+          // issued before tile jt is rescaled, so at most two results are live
+          // (the register budget of two workgroups per CU).  Scheduling
+          // barriers keep that order.
+          // Whole result vectors are reinterpreted: hipcc (ROCm 7.2)
+          // miscompiles a per-element int <-> float bit cast of an MFMA
+          // result, propagating element 0 to every element.
+          if constexpr (!kAhead) {
+            a = lds_a(blk);
+            bf[0] = lds_w(blk, 0);
+            dwf[0] = lds_dwc(blk, 0);
+          }
+          v16i Di = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bf[0], seed, 0, 0, 0);
+          if constexpr (kAhead) {
+            bf[2] = lds_w(blk, 2);
+            dwf[2] = lds_dwc(blk, 2);
+          }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int n = n0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              const int m = m0 + jt * 32 + l32;
-              // Q4 operands carry 16 (q - 8): the exact multiple of 16 is shifted back
-              const int I = WF == kWeightQ8 ? Di[r] - kMagicBits : (Di[r] - kMagicBits) >> 4;
-              if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = I;
+          for (int jt = 0; jt < kJT; ++jt) {
+            v16i Dn;
+            if (jt + 1 < kJT) {
+              if constexpr (!kAhead) {
+                bf[jt + 1] = lds_w(blk, jt + 1);
+                dwf[jt + 1] = lds_dwc(blk, jt + 1);
+              }
+              Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bf[jt + 1], seed, 0, 0, 0);
             }
-          }
-          // Two passes, so that no fma waits on the one just before it
-          // (back-to-back dependent vector instructions stall on gfx950):
-          // t = fl(I * d_w) in place of F for all 16 elements, then the sums.
-          v16f Fv = __builtin_bit_cast(v16f, Di);
+            if (kAhead && jt == 0) {
+              bf[3] = lds_w(blk, 3);
+              dwf[3] = lds_dwc(blk, 3);
+            }
+            if (kAhead && jt == kJT - 2 && blk + 1 < kKB) {  // the last MFMA of the block has read a
+              a = lds_a(blk + 1);
+              bf[0] = lds_w(blk + 1, 0);
+              bf[1] = lds_w(blk + 1, 1);
+              dwf[0] = lds_dwc(blk + 1, 0);
+              dwf[1] = lds_dwc(blk + 1, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (WRITE_I) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) Fv[r] = __builtin_fmaf(Fv[r], dwc.x, dwc.y);
+              for (int r = 0; r < 16; ++r) {
+                const int n = n0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int m = m0 + jt * 32 + l32;
+                // Q4 operands carry 16 (q - 8): the exact multiple of 16 is shifted back
+                const int I = WF == kWeightQ8 ? Di[r] - kMagicBits : (Di[r] - kMagicBits) >> 4;
+                if (n < B && m < M) Iout[((int64_t)n * M + m) * nb + kb0 + blk] = I;
+              }
+            }
+            // Two passes, so that no fma waits on the one just before it
+            // (back-to-back dependent vector instructions stall on gfx950):
+            // t = fl(I * d_w) in place of F for all 16 elements, then the sums.
+            const f32x2 dwc = dwf[jt];
+            v16f Fv = __builtin_bit_cast(v16f, Di);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[jt][r] = __builtin_fmaf(Fv[r], dx[r], acc[jt][r]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (jt + 1 < kJT) {
-            Di = Dn;
-            dwc = dwn;
+            for (int r = 0; r < 16; ++r) Fv[r] = __builtin_fmaf(Fv[r], dwc.x, dwc.y);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[jt][r] = __builtin_fmaf(Fv[r], dx[r], acc[jt][r]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (jt + 1 < kJT) Di = Dn;
           }
         }
       }
+      // The other buffer was last read in the previous stage, which every wave
+      // finished before the barrier that ended it.
+      if (more) store_stage(st[buf ^ 1], fast, f);
+      __syncthreads();
     }
-    // The other buffer was last read in the previous stage, which every wave
-    // finished before the barrier that ended it.
-    if (more) store_stage(st[buf ^ 1], fast, f);
-    __syncthreads();
-    buf ^= 1;
   }
 
 #pragma unroll
