@@ -1090,7 +1090,7 @@ def bench_moe(args, dev):
     sum_bytes = cfg.T * cfg.top_k * (cfg.hidden + 1) * 4 + cfg.T * cfg.hidden * 4
     return {"GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
             "distinct_experts": distinct, "bytes": nbytes,
-            "launches": "2 routed calls (stacked gate/up, down), each a routing kernel + a streaming kernel",
+            "launches": "2 routed calls (stacked gate/up, down), each one streaming launch whose workgroups route the pairs in LDS before streaming (a small routing)",
             "weight_copies": len(copies),
             "expert_sum": {"us": round(ms_sum * 1e3, 2), "GB/s": round(sum_bytes / (ms_sum * 1e-3) / 1e9, 1),
                            "bytes": sum_bytes,
