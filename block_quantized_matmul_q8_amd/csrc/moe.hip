@@ -119,26 +119,64 @@ __device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int n
       list[n - 1 - atomicAdd(n_bad, 1)] = i;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += NT) {
-    const int c = cnt[e];
-    sidx[e] = c > 0 ? 1 : 0;
-    cpre[e] = c > 0 ? n_win * moe_window_cost(c, band) : 0;
-  }
-  __syncthreads();
-  block_exclusive_scan<NT>(cnt, E, wave_tot, tid);
-  block_exclusive_scan<NT>(sidx, E, wave_tot, tid);
-  block_exclusive_scan<NT>(cpre, E, wave_tot, tid);
-  for (int e = tid; e <= E; e += NT) offsets[e] = cnt[e];
-  // Selected experts in expert order with the prefix of their costs.
-  for (int e = tid; e < E; e += NT) {
-    if (cnt[e + 1] > cnt[e]) {
-      sel[sidx[e]] = e;
-      costp[sidx[e]] = cpre[e];
+  if (E <= kWave) {
+    // Up to one expert per lane: wave 0 takes the three prefix sums with
+    // shuffles (no block scans and their barriers).
+    if (tid < kWave) {
+      const int e = tid;
+      const int c = e < E ? cnt[e] : 0;
+      const int si = c > 0 ? 1 : 0;
+      const int cp = c > 0 ? n_win * moe_window_cost(c, band) : 0;
+      int ic = c, is = si, ip = cp;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int tc = __shfl_up(ic, off, kWave), ts = __shfl_up(is, off, kWave), tq = __shfl_up(ip, off, kWave);
+        if (e >= off) {
+          ic += tc;
+          is += ts;
+          ip += tq;
+        }
+      }
+      const int tot_c = __shfl(ic, kWave - 1, kWave), tot_s = __shfl(is, kWave - 1, kWave);
+      const int tot_p = __shfl(ip, kWave - 1, kWave);
+      if (e < E) {
+        cnt[e] = ic - c;
+        offsets[e] = ic - c;
+        if (c > 0) {
+          sel[is - si] = e;
+          costp[is - si] = ip - cp;
+        }
+      }
+      if (e == 0) {
+        cnt[E] = tot_c;
+        offsets[E] = tot_c;
+        costp[tot_s] = tot_p;
+        ctl[0] = tot_s;
+      }
     }
-  }
-  if (tid == 0) {
-    costp[sidx[E]] = cpre[E];
-    ctl[0] = sidx[E];
+    __syncthreads();
+  } else {
+    for (int e = tid; e < E; e += NT) {
+      const int c = cnt[e];
+      sidx[e] = c > 0 ? 1 : 0;
+      cpre[e] = c > 0 ? n_win * moe_window_cost(c, band) : 0;
+    }
+    __syncthreads();
+    block_exclusive_scan<NT>(cnt, E, wave_tot, tid);
+    block_exclusive_scan<NT>(sidx, E, wave_tot, tid);
+    block_exclusive_scan<NT>(cpre, E, wave_tot, tid);
+    for (int e = tid; e <= E; e += NT) offsets[e] = cnt[e];
+    // Selected experts in expert order with the prefix of their costs.
+    for (int e = tid; e < E; e += NT) {
+      if (cnt[e + 1] > cnt[e]) {
+        sel[sidx[e]] = e;
+        costp[sidx[e]] = cpre[e];
+      }
+    }
+    if (tid == 0) {
+      costp[sidx[E]] = cpre[E];
+      ctl[0] = sidx[E];
+    }
   }
   for (int i = tid; i < n; i += NT) {
     const int e = ids[i];
